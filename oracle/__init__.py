@@ -1,0 +1,195 @@
+"""CPU float64 oracle for the fused attention-variant forward.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline leg may import this package; the product path never does.  It shares
+no code with the GPU library.  The arithmetic lives in ``oracle.c`` (plain C,
+float64, two passes per query row); this module only marshals numpy arrays
+through ctypes.
+
+Every function takes float64 (or uint8 / int32 where stated) numpy arrays in
+the layouts documented in ``oracle.h`` and returns float64 outputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+
+VANILLA, ALIBI, SOFTCAP, CAUSAL, SLIDING_WINDOW, PREFIX_LM, DOCUMENT = range(7)
+VARIANTS = {
+    "vanilla": VANILLA,
+    "alibi": ALIBI,
+    "softcap": SOFTCAP,
+    "causal": CAUSAL,
+    "sliding_window": SLIDING_WINDOW,
+    "prefix_lm": PREFIX_LM,
+    "document": DOCUMENT,
+}
+
+
+def build(force: bool = False) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` with gcc (no GPU code)."""
+    src = os.path.join(_HERE, "oracle.c")
+    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(src):
+        tmp = _SO + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                               "-Wall", "-o", tmp, src, "-lm"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [
+        ("variant", ctypes.c_int),
+        ("scale", ctypes.c_double),
+        ("softcap", ctypes.c_double),
+        ("alibi_max_bias", ctypes.c_double),
+        ("window", ctypes.c_int),
+        ("window_causal", ctypes.c_int),
+        ("prefix", ctypes.c_int),
+        ("doc_offsets", ctypes.c_void_p),
+        ("n_docs", ctypes.c_int),
+    ]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        lib = ctypes.CDLL(_SO)
+        P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.oracle_attn_rows.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I,
+                                         ctypes.POINTER(_Params), P, I64, I, I]
+        lib.oracle_diffattn_rows.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I,
+                                             D, D, I, P, I64, I]
+        lib.oracle_evoformer_row.argtypes = [P, P, P, P, P, P, P, I, I, I, I, D, P, I64, I]
+        lib.oracle_evoformer_col.argtypes = [P, P, P, P, P, P, I, I, I, I, D, P, I64, I]
+        for f in (lib.oracle_attn_rows, lib.oracle_diffattn_rows,
+                  lib.oracle_evoformer_row, lib.oracle_evoformer_col):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _rows(rows, total):
+    if rows is None:
+        return None, total
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    return r, int(r.size)
+
+
+def attn(q, k, v, *, variant="vanilla", scale=None, bias=None, softcap=50.0,
+         alibi_max_bias=8.0, window=256, window_causal=True, prefix=512,
+         doc_offsets=None, rows=None, block_keys=0, threads=None):
+    """Attention forward for q [B,Hq,Sq,D], k [B,Hkv,Sk,D], v [B,Hkv,Sk,Dv].
+
+    Returns (o, lse).  With ``rows`` (flat indices (b*Hq+h)*Sq+i) the outputs
+    are compact [n_rows, Dv] and [n_rows]; otherwise [B,Hq,Sq,Dv] and [B,Hq,Sq].
+    ``block_keys > 0`` selects the online twin.
+    """
+    q, k, v, bias = _f64(q), _f64(k), _f64(v), _f64(bias)
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Sk, Dv = v.shape
+    assert k.shape == (B, Hkv, Sk, D) and v.shape[:3] == (B, Hkv, Sk)
+    if bias is not None:
+        assert bias.shape == (Hq, Sq, Sk)
+    var = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    docs = None
+    if var == DOCUMENT:
+        docs = np.ascontiguousarray(doc_offsets, dtype=np.int32)
+        assert docs.ndim == 2 and docs.shape[0] == B
+    p = _Params(var, float(scale if scale is not None else 1.0 / np.sqrt(D)), float(softcap),
+                float(alibi_max_bias), int(window), int(bool(window_causal)), int(prefix),
+                None if docs is None else docs.ctypes.data,
+                0 if docs is None else docs.shape[1] - 1)
+    r, n = _rows(rows, B * Hq * Sq)
+    o = np.empty((n, Dv), np.float64)
+    lse = np.empty((n,), np.float64)
+    rc = _load().oracle_attn_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(o), _ptr(lse),
+                                  B, Hq, Hkv, Sq, Sk, D, Dv, ctypes.byref(p), _ptr(r), n,
+                                  int(block_keys), threads or default_threads())
+    if rc:
+        raise ValueError("oracle_attn_rows rejected its arguments (%d)" % rc)
+    if rows is None:
+        return o.reshape(B, Hq, Sq, Dv), lse.reshape(B, Hq, Sq)
+    return o, lse
+
+
+def diffattn(q1, q2, k1, k2, v, *, scale=None, lam=0.8, causal=False, rows=None,
+             threads=None):
+    """Differential attention; returns (o, lse1, lse2) shaped like :func:`attn`."""
+    q1, q2, k1, k2, v = map(_f64, (q1, q2, k1, k2, v))
+    B, H, Sq, Dqk = q1.shape
+    Sk, Dv = v.shape[2], v.shape[3]
+    r, n = _rows(rows, B * H * Sq)
+    o = np.empty((n, Dv), np.float64)
+    l1 = np.empty((n,), np.float64)
+    l2 = np.empty((n,), np.float64)
+    rc = _load().oracle_diffattn_rows(_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), _ptr(o),
+                                      _ptr(l1), _ptr(l2), B, H, Sq, Sk, Dqk, Dv,
+                                      float(scale if scale is not None else 1.0 / np.sqrt(Dqk)),
+                                      float(lam), int(bool(causal)), _ptr(r), n,
+                                      threads or default_threads())
+    if rc:
+        raise ValueError("oracle_diffattn_rows rejected its arguments (%d)" % rc)
+    if rows is None:
+        return o.reshape(B, H, Sq, Dv), l1.reshape(B, H, Sq), l2.reshape(B, H, Sq)
+    return o, l1, l2
+
+
+def evoformer(q, k, v, gate, *, pair_bias=None, key_mask=None, axis="row", scale=None,
+              rows=None, threads=None):
+    """Evoformer gated self-attention on MSA tensors [N_seq, N_res, H, C].
+
+    axis="row": attention along residues, optional pair_bias [H,N_res,N_res],
+    key_mask [N_seq,N_res] (uint8, 1 keep).  axis="col": attention along
+    sequences within each residue column (no pair bias); rows then index the
+    transposed problem and the full output is returned in [N_seq,N_res,H,C].
+    """
+    q, k, v, gate, pair_bias = map(_f64, (q, k, v, gate, pair_bias))
+    N_seq, N_res, H, C = q.shape
+    km = None if key_mask is None else np.ascontiguousarray(key_mask, dtype=np.uint8)
+    sc = float(scale if scale is not None else 1.0 / np.sqrt(C))
+    lib = _load()
+    th = threads or default_threads()
+    if axis == "row":
+        r, n = _rows(rows, N_seq * N_res * H)
+        o = np.empty((n, C), np.float64)
+        rc = lib.oracle_evoformer_row(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(pair_bias),
+                                      _ptr(km), _ptr(o), N_seq, N_res, H, C, sc, _ptr(r), n, th)
+        if rc:
+            raise ValueError("oracle_evoformer_row rejected its arguments (%d)" % rc)
+        return o.reshape(N_seq, N_res, H, C) if rows is None else o
+    if axis == "col":
+        assert pair_bias is None
+        r, n = _rows(rows, N_seq * N_res * H)
+        o = np.empty((n, C), np.float64)
+        rc = lib.oracle_evoformer_col(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(km), _ptr(o),
+                                      N_seq, N_res, H, C, sc, _ptr(r), n, th)
+        if rc:
+            raise ValueError("oracle_evoformer_col rejected its arguments (%d)" % rc)
+        if rows is None:
+            return o.reshape(N_res, N_seq, H, C).transpose(1, 0, 2, 3).copy()
+        return o
+    raise ValueError("axis must be 'row' or 'col'")
