@@ -1,0 +1,288 @@
+"""Throughput of the fused attention-variant forward on one MI355X.
+
+One step = one forward call of each of the seven FlexAttention-class variants
+(vanilla, ALiBi, softcap, causal, causal sliding window 256, PrefixLM 512,
+document mask) on the MHA workload B=4, H=16, S=4096, D=64, bf16 (inputs
+resident in HBM before timing).  ``value`` is the useful TFLOP/s of the whole
+step; per-variant figures, the roofline of the dominant kernel (live HIP
+event timing on the launch stream) and the CPU oracle's throughput on a
+bounded sample of the same workload are printed on the same JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --report        # extra lines: every workload, every variant
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "attention fwd useful TFLOP/s + % bf16 MFMA peak (S=4k, D=64, per variant)"
+HEADLINE = "mha_bf16_b4_h16_s4096_d64"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--variants", default=None, help="comma list (default: all seven)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--report", action="store_true",
+                    help="also print one JSON line per workload and variant")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with HBM bytes per launch measured by rocprofv3 counters")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from flashattention_attention_variants_amd import api, flops, inputs
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    api.load_library()
+    dev = "cuda"
+    wl = inputs.WORKLOADS[args.workload]
+    assert wl.kind == "attn"
+    s = wl.shape
+    B, Hq, Hkv, S, D = s["B"], s["Hq"], s["Hkv"], s["S"], s["D"]
+    t = inputs.make(wl)
+    q, k, v = t["q"].to(dev), t["k"].to(dev), t["v"].to(dev)
+    docs = t.get("doc_offsets")
+    docs_dev = docs.to(dev) if docs is not None else None
+    variants = args.variants.split(",") if args.variants else list(wl.variants)
+    pr = wl.params
+    outs = {vname: torch.empty_like(q) for vname in variants}
+
+    def kw_for(vname):
+        kw = dict(variant=vname)
+        for key in ("softcap", "alibi_max_bias", "window", "window_causal", "prefix"):
+            if key in pr:
+                kw[key] = pr[key]
+        if vname == "document":
+            kw["doc_offsets"] = docs_dev
+        return kw
+
+    kws = {vname: kw_for(vname) for vname in variants}
+    fl = {vname: flops.attn_flops(vname, B, Hq, S, S, D, window=pr.get("window", 256),
+                                  window_causal=pr.get("window_causal", True),
+                                  prefix=pr.get("prefix", 512),
+                                  doc_offsets=None if docs is None else docs.numpy())
+          for vname in variants}
+    nbytes = flops.attn_bytes(B, Hq, Hkv, S, S, D)
+
+    def step(events=None):
+        for vname in variants:
+            if events is not None:
+                events[vname][0].record()
+            api.fl_attn_fwd(q, k, v, out=outs[vname], **kws[vname])
+            if events is not None:
+                events[vname][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region: K steps, every launch bracketed by events on the launch stream
+    ev = {vname: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)] for vname in variants}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step({vname: ev[vname][i] for vname in variants})
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {vname: sum(a.elapsed_time(b) for a, b in ev[vname]) / args.steps for vname in variants}
+    total_flops = sum(fl.values())
+    value = total_flops * args.steps / wall / 1e12
+
+    per = {}
+    for vname in variants:
+        tf = fl[vname] / (ms[vname] * 1e-3) / 1e12
+        bound, roof = flops.roofline_tflops(fl[vname], nbytes)
+        per[vname] = dict(ms=round(ms[vname], 4), tflops=round(tf, 1),
+                          frac_bf16_peak=round(tf / flops.PEAK_BF16_TFLOPS, 4), bound=bound,
+                          roofline_tflops=round(roof, 1), frac_roofline=round(tf / roof, 4),
+                          useful_gflop=round(fl[vname] / 1e9, 2))
+    dom = max(variants, key=lambda vname: ms[vname])
+    achieved = fl[dom] / (ms[dom] * 1e-3) / 1e12
+    bound, roof = flops.roofline_tflops(fl[dom], nbytes)
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        rec = json.load(open(args.traffic))
+        traffic = rec.get(dom)
+    roofline = dict(bound=bound, achieved=round(achieved, 1),
+                    peak=flops.PEAK_BF16_TFLOPS if bound == "mfma" else flops.PEAK_HBM_GBS,
+                    unit="TFLOP/s" if bound == "mfma" else "GB/s",
+                    frac=round(achieved / flops.PEAK_BF16_TFLOPS, 4), traffic=traffic,
+                    kernel="attn_mfma_kernel (%s)" % dom, ms_per_launch=round(ms[dom], 4),
+                    useful_flop_per_launch=fl[dom], algorithmic_bytes_per_launch=nbytes)
+    if bound == "hbm":
+        gbs = nbytes / (ms[dom] * 1e-3) / 1e9
+        roofline.update(achieved=round(gbs, 1), frac=round(gbs / flops.PEAK_HBM_GBS, 4))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(t, variants, kws, wl, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "H_q": Hq, "H_kv": Hkv, "S": S, "D": D,
+                   "variants": variants, "step": "one forward call per variant",
+                   "seed": wl.seed},
+        "frac_bf16_peak": round(value / flops.PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline, "cpu_baseline": cpu, "per_variant": per,
+    }
+    print(json.dumps(line), flush=True)
+    if args.report:
+        report(torch, api, flops, inputs, dev)
+
+
+def cpu_baseline(t, variants, kws, wl, seconds):
+    """Oracle throughput (useful TFLOP/s) on sampled query rows of the same
+    workload, all variants, float64, host threads."""
+    import numpy as np
+
+    import oracle
+    from flashattention_attention_variants_amd import flops
+
+    oracle.build()
+    s = wl.shape
+    B, Hq, S, D = s["B"], s["Hq"], s["S"], s["D"]
+    q64 = t["q"].to(__import__("torch").float64).numpy()
+    k64 = t["k"].to(__import__("torch").float64).numpy()
+    v64 = t["v"].to(__import__("torch").float64).numpy()
+    docs = t.get("doc_offsets")
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(0)
+
+    def sample(n):
+        return np.sort(rng.choice(B * Hq * S, size=n, replace=False))
+
+    def useful(vname, rows):
+        # allowed keys of each sampled row, from the same closed forms as the GPU count
+        tot = 0
+        i = rows % S
+        b = rows // (Hq * S)
+        kw = kws[vname]
+        for ii, bb in zip(i, b):
+            if vname in ("vanilla", "alibi", "softcap"):
+                n = S
+            elif vname == "causal":
+                n = ii + 1
+            elif vname == "sliding_window":
+                n = min(ii + 1, kw["window"])
+            elif vname == "prefix_lm":
+                n = max(ii + 1, min(kw["prefix"], S))
+            else:
+                off = docs[bb].numpy()
+                d = np.searchsorted(off, ii, side="right") - 1
+                n = off[d + 1] - off[d]
+            tot += 2 * int(n) * (D + D)
+        return tot
+
+    def run(vname, rows):
+        kw = {k: v for k, v in kws[vname].items() if k != "doc_offsets"}
+        if vname == "document":
+            kw["doc_offsets"] = docs.numpy()
+        oracle.attn(q64, k64, v64, rows=rows, threads=threads, **kw)
+
+    # calibrate on a small sample, then size the sample to ~seconds of work
+    probe = sample(64 * threads)
+    t0 = time.perf_counter()
+    run("vanilla", probe)
+    per_row = (time.perf_counter() - t0) / len(probe)
+    n = int(max(threads, min(B * Hq * S, seconds / len(variants) / max(per_row, 1e-9))))
+    total_flop, total_s = 0, 0.0
+    for vname in variants:
+        rows = sample(n)
+        t0 = time.perf_counter()
+        run(vname, rows)
+        total_s += time.perf_counter() - t0
+        total_flop += useful(vname, rows)
+    return {"value": round(total_flop / total_s / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d random query rows per variant (x%d variants) of %s, float64 two-pass, "
+                      "%.1f s" % (n, len(variants), wl.name, total_s)}
+
+
+def report(torch, api, flops, inputs, dev):
+    """One JSON line per (workload, variant): time, TFLOP/s, roofline fraction."""
+
+    def timeit(fn, iters=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters
+
+    for name, wl in inputs.WORKLOADS.items():
+        t = inputs.make(wl)
+        g = {k: v.to(dev) for k, v in t.items()}
+        s = wl.shape
+        for vname in wl.variants:
+            if wl.kind == "attn":
+                kw = dict(variant=vname)
+                for key in ("softcap", "alibi_max_bias", "window", "window_causal", "prefix"):
+                    if key in wl.params:
+                        kw[key] = wl.params[key]
+                if vname == "document":
+                    kw["doc_offsets"] = g["doc_offsets"]
+                out = torch.empty_like(g["q"])
+                ms = timeit(lambda: api.fl_attn_fwd(g["q"], g["k"], g["v"], out=out, **kw))
+                f = flops.attn_flops(vname, s["B"], s["Hq"], s["S"], s["S"], s["D"],
+                                     window=wl.params.get("window", 256),
+                                     window_causal=wl.params.get("window_causal", True),
+                                     prefix=wl.params.get("prefix", 512),
+                                     doc_offsets=None if "doc_offsets" not in t else t["doc_offsets"].numpy())
+                nb = flops.attn_bytes(s["B"], s["Hq"], s["Hkv"], s["S"], s["S"], s["D"],
+                                      elem=2 if wl.dtype == "bf16" else 4)
+                peak = flops.PEAK_BF16_TFLOPS if wl.dtype == "bf16" else flops.PEAK_F32_VALU_TFLOPS
+            elif wl.kind == "diffattn":
+                out = torch.empty(s["B"], s["H"], s["S"], s["Dv"], dtype=torch.bfloat16, device=dev)
+                causal = vname == "causal"
+                ms = timeit(lambda: api.fl_diffattn_fwd(g["q1"], g["q2"], g["k1"], g["k2"], g["v"],
+                                                        lam=wl.params["lam"], causal=causal, out=out))
+                f = flops.diffattn_flops(s["B"], s["H"], s["S"], s["Dqk"], s["Dv"], causal)
+                nb = flops.diffattn_bytes(s["B"], s["H"], s["S"], s["Dqk"], s["Dv"])
+                peak = flops.PEAK_BF16_TFLOPS
+            else:
+                out = torch.empty_like(g["q"])
+                pb = g["pair_bias"] if vname == "row" else None
+                ms = timeit(lambda: api.fl_evoformer_gated_attn_fwd(
+                    g["q"], g["k"], g["v"], g["gate"], pair_bias=pb, key_mask=g["key_mask"],
+                    axis=vname, out=out))
+                f = flops.evoformer_flops(s["N_seq"], s["N_res"], s["H"], s["C"], vname)
+                nb = flops.evoformer_bytes(s["N_seq"], s["N_res"], s["H"], s["C"], vname)
+                peak = flops.PEAK_BF16_TFLOPS
+            tf = f / (ms * 1e-3) / 1e12
+            bound, roof = flops.roofline_tflops(f, nb, peak_tflops=peak)
+            print(json.dumps({"report": name, "variant": vname, "ms": round(ms, 4),
+                              "tflops": round(tf, 2), "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
+                              "bound": bound, "roofline_tflops": round(roof, 1),
+                              "frac_roofline": round(tf / roof, 4),
+                              "frac_peak": round(tf / peak, 4)}), flush=True)
+
+
+if __name__ == "__main__":
+    main()

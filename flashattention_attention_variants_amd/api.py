@@ -1,0 +1,189 @@
+"""ctypes binding of ``libflattn.so`` (entry points declared in include/flattn.h).
+
+Argument marshalling only: each function checks that the torch tensors are
+contiguous, on the GPU and of the right dtype, allocates the outputs it was
+not given, and passes raw device pointers plus torch's current HIP stream to
+the C entry point of the same name.  Every step of the computation runs in
+the library's kernels; there is no fallback.  A missing library or a
+non-zero status raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libflattn.so")
+
+FL_OK, FL_ERR_NULL, FL_ERR_SHAPE, FL_ERR_ALIGN, FL_ERR_UNSUPPORTED, FL_ERR_PARAM, FL_ERR_LAUNCH = range(7)
+FL_BF16, FL_F32 = 0, 1
+VARIANTS = {"vanilla": 0, "alibi": 1, "softcap": 2, "causal": 3, "sliding_window": 4,
+            "prefix_lm": 5, "document": 6}
+EVO_AXES = {"row": 0, "col": 1}
+SYMBOLS = ("fl_attn_fwd", "fl_diffattn_fwd", "fl_evoformer_gated_attn_fwd", "fl_status_str",
+           "fl_abi_version")
+
+
+class FlError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__("%s failed: status %d (%s)" % (fn, status, msg))
+        self.status = status
+
+
+class AttnParams(ctypes.Structure):
+    """Mirror of ``fl_attn_params``."""
+
+    _fields_ = [
+        ("variant", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("softcap", ctypes.c_float),
+        ("alibi_max_bias", ctypes.c_float),
+        ("window", ctypes.c_int32),
+        ("window_causal", ctypes.c_int32),
+        ("prefix", ctypes.c_int32),
+        ("n_docs", ctypes.c_int32),
+        ("doc_offsets", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str | None = None):
+    """Load the shared library (once); raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError("libflattn.so is not built (%s); run "
+                           "`python -m flashattention_attention_variants_amd.build`" % p)
+    lib = ctypes.CDLL(p)
+    V, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fl_attn_fwd.argtypes = [V, V, V, V, V, V, I, I, I, I, I, I, I, ctypes.POINTER(AttnParams), V]
+    lib.fl_diffattn_fwd.argtypes = [V, V, V, V, V, V, V, V, I, I, I, I, I, I, I, F, F, I, V]
+    lib.fl_evoformer_gated_attn_fwd.argtypes = [V, V, V, V, V, V, V, I, I, I, I, I, I, F, V]
+    for f in (lib.fl_attn_fwd, lib.fl_diffattn_fwd, lib.fl_evoformer_gated_attn_fwd):
+        f.restype = ctypes.c_int
+    lib.fl_status_str.argtypes = [I]
+    lib.fl_status_str.restype = ctypes.c_char_p
+    lib.fl_abi_version.argtypes = []
+    lib.fl_abi_version.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(fn, status):
+    if status != FL_OK:
+        raise FlError(fn, status, load_library().fl_status_str(status).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FL_BF16
+    if t.dtype == torch.float32:
+        return FL_F32
+    raise TypeError("dtype must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def fl_attn_fwd(q, k, v, *, variant="vanilla", scale=None, bias=None, softcap=50.0,
+                alibi_max_bias=8.0, window=256, window_causal=True, prefix=512,
+                doc_offsets=None, out=None, lse=None, return_lse=False, stream=None):
+    """softmax(score_mod(scale q k^T) + bias) v for q [B,Hq,Sq,D], k/v [B,Hkv,Sk,D].
+
+    Returns ``o`` or ``(o, lse)``; ``lse`` [B,Hq,Sq] float32 is computed when
+    given or when ``return_lse``.
+    """
+    q = _dev(q, "q")
+    dt = q.dtype
+    k, v = _dev(k, "k", dt), _dev(v, "v", dt)
+    bias = _dev(bias, "bias", dt)
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Sk, _ = k.shape
+    if out is None:
+        out = torch.empty(B, Hq, Sq, v.shape[3], dtype=dt, device=q.device)
+    _dev(out, "out", dt)
+    if lse is None and return_lse:
+        lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=q.device)
+    _dev(lse, "lse", torch.float32)
+    var = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    docs = None
+    if var == VARIANTS["document"]:
+        docs = _dev(doc_offsets, "doc_offsets", torch.int32)
+    p = AttnParams(var, float(scale if scale is not None else 1.0 / math.sqrt(D)), float(softcap),
+                   float(alibi_max_bias), int(window), int(bool(window_causal)), int(prefix),
+                   0 if docs is None else docs.shape[-1] - 1,
+                   None if docs is None else docs.data_ptr())
+    st = load_library().fl_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(out), _ptr(lse),
+                                    B, Hq, Hkv, Sq, Sk, D, _dtype_code(q), ctypes.byref(p),
+                                    _stream(stream))
+    _check("fl_attn_fwd", st)
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def fl_diffattn_fwd(q1, q2, k1, k2, v, *, lam=0.8, scale=None, causal=False, out=None,
+                    return_lse=False, stream=None):
+    """softmax(scale q1 k1^T) v - lam * softmax(scale q2 k2^T) v (MHA)."""
+    q1 = _dev(q1, "q1")
+    dt = q1.dtype
+    q2, k1, k2, v = (_dev(t, n, dt) for t, n in ((q2, "q2"), (k1, "k1"), (k2, "k2"), (v, "v")))
+    B, H, Sq, Dqk = q1.shape
+    Sk, Dv = v.shape[2], v.shape[3]
+    if out is None:
+        out = torch.empty(B, H, Sq, Dv, dtype=dt, device=q1.device)
+    _dev(out, "out", dt)
+    l1 = l2 = None
+    if return_lse:
+        l1 = torch.empty(B, H, Sq, dtype=torch.float32, device=q1.device)
+        l2 = torch.empty_like(l1)
+    st = load_library().fl_diffattn_fwd(_ptr(q1), _ptr(q2), _ptr(k1), _ptr(k2), _ptr(v), _ptr(out),
+                                        _ptr(l1), _ptr(l2), B, H, Sq, Sk, Dqk, Dv, _dtype_code(q1),
+                                        float(scale if scale is not None else 1.0 / math.sqrt(Dqk)),
+                                        float(lam), int(bool(causal)), _stream(stream))
+    _check("fl_diffattn_fwd", st)
+    return (out, l1, l2) if return_lse else out
+
+
+def fl_evoformer_gated_attn_fwd(q, k, v, gate, *, pair_bias=None, key_mask=None, axis="row",
+                                scale=None, out=None, stream=None):
+    """Evoformer gated self-attention on [N_seq, N_res, H, C] MSA tensors."""
+    q = _dev(q, "q")
+    dt = q.dtype
+    k, v, gate = _dev(k, "k", dt), _dev(v, "v", dt), _dev(gate, "gate", dt)
+    pair_bias = _dev(pair_bias, "pair_bias", dt)
+    key_mask = _dev(key_mask, "key_mask", torch.uint8)
+    N_seq, N_res, H, C = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", dt)
+    st = load_library().fl_evoformer_gated_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(pair_bias), _ptr(key_mask), _ptr(out),
+        N_seq, N_res, H, C, EVO_AXES[axis], _dtype_code(q),
+        float(scale if scale is not None else 1.0 / math.sqrt(C)), _stream(stream))
+    _check("fl_evoformer_gated_attn_fwd", st)
+    return out

@@ -1,0 +1,279 @@
+// fl_api.hip -- the C ABI: argument validation on the host, then one kernel
+// launch on the caller's stream.  No allocation, no synchronisation.
+#include <math.h>
+#include <stdint.h>
+
+#include "flattn.h"
+#include "fl_launch.hpp"
+
+using namespace fl;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p & (n - 1)) == 0; }
+
+constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+constexpr int kMaxSeq = 1 << 30;
+
+fl_status launch_status(hipError_t e) { return e == hipSuccess ? FL_OK : FL_ERR_LAUNCH; }
+
+void init_args(KernelArgs& a) {
+  a = KernelArgs{};
+  a.scale_log2 = 0.0f;
+  a.lambda = 0.0f;
+  a.iv_kind = IV_FULL;
+}
+
+// Contiguous [B, H, S, D] strides.
+void bhsd(int64_t H, int64_t S, int64_t D, int64_t& sb, int64_t& sh, int64_t& si) {
+  si = D;
+  sh = S * D;
+  sb = H * S * D;
+}
+
+int grid_qtiles(int S_q, int rows_per_wg) { return (S_q + rows_per_wg - 1) / rows_per_wg; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fl_status_str(fl_status s) {
+  switch (s) {
+    case FL_OK: return "ok";
+    case FL_ERR_NULL: return "a required pointer is NULL";
+    case FL_ERR_SHAPE: return "sizes inconsistent, negative or too large";
+    case FL_ERR_ALIGN: return "pointer or row not aligned as required";
+    case FL_ERR_UNSUPPORTED: return "head dimension / dtype combination not built";
+    case FL_ERR_PARAM: return "variant parameter out of range";
+    case FL_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int fl_abi_version(void) { return FL_ABI_VERSION; }
+
+fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* bias, void* o,
+                      float* lse, int B, int H_q, int H_kv, int S_q, int S_k, int D,
+                      fl_dtype dtype, const fl_attn_params* p, void* stream) {
+  if (!p) return FL_ERR_NULL;
+  if (B < 0 || H_q < 1 || H_kv < 1 || S_q < 0 || S_k < 0 || D < 1) return FL_ERR_SHAPE;
+  if (H_q % H_kv) return FL_ERR_SHAPE;
+  if (S_q > kMaxSeq || S_k > kMaxSeq) return FL_ERR_SHAPE;
+  if (dtype != FL_BF16 && dtype != FL_F32) return FL_ERR_UNSUPPORTED;
+  if (p->variant < FL_VANILLA || p->variant > FL_DOCUMENT) return FL_ERR_PARAM;
+  if (!isfinite(p->scale)) return FL_ERR_PARAM;
+  const bool positional = p->variant == FL_CAUSAL || p->variant == FL_SLIDING_WINDOW ||
+                          p->variant == FL_PREFIX_LM || p->variant == FL_DOCUMENT;
+  if (positional && S_q != S_k) return FL_ERR_SHAPE;
+  if (p->variant == FL_SOFTCAP && !(p->softcap > 0.0f && isfinite(p->softcap))) return FL_ERR_PARAM;
+  if (p->variant == FL_ALIBI && !(p->alibi_max_bias >= 0.0f && isfinite(p->alibi_max_bias)))
+    return FL_ERR_PARAM;
+  if (p->variant == FL_SLIDING_WINDOW && p->window < 1) return FL_ERR_PARAM;
+  if (p->variant == FL_PREFIX_LM && p->prefix < 0) return FL_ERR_PARAM;
+  if (p->variant == FL_DOCUMENT) {
+    if (p->n_docs < 1) return FL_ERR_PARAM;
+    if (!p->doc_offsets) return FL_ERR_NULL;
+  }
+  if (dtype == FL_BF16 && D != 64) return FL_ERR_UNSUPPORTED;
+  if (dtype == FL_F32 && D != 32 && D != 64 && D != 128) return FL_ERR_UNSUPPORTED;
+  if ((int64_t)B * H_q * S_q == 0) return FL_OK;  // no output element
+  if (!q || !o || (S_k > 0 && (!k || !v))) return FL_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(bias, 16) || !aligned(lse, 4))
+    return FL_ERR_ALIGN;
+  if (bias && dtype == FL_BF16 && S_k % 8) return FL_ERR_ALIGN;
+
+  KernelArgs a;
+  init_args(a);
+  a.q[0] = q;
+  a.k[0] = k;
+  a.v = v;
+  a.bias = bias;
+  a.o = o;
+  a.lse[0] = lse;
+  bhsd(H_q, S_q, D, a.q_sb, a.q_sh, a.q_si);
+  bhsd(H_kv, S_k, D, a.k_sb, a.k_sh, a.k_si);
+  bhsd(H_kv, S_k, D, a.v_sb, a.v_sh, a.v_si);
+  bhsd(H_q, S_q, D, a.o_sb, a.o_sh, a.o_si);
+  a.lse_sh = S_q;
+  a.lse_sb = (int64_t)H_q * S_q;
+  a.bias_si = S_k;
+  a.bias_sh = (int64_t)S_q * S_k;
+  a.nb = B;
+  a.nh = H_q;
+  a.group = H_q / H_kv;
+  a.sq = S_q;
+  a.sk = S_k;
+  a.scale_log2 = p->scale * kLog2e;
+  int mod = MOD_NONE;
+  switch (p->variant) {
+    case FL_ALIBI:
+      mod = MOD_ALIBI;
+      a.alibi_max_bias = p->alibi_max_bias;
+      break;
+    case FL_SOFTCAP:
+      mod = MOD_SOFTCAP;
+      a.softcap_arg = 2.0f * p->scale * kLog2e / p->softcap;
+      a.softcap_log2 = p->softcap * kLog2e;
+      break;
+    case FL_CAUSAL:
+      a.iv_kind = IV_CAUSAL;
+      a.heavy_first = 1;
+      break;
+    case FL_SLIDING_WINDOW:
+      a.iv_kind = p->window_causal ? IV_WINDOW_CAUSAL : IV_WINDOW_TWO_SIDED;
+      a.window = p->window > S_k + 1 ? S_k + 1 : p->window;  // wider windows change nothing
+      break;
+    case FL_PREFIX_LM:
+      a.iv_kind = IV_PREFIX;
+      a.prefix = p->prefix > S_k ? S_k : p->prefix;
+      a.heavy_first = 1;
+      break;
+    case FL_DOCUMENT:
+      a.iv_kind = IV_DOCUMENT;
+      a.n_docs = p->n_docs;
+      a.doc_offsets = p->doc_offsets;
+      break;
+    default:
+      break;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == FL_F32) {
+    a.n_qt = grid_qtiles(S_q, f32_rows_per_wg());
+    if ((int64_t)a.n_qt * B * H_q > kMaxGrid) return FL_ERR_SHAPE;
+    return launch_status(launch_f32(a, D, D, 1, mod, st));
+  }
+  // two 32-row blocks per wave when that still leaves enough work-groups to
+  // fill the 256 compute units twice
+  const int64_t wg2 = (int64_t)grid_qtiles(S_q, mfma_rows_per_wg(2)) * B * H_q;
+  const int qb = wg2 >= 512 ? 2 : 1;
+  a.n_qt = grid_qtiles(S_q, mfma_rows_per_wg(qb));
+  if ((int64_t)a.n_qt * B * H_q > kMaxGrid) return FL_ERR_SHAPE;
+  return launch_status(launch_attn_bf16(a, qb, mod, bias != nullptr, st));
+}
+
+fl_status fl_diffattn_fwd(const void* q1, const void* q2, const void* k1, const void* k2,
+                          const void* v, void* o, float* lse1, float* lse2, int B, int H,
+                          int S_q, int S_k, int D_qk, int D_v, fl_dtype dtype, float scale,
+                          float lambda, int causal, void* stream) {
+  if (B < 0 || H < 1 || S_q < 0 || S_k < 0 || D_qk < 1 || D_v < 1) return FL_ERR_SHAPE;
+  if (S_q > kMaxSeq || S_k > kMaxSeq) return FL_ERR_SHAPE;
+  if (causal && S_q != S_k) return FL_ERR_SHAPE;
+  if (dtype != FL_BF16 && dtype != FL_F32) return FL_ERR_UNSUPPORTED;
+  if (D_qk != 64 || (D_v != 64 && D_v != 128)) return FL_ERR_UNSUPPORTED;
+  if (!isfinite(scale) || !isfinite(lambda)) return FL_ERR_PARAM;
+  if ((int64_t)B * H * S_q == 0) return FL_OK;
+  if (!q1 || !q2 || !o || (S_k > 0 && (!k1 || !k2 || !v))) return FL_ERR_NULL;
+  if (!aligned(q1, 16) || !aligned(q2, 16) || !aligned(k1, 16) || !aligned(k2, 16) ||
+      !aligned(v, 16) || !aligned(o, 16) || !aligned(lse1, 4) || !aligned(lse2, 4))
+    return FL_ERR_ALIGN;
+
+  KernelArgs a;
+  init_args(a);
+  a.q[0] = q1;
+  a.q[1] = q2;
+  a.k[0] = k1;
+  a.k[1] = k2;
+  a.v = v;
+  a.o = o;
+  a.lse[0] = lse1;
+  a.lse[1] = lse2;
+  bhsd(H, S_q, D_qk, a.q_sb, a.q_sh, a.q_si);
+  bhsd(H, S_k, D_qk, a.k_sb, a.k_sh, a.k_si);
+  bhsd(H, S_k, D_v, a.v_sb, a.v_sh, a.v_si);
+  bhsd(H, S_q, D_v, a.o_sb, a.o_sh, a.o_si);
+  a.lse_sh = S_q;
+  a.lse_sb = (int64_t)H * S_q;
+  a.nb = B;
+  a.nh = H;
+  a.group = 1;
+  a.sq = S_q;
+  a.sk = S_k;
+  a.scale_log2 = scale * kLog2e;
+  a.lambda = lambda;
+  if (causal) {
+    a.iv_kind = IV_CAUSAL;
+    a.heavy_first = 1;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == FL_F32) {
+    a.n_qt = grid_qtiles(S_q, f32_rows_per_wg());
+    if ((int64_t)a.n_qt * B * H > kMaxGrid) return FL_ERR_SHAPE;
+    return launch_status(launch_f32(a, D_qk, D_v, 2, MOD_NONE, st));
+  }
+  a.n_qt = grid_qtiles(S_q, mfma_rows_per_wg(1));
+  if ((int64_t)a.n_qt * B * H > kMaxGrid) return FL_ERR_SHAPE;
+  return launch_status(launch_diff_bf16(a, D_qk, D_v, st));
+}
+
+fl_status fl_evoformer_gated_attn_fwd(const void* q, const void* k, const void* v,
+                                      const void* gate, const void* pair_bias,
+                                      const uint8_t* key_mask, void* o, int N_seq, int N_res,
+                                      int H, int C, fl_evo_axis axis, fl_dtype dtype,
+                                      float scale, void* stream) {
+  if (N_seq < 0 || N_res < 0 || H < 1 || C < 1) return FL_ERR_SHAPE;
+  if (N_seq > kMaxSeq || N_res > kMaxSeq) return FL_ERR_SHAPE;
+  if (axis != FL_EVO_ROW && axis != FL_EVO_COL) return FL_ERR_PARAM;
+  if (axis == FL_EVO_COL && pair_bias) return FL_ERR_PARAM;
+  if (dtype != FL_BF16 && dtype != FL_F32) return FL_ERR_UNSUPPORTED;
+  if (C != 32) return FL_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return FL_ERR_PARAM;
+  if ((int64_t)N_seq * N_res == 0) return FL_OK;
+  if (!q || !k || !v || !gate || !o) return FL_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(gate, 16) ||
+      !aligned(o, 16) || !aligned(pair_bias, 16))
+    return FL_ERR_ALIGN;
+  if (pair_bias && dtype == FL_BF16 && N_res % 8) return FL_ERR_ALIGN;
+
+  KernelArgs a;
+  init_args(a);
+  a.q[0] = q;
+  a.k[0] = k;
+  a.v = v;
+  a.gate = gate;
+  a.bias = pair_bias;
+  a.kmask = key_mask;
+  a.o = o;
+  const int64_t row = (int64_t)H * C;  // one (sequence, residue) position
+  int L;
+  if (axis == FL_EVO_ROW) {
+    // batch = MSA row s, positions = residues
+    a.nb = N_seq;
+    L = N_res;
+    a.q_sb = (int64_t)N_res * row;
+    a.q_si = row;
+    a.km_sb = N_res;
+    a.km_sj = 1;
+  } else {
+    // batch = residue column r, positions = sequences
+    a.nb = N_res;
+    L = N_seq;
+    a.q_sb = row;
+    a.q_si = (int64_t)N_res * row;
+    a.km_sb = 1;
+    a.km_sj = N_res;
+  }
+  a.q_sh = C;
+  a.k_sb = a.v_sb = a.o_sb = a.q_sb;
+  a.k_si = a.v_si = a.o_si = a.q_si;
+  a.k_sh = a.v_sh = a.o_sh = a.q_sh;
+  a.bias_si = L;
+  a.bias_sh = (int64_t)L * L;
+  a.nh = H;
+  a.group = 1;
+  a.sq = L;
+  a.sk = L;
+  a.scale_log2 = scale * kLog2e;
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == FL_F32) {
+    a.n_qt = grid_qtiles(L, f32_rows_per_wg());
+    if ((int64_t)a.n_qt * a.nb * H > kMaxGrid) return FL_ERR_SHAPE;
+    return launch_status(launch_f32(a, C, C, 1, MOD_NONE, st));
+  }
+  const int qb = L > 128 ? 2 : 1;
+  a.n_qt = grid_qtiles(L, mfma_rows_per_wg(qb));
+  if ((int64_t)a.n_qt * a.nb * H > kMaxGrid) return FL_ERR_SHAPE;
+  return launch_status(launch_evo_bf16(a, C, qb, pair_bias != nullptr, st));
+}
+
+}  // extern "C"

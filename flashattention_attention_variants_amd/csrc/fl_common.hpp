@@ -1,0 +1,155 @@
+// fl_common.hpp -- types, launch arguments and per-row key intervals shared
+// by the attention kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fl {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// Score modification applied to every score (FlexAttention's score_mod class).
+enum ModKind { MOD_NONE = 0, MOD_ALIBI = 1, MOD_SOFTCAP = 2 };
+
+// Every mask variant on the pages allows, for query i, one contiguous run of
+// keys [lo(i), hi(i)], and both ends never decrease as i grows.  That is
+// what lets a tile's fate (all allowed / none allowed / mixed) follow from
+// index arithmetic on its first and last query, with no mask tensor.
+enum IntervalKind {
+  IV_FULL = 0,              // vanilla, ALiBi, softcap: [0, S_k-1]
+  IV_CAUSAL = 1,            // [0, i]
+  IV_WINDOW_CAUSAL = 2,     // [i-W+1, i]
+  IV_WINDOW_TWO_SIDED = 3,  // [i-W+1, i+W-1]
+  IV_PREFIX = 4,            // [0, max(i, P-1)]
+  IV_DOCUMENT = 5           // [start(doc(i)), end(doc(i))-1]
+};
+
+// Everything a launch needs.  Strides are in elements; the head dimension is
+// always contiguous.  "b" is the batch index (the MSA row or column for the
+// Evoformer), "h" the query head, "i"/"j" query/key positions.
+struct KernelArgs {
+  const void* q[2];
+  const void* k[2];
+  const void* v;
+  const void* bias;        // [h][i][j], j contiguous
+  const void* gate;        // same layout and strides as o
+  const uint8_t* kmask;    // [b][j]
+  void* o;
+  float* lse[2];           // [b][h][i]
+  int64_t q_sb, q_sh, q_si;
+  int64_t k_sb, k_sh, k_si;  // head index is the K/V head
+  int64_t v_sb, v_sh, v_si;
+  int64_t o_sb, o_sh, o_si;
+  int64_t lse_sb, lse_sh;
+  int64_t bias_sh, bias_si;
+  int64_t km_sb, km_sj;
+  int nb, nh, group, sq, sk;  // group = H_q / H_kv
+  int n_qt;                   // query tiles per (b, h)
+  int iv_kind, window, prefix, n_docs;
+  const int32_t* doc_offsets;  // [b][n_docs+1]
+  float scale_log2;            // scale * log2(e)
+  float softcap_arg;           // 2 * scale * log2(e) / cap
+  float softcap_log2;          // cap * log2(e)
+  float alibi_max_bias;
+  float lambda;
+  int heavy_first;             // schedule the most expensive query tiles first
+};
+
+// Key interval [lo, hi] of query i, clamped to [0, S_k-1] (empty: lo > hi).
+__device__ __forceinline__ void key_interval(const KernelArgs& a, int b, int i, int& lo,
+                                             int& hi) {
+  switch (a.iv_kind) {
+    case IV_CAUSAL:
+      lo = 0;
+      hi = i;
+      break;
+    case IV_WINDOW_CAUSAL:
+      lo = i - a.window + 1;
+      hi = i;
+      break;
+    case IV_WINDOW_TWO_SIDED:
+      lo = i - a.window + 1;
+      hi = i + a.window - 1;
+      break;
+    case IV_PREFIX:
+      lo = 0;
+      hi = i > a.prefix - 1 ? i : a.prefix - 1;
+      break;
+    case IV_DOCUMENT: {
+      // largest d with off[d] <= i (binary search over n_docs+1 offsets)
+      const int32_t* off = a.doc_offsets + (int64_t)b * (a.n_docs + 1);
+      int dlo = 0, dhi = a.n_docs - 1;
+      while (dlo < dhi) {
+        const int mid = (dlo + dhi + 1) >> 1;
+        if (off[mid] <= i) dlo = mid; else dhi = mid - 1;
+      }
+      lo = off[dlo];
+      hi = off[dlo + 1] - 1;
+      break;
+    }
+    default:
+      lo = 0;
+      hi = a.sk - 1;
+      break;
+  }
+  lo = lo < 0 ? 0 : lo;
+  hi = hi > a.sk - 1 ? a.sk - 1 : hi;
+}
+
+// Work-group id -> (b*H + h, query tile).  Work-groups are dealt to the 8
+// XCDs round-robin by id, and each XCD has its own L2; when the (b, h) count
+// is a multiple of 8, every query tile of one (b, h) -- and, with contiguous
+// GQA groups, of one K/V head -- is placed on the same XCD so their K/V
+// reads share that L2.  Within an XCD the tiles go out tile-index-major, so
+// with heavy_first the most expensive tiles of every head start first.
+__device__ __forceinline__ void decode_tile(const KernelArgs& a, int bid, int& bh, int& qt) {
+  const int nbh = a.nb * a.nh;
+  int order;
+  if ((nbh & 7) == 0) {
+    const int hpx = nbh >> 3;
+    const int xcd = bid & 7, slot = bid >> 3;
+    bh = xcd * hpx + slot % hpx;
+    order = slot / hpx;
+  } else {
+    bh = bid % nbh;
+    order = bid / nbh;
+  }
+  qt = a.heavy_first ? a.n_qt - 1 - order : order;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// sigmoid(x) = 1 / (1 + e^-x)
+__device__ __forceinline__ float sigmoid(float x) {
+  return fast_rcp(1.0f + fast_exp2(-x * kLog2e));
+}
+
+// ALiBi slope of query head h: 2^(-max_bias * (h+1) / H), in log2 units of
+// the exponent (times log2 e) so it can be applied to base-2 scores.
+__device__ __forceinline__ float alibi_slope_log2(const KernelArgs& a, int h) {
+  return fast_exp2(-a.alibi_max_bias * (float)(h + 1) / (float)a.nh) * kLog2e;
+}
+
+// cap * tanh(y) in log2 units, from t = 2*y*log2(e):
+// tanh(y) = 1 - 2 / (e^(2y) + 1).
+__device__ __forceinline__ float softcap_log2(const KernelArgs& a, float raw) {
+  const float e = fast_exp2(raw * a.softcap_arg);
+  return a.softcap_log2 - 2.0f * a.softcap_log2 * fast_rcp(e + 1.0f);
+}
+
+__device__ __forceinline__ float bf16_to_f32(bf16 x) { return (float)x; }
+
+}  // namespace fl

@@ -1,0 +1,28 @@
+// fl_launch.hpp -- host-side launchers of the kernel families, one per
+// translation unit so the template instances compile in parallel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "fl_common.hpp"
+
+namespace fl {
+
+// bf16 attention, D = 64: qb = 32-query blocks per wave (1 or 2), mod =
+// ModKind, bias = additive [H_q, S_q, S_k] bias present.
+hipError_t launch_attn_bf16(const KernelArgs& a, int qb, int mod, bool bias, hipStream_t st);
+
+// bf16 differential attention: (dqk, dv) = (64, 128) or (64, 64).
+hipError_t launch_diff_bf16(const KernelArgs& a, int dqk, int dv, hipStream_t st);
+
+// bf16 Evoformer gated attention, C = 32: qb = 1 or 2, bias = pair bias.
+hipError_t launch_evo_bf16(const KernelArgs& a, int c, int qb, bool bias, hipStream_t st);
+
+// float32 path: (dqk, dv, ns, mod) as built in inst_f32.hip.
+hipError_t launch_f32(const KernelArgs& a, int dqk, int dv, int ns, int mod, hipStream_t st);
+
+// Query rows per work-group of each family.
+constexpr int mfma_rows_per_wg(int qb) { return 4 * 32 * qb; }
+constexpr int f32_rows_per_wg() { return 64; }
+
+}  // namespace fl

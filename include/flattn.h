@@ -1,0 +1,163 @@
+/*
+ * flattn.h -- C ABI of the fused attention-variant forward for AMD MI355X
+ * (gfx950).
+ *
+ * One entry point per operation family.  Each computes, in one kernel launch,
+ * the single-pass tiled attention forward softmax(score_mod(Q K^T) + bias) V
+ * with an online softmax: a running maximum and sum per query row, rescaled
+ * whenever the maximum grows (gist.science explainer of Flashlight, arXiv
+ * 2511.02043, "Technical Summary: Methodology", semantic fusion paragraph;
+ * papers.lqhl.me wiki, "核心方法").  Scores are never written to memory.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees or synchronises; the call enqueues one
+ *     kernel on `stream` (a hipStream_t; NULL = the default stream) and
+ *     returns.  Inputs are read-only; outputs must not alias inputs.
+ *   - Argument errors are detected on the host before anything is launched
+ *     and are returned synchronously (FL_ERR_*); nothing is written then.
+ *     A failed launch returns FL_ERR_LAUNCH.  Faults inside the kernel
+ *     surface at the caller's next synchronisation.
+ *   - Tensor pointers must be 16-byte aligned (the kernels move 128-bit
+ *     words); lse pointers 4-byte aligned.
+ *   - dtype FL_BF16: bfloat16 inputs and outputs, float32 accumulation,
+ *     probabilities rounded to bfloat16 (round to nearest even) before the
+ *     P.V product.  dtype FL_F32: float32 throughout.
+ *   - Every output element is written, including rows that no key may
+ *     attend to: such a row gets O = 0 and LSE = -inf.
+ *   - The library holds no state and is safe to call from several threads.
+ */
+#ifndef FLATTN_H
+#define FLATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FL_ABI_VERSION 1
+
+typedef enum {
+  FL_OK = 0,
+  FL_ERR_NULL = 1,        /* a required pointer is NULL */
+  FL_ERR_SHAPE = 2,       /* sizes inconsistent, negative or too large */
+  FL_ERR_ALIGN = 3,       /* a pointer or row is not aligned as required */
+  FL_ERR_UNSUPPORTED = 4, /* head dimension / dtype combination not built */
+  FL_ERR_PARAM = 5,       /* a variant parameter is out of range */
+  FL_ERR_LAUNCH = 6       /* the kernel launch failed */
+} fl_status;
+
+typedef enum { FL_BF16 = 0, FL_F32 = 1 } fl_dtype;
+
+/*
+ * The FlexAttention-expressible variants the pages evaluate (gist.science
+ * explainer, "Technical Summary: Results"; papers.lqhl.me wiki, "实验与结果").
+ * The pages name them without formulas; the definitions used are:
+ *   FL_VANILLA         every key.
+ *   FL_ALIBI           s -= slope_h * |i - j|, slope_h = 2^(-alibi_max_bias*(h+1)/H_q).
+ *   FL_SOFTCAP         s = softcap * tanh(s / softcap).
+ *   FL_CAUSAL          j <= i (top-left aligned).
+ *   FL_SLIDING_WINDOW  window_causal = 1: i - window < j <= i (window keys
+ *                      including the query itself); 0: |i - j| < window.
+ *   FL_PREFIX_LM       j < prefix or j <= i.
+ *   FL_DOCUMENT        query and key lie in the same document of
+ *                      doc_offsets (block diagonal, not causal).
+ * s is the scaled score scale * q.k; the score modification acts on s, the
+ * bias is added after it, and masked keys are excluded.
+ */
+typedef enum {
+  FL_VANILLA = 0,
+  FL_ALIBI = 1,
+  FL_SOFTCAP = 2,
+  FL_CAUSAL = 3,
+  FL_SLIDING_WINDOW = 4,
+  FL_PREFIX_LM = 5,
+  FL_DOCUMENT = 6
+} fl_variant;
+
+typedef struct {
+  int32_t variant;         /* fl_variant */
+  float scale;             /* multiplies q.k; usually 1/sqrt(D) */
+  float softcap;           /* FL_SOFTCAP: > 0 */
+  float alibi_max_bias;    /* FL_ALIBI: >= 0 */
+  int32_t window;          /* FL_SLIDING_WINDOW: >= 1 */
+  int32_t window_causal;   /* FL_SLIDING_WINDOW: 1 causal, 0 two-sided */
+  int32_t prefix;          /* FL_PREFIX_LM: >= 0 */
+  int32_t n_docs;          /* FL_DOCUMENT: >= 1 */
+  const int32_t* doc_offsets; /* FL_DOCUMENT: device [B][n_docs+1] int32,
+                                 0 = o_0 < o_1 < ... < o_n = S.  Not checked
+                                 on the host (it is device memory); offsets
+                                 outside [0, S] are clamped, never followed
+                                 out of bounds. */
+} fl_attn_params;
+
+/*
+ * Attention forward with a FlexAttention-class variant, MHA or GQA.
+ *   q    [B, H_q,  S_q, D]   contiguous
+ *   k    [B, H_kv, S_k, D]   contiguous; query head h uses K/V head
+ *   v    [B, H_kv, S_k, D]   h / (H_q / H_kv) (contiguous groups)
+ *   bias NULL or [H_q, S_q, S_k] additive score bias, shared by all B,
+ *        same dtype as q (FL_BF16 requires S_k % 8 == 0 with a bias)
+ *   o    [B, H_q, S_q, D]    output, same dtype as q
+ *   lse  NULL or [B, H_q, S_q] float32 natural-log logsumexp of the scores
+ * Requires H_q % H_kv == 0; S_q == S_k for the positional masks (causal,
+ * sliding window, PrefixLM, document).  D: 64 for FL_BF16; 32, 64 or 128
+ * for FL_F32.
+ */
+fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* bias,
+                      void* o, float* lse, int B, int H_q, int H_kv, int S_q, int S_k,
+                      int D, fl_dtype dtype, const fl_attn_params* params, void* stream);
+
+/*
+ * Differential attention: two softmax maps over the same values combined as
+ *   O = softmax(scale Q1 K1^T) V - lambda * softmax(scale Q2 K2^T) V
+ * with the same (optional causal, top-left) mask on both maps; MHA only.
+ * The pages name it as a variant FlexAttention cannot express (gist.science
+ * explainer, "Technical Summary: Problem Statement" and "Results") without a
+ * formula; this is the plain combination with a scalar lambda.
+ *   q1, q2 [B, H, S_q, D_qk]; k1, k2 [B, H, S_k, D_qk]; v [B, H, S_k, D_v]
+ *   o      [B, H, S_q, D_v]
+ *   lse1, lse2  NULL or [B, H, S_q] float32, one per map
+ * D_qk = 64 and D_v = 128 for FL_BF16 (64/64 also built); FL_F32 the same.
+ * causal requires S_q == S_k.
+ */
+fl_status fl_diffattn_fwd(const void* q1, const void* q2, const void* k1, const void* k2,
+                          const void* v, void* o, float* lse1, float* lse2, int B, int H,
+                          int S_q, int S_k, int D_qk, int D_v, fl_dtype dtype, float scale,
+                          float lambda, int causal, void* stream);
+
+typedef enum { FL_EVO_ROW = 0, FL_EVO_COL = 1 } fl_evo_axis;
+
+/*
+ * Evoformer gated self-attention on MSA tensors (AlphaFold2 layout), named on
+ * the pages as a data-dependent variant with a bias broadcast over an extra
+ * dimension (papers.lqhl.me wiki, "设计取舍"; gist.science explainer,
+ * "Technical Summary: Results").
+ *   q, k, v, gate, o  [N_seq, N_res, H, C] contiguous
+ *   axis FL_EVO_ROW: each MSA row attends along residues (N_res keys);
+ *        pair_bias NULL or [H, N_res(query), N_res(key)], shared by all rows;
+ *        key_mask NULL or [N_seq, N_res] uint8, 0 excludes that key.
+ *   axis FL_EVO_COL: each residue column attends along sequences (N_seq
+ *        keys) of the same tensors, read in place (no transpose); pair_bias
+ *        must be NULL; key_mask NULL or [N_seq, N_res], 0 excludes that key.
+ *   O[s, r, h, :] = sigmoid(gate[s, r, h, :]) * attention output.
+ * scale multiplies q.k only (usually 1/sqrt(C)).  C: 32 or 64 (FL_BF16),
+ * 32 or 64 (FL_F32).  With a pair bias, N_res % 8 == 0.
+ */
+fl_status fl_evoformer_gated_attn_fwd(const void* q, const void* k, const void* v,
+                                      const void* gate, const void* pair_bias,
+                                      const uint8_t* key_mask, void* o, int N_seq, int N_res,
+                                      int H, int C, fl_evo_axis axis, fl_dtype dtype,
+                                      float scale, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* fl_status_str(fl_status status);
+
+/* FL_ABI_VERSION of the library that was loaded. */
+int fl_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLATTN_H */

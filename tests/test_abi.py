@@ -1,0 +1,117 @@
+"""The C-ABI library loads, exports every symbol include/flattn.h declares,
+and rejects bad arguments on the host before anything is launched.
+
+No GPU is needed: every call here fails validation, which happens before the
+library touches the HIP runtime.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from flashattention_attention_variants_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "flattn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fl_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(api.LIB_PATH):
+        pytest.fail("libflattn.so is not built; run python -m flashattention_attention_variants_amd.build")
+    return api.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(api.SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.fl_abi_version() == 1
+    for s in range(7):
+        assert lib.fl_status_str(s)
+    assert lib.fl_status_str(99) == b"unknown status"
+
+
+P = ctypes.c_void_p
+FAKE = P(0x10000)        # 16-byte aligned, never dereferenced: validation fails first
+MISALIGNED = P(0x10008)
+
+
+def params(variant=0, **kw):
+    p = api.AttnParams(variant, 0.125, 50.0, 8.0, 256, 1, 512, 0, None)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def attn(lib, p, q=FAKE, k=FAKE, v=FAKE, bias=None, o=FAKE, lse=None, B=1, Hq=2, Hkv=2, Sq=8,
+         Sk=8, D=64, dt=api.FL_BF16):
+    return lib.fl_attn_fwd(q, k, v, bias, o, lse, B, Hq, Hkv, Sq, Sk, D, dt,
+                           None if p is None else ctypes.byref(p), None)
+
+
+def test_attn_validation(lib):
+    assert attn(lib, None) == api.FL_ERR_NULL
+    assert attn(lib, params(), q=None) == api.FL_ERR_NULL
+    assert attn(lib, params(), o=None) == api.FL_ERR_NULL
+    assert attn(lib, params(), Hq=3, Hkv=2) == api.FL_ERR_SHAPE
+    assert attn(lib, params(), B=-1) == api.FL_ERR_SHAPE
+    assert attn(lib, params(), D=48) == api.FL_ERR_UNSUPPORTED
+    assert attn(lib, params(), D=128) == api.FL_ERR_UNSUPPORTED          # bf16 is D=64 only
+    assert attn(lib, params(), dt=7) == api.FL_ERR_UNSUPPORTED
+    assert attn(lib, params(), q=MISALIGNED) == api.FL_ERR_ALIGN
+    assert attn(lib, params(), lse=P(0x10002)) == api.FL_ERR_ALIGN
+    assert attn(lib, params(), bias=FAKE, Sk=12, Sq=12) == api.FL_ERR_ALIGN  # bf16 bias rows
+    assert attn(lib, params(variant=9)) == api.FL_ERR_PARAM
+    assert attn(lib, params(variant=2, softcap=0.0)) == api.FL_ERR_PARAM
+    assert attn(lib, params(variant=2, softcap=float("inf"))) == api.FL_ERR_PARAM
+    assert attn(lib, params(variant=1, alibi_max_bias=-1.0)) == api.FL_ERR_PARAM
+    assert attn(lib, params(variant=4, window=0)) == api.FL_ERR_PARAM
+    assert attn(lib, params(variant=5, prefix=-1)) == api.FL_ERR_PARAM
+    assert attn(lib, params(variant=6, n_docs=0)) == api.FL_ERR_PARAM
+    assert attn(lib, params(variant=6, n_docs=2)) == api.FL_ERR_NULL     # no offsets
+    assert attn(lib, params(scale=float("nan"))) == api.FL_ERR_PARAM
+    for var in (3, 4, 5):  # positional masks need S_q == S_k
+        assert attn(lib, params(variant=var), Sq=8, Sk=16) == api.FL_ERR_SHAPE
+    # nothing to write: success without touching the pointers
+    assert attn(lib, params(), q=None, k=None, v=None, o=None, B=0) == api.FL_OK
+    assert attn(lib, params(), q=None, k=None, v=None, o=None, Sq=0) == api.FL_OK
+
+
+def test_diffattn_validation(lib):
+    f = lambda **kw: lib.fl_diffattn_fwd(*[kw.get(n, FAKE) for n in ("q1", "q2", "k1", "k2", "v", "o")],
+                                         kw.get("lse1"), kw.get("lse2"), kw.get("B", 1), 2,
+                                         kw.get("Sq", 8), kw.get("Sk", 8), kw.get("Dqk", 64),
+                                         kw.get("Dv", 128), kw.get("dt", api.FL_BF16), 0.125,
+                                         kw.get("lam", 0.8), kw.get("causal", 0), None)
+    assert f(q2=None) == api.FL_ERR_NULL
+    assert f(Dqk=32) == api.FL_ERR_UNSUPPORTED
+    assert f(Dv=96) == api.FL_ERR_UNSUPPORTED
+    assert f(causal=1, Sk=16) == api.FL_ERR_SHAPE
+    assert f(v=MISALIGNED) == api.FL_ERR_ALIGN
+    assert f(lam=float("inf")) == api.FL_ERR_PARAM
+    assert f(B=0, q1=None, q2=None) == api.FL_OK
+
+
+def test_evoformer_validation(lib):
+    f = lambda **kw: lib.fl_evoformer_gated_attn_fwd(
+        *[kw.get(n, FAKE) for n in ("q", "k", "v", "gate")], kw.get("bias"), kw.get("mask"),
+        kw.get("o", FAKE), kw.get("N_seq", 4), kw.get("N_res", 16), 2, kw.get("C", 32),
+        kw.get("axis", 0), kw.get("dt", api.FL_BF16), 0.17, None)
+    assert f(gate=None) == api.FL_ERR_NULL
+    assert f(C=16) == api.FL_ERR_UNSUPPORTED
+    assert f(axis=1, bias=FAKE) == api.FL_ERR_PARAM   # column attention has no pair bias
+    assert f(axis=2) == api.FL_ERR_PARAM
+    assert f(bias=FAKE, N_res=12) == api.FL_ERR_ALIGN
+    assert f(o=MISALIGNED) == api.FL_ERR_ALIGN
+    assert f(N_seq=0, q=None) == api.FL_OK

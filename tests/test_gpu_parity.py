@@ -1,0 +1,378 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Small problems are compared element by element on every output; the full
+workload sizes are compared on sampled rows the oracle computes one by one.
+Every input is seeded and synthetic (flashattention_attention_variants_amd.inputs).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from flashattention_attention_variants_amd import api, inputs
+from tests._gpu_common import check, errors, gpu_rows, np64, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = inputs.ALL_MASK_VARIANTS
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    oracle.build()
+    api.load_library()
+
+
+def variant_kw(variant, S, B, seed, window=37, prefix=50, n_docs=5, window_causal=True):
+    kw = dict(variant=variant)
+    if variant == "sliding_window":
+        kw.update(window=window, window_causal=window_causal)
+    elif variant == "prefix_lm":
+        kw.update(prefix=prefix)
+    elif variant == "softcap":
+        kw.update(softcap=50.0)
+    elif variant == "alibi":
+        kw.update(alibi_max_bias=8.0)
+    elif variant == "document":
+        kw.update(doc_offsets=inputs.doc_offsets(B, S, min(n_docs, S), seed))
+    return kw
+
+
+def run_gpu_attn(q, k, v, bias=None, **kw):
+    kw = dict(kw)
+    docs = kw.pop("doc_offsets", None)
+    o, lse = api.fl_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV),
+                             bias=None if bias is None else bias.to(DEV),
+                             doc_offsets=None if docs is None else docs.to(DEV),
+                             return_lse=True, **kw)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def run_oracle_attn(q, k, v, bias=None, rows=None, **kw):
+    kw = dict(kw)
+    docs = kw.pop("doc_offsets", None)
+    return oracle.attn(np64(q), np64(k), np64(v), bias=None if bias is None else np64(bias),
+                       doc_offsets=None if docs is None else docs.numpy(), rows=rows, **kw)
+
+
+# ---------------------------------------------------------------------------
+# float32: the 128-token MHA workload (with LSE) and every variant
+
+
+def test_f32_mha_s128_with_lse():
+    wl = inputs.WORKLOADS["mha_f32_b1_h2_s128_d64"]
+    t = inputs.make(wl)
+    o, lse = run_gpu_attn(t["q"], t["k"], t["v"])
+    ro, rl = run_oracle_attn(t["q"], t["k"], t["v"])
+    check(np64(o), ro, "f32", "O")
+    check(np64(lse), rl, "f32", "LSE")
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_f32_variants(variant, D):
+    B, Hq, Hkv, S = 2, 4, 2, 150
+    q, k, v = inputs.attn_inputs(B, Hq, Hkv, S, S, D, "f32", seed=11)
+    kw = variant_kw(variant, S, B, seed=12)
+    o, lse = run_gpu_attn(q, k, v, **kw)
+    ro, rl = run_oracle_attn(q, k, v, **kw)
+    check(np64(o), ro, "f32", variant)
+    check(np64(lse), rl, "f32", variant + " lse")
+
+
+# ---------------------------------------------------------------------------
+# bf16: every variant, GQA and MHA, ragged lengths spanning several tiles
+
+
+@pytest.mark.parametrize("S", [1, 17, 64, 100, 300, 513])
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_bf16_variants(variant, S):
+    B, Hq, Hkv, D = 2, 4, 2, 64
+    q, k, v = inputs.attn_inputs(B, Hq, Hkv, S, S, D, "bf16", seed=20 + S)
+    kw = variant_kw(variant, S, B, seed=21 + S)
+    o, lse = run_gpu_attn(q, k, v, **kw)
+    ro, rl = run_oracle_attn(q, k, v, **kw)
+    check(np64(o), ro, "bf16", "%s S=%d" % (variant, S))
+    mx, _, _ = errors(np64(lse), rl)
+    assert mx <= 2e-2, "lse %g" % mx
+
+
+@pytest.mark.parametrize("window_causal", [True, False])
+@pytest.mark.parametrize("window", [1, 64, 100, 1000])
+def test_bf16_window_shapes(window, window_causal):
+    B, H, S = 1, 2, 700
+    q, k, v = inputs.attn_inputs(B, H, H, S, S, 64, "bf16", seed=window)
+    kw = dict(variant="sliding_window", window=window, window_causal=window_causal)
+    o, _ = run_gpu_attn(q, k, v, **kw)
+    ro, _ = run_oracle_attn(q, k, v, **kw)
+    check(np64(o), ro, "bf16", "window %d" % window)
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_bf16_gqa_groups(group):
+    B, Hkv, S = 1, 2, 260
+    q, k, v = inputs.attn_inputs(B, Hkv * group, Hkv, S, S, 64, "bf16", seed=30 + group)
+    for variant in ("vanilla", "causal"):
+        o, _ = run_gpu_attn(q, k, v, variant=variant)
+        ro, _ = run_oracle_attn(q, k, v, variant=variant)
+        check(np64(o), ro, "bf16", "gqa %d %s" % (group, variant))
+
+
+def test_bf16_cross_lengths():
+    """S_q != S_k (vanilla, ALiBi, softcap allow it)."""
+    q, _, _ = inputs.attn_inputs(2, 2, 2, 77, 77, 64, "bf16", seed=40)
+    _, k, v = inputs.attn_inputs(2, 2, 2, 333, 333, 64, "bf16", seed=41)
+    for variant in ("vanilla", "alibi", "softcap"):
+        o, lse = run_gpu_attn(q, k, v, variant=variant)
+        ro, rl = run_oracle_attn(q, k, v, variant=variant)
+        check(np64(o), ro, "bf16", variant)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bias(dtype):
+    B, H, S = 2, 3, 136
+    q, k, v = inputs.attn_inputs(B, H, H, S, S, 64, dtype, seed=50)
+    bias = inputs.bias_inputs(H, S, S, dtype, seed=51)
+    for variant in ("vanilla", "causal", "alibi", "softcap"):
+        o, lse = run_gpu_attn(q, k, v, bias=bias, variant=variant)
+        ro, rl = run_oracle_attn(q, k, v, bias=bias, variant=variant)
+        check(np64(o), ro, dtype, "bias " + variant)
+
+
+# ---------------------------------------------------------------------------
+# discriminating cases: effects large against the tolerance
+
+
+def test_softcap_small_cap_sharpened():
+    """cap = 2 with Q scaled by 4: softcap moves O by far more than the
+    tolerance, and the GPU follows the oracle."""
+    B, H, S = 1, 4, 256
+    q, k, v = inputs.attn_inputs(B, H, H, S, S, 64, "bf16", seed=60)
+    q = (q.float() * 4).to(torch.bfloat16)
+    o, _ = run_gpu_attn(q, k, v, variant="softcap", softcap=2.0)
+    ro, _ = run_oracle_attn(q, k, v, variant="softcap", softcap=2.0)
+    check(np64(o), ro, "bf16", "softcap 2")
+    rv, _ = run_oracle_attn(q, k, v, variant="vanilla")
+    assert np.abs(ro - rv).max() > 0.3
+
+
+def test_alibi_closed_form_on_gpu():
+    """Q = 0, V = identity (S = D = 64): row i of O is r^|i-j| / Z_i."""
+    H, S = 8, 64
+    q = torch.zeros(1, H, S, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, H, S, 64, dtype=torch.bfloat16)
+    v = torch.eye(S, dtype=torch.bfloat16).expand(1, H, S, S).contiguous()
+    o, lse = run_gpu_attn(q, k, v, variant="alibi", alibi_max_bias=8.0)
+    got = np64(o)[0]
+    for h in range(H):
+        r = math.exp(-(2.0 ** (-8.0 * (h + 1) / H)))
+        i, j = np.arange(S)[:, None], np.arange(S)[None, :]
+        w = r ** np.abs(i - j)
+        want = w / w.sum(1, keepdims=True)
+        assert np.abs(got[h] - want).max() < 4e-3, h
+
+
+def test_uniform_scores_mean_of_values():
+    """Q = 0: causal O_i is the prefix mean of V, LSE_i = ln(i+1)."""
+    B, H, S = 1, 2, 333
+    _, k, v = inputs.attn_inputs(B, H, H, S, S, 64, "bf16", seed=61)
+    q = torch.zeros(B, H, S, 64, dtype=torch.bfloat16)
+    o, lse = run_gpu_attn(q, k, v, variant="causal")
+    vv = np64(v)
+    want = np.cumsum(vv, 2) / np.arange(1, S + 1)[None, None, :, None]
+    check(np64(o), want, "bf16", "prefix mean")
+    assert np.abs(np64(lse) - np.log(np.arange(1, S + 1))[None, None]).max() < 1e-3
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fully_masked_rows(dtype):
+    """A -inf bias row and an empty key set give O = 0 and LSE = -inf."""
+    B, H, S = 1, 2, 64
+    q, k, v = inputs.attn_inputs(B, H, H, S, S, 64, dtype, seed=62)
+    bias = torch.zeros(H, S, S, dtype=q.dtype)
+    bias[:, 5, :] = float("-inf")
+    o, lse = run_gpu_attn(q, k, v, bias=bias)
+    assert (np64(o)[:, :, 5] == 0).all() and np.isneginf(np64(lse)[:, :, 5]).all()
+    ro, rl = run_oracle_attn(q, k, v, bias=bias)
+    check(np64(o), ro, dtype, "masked row")
+    # no keys at all
+    k0 = torch.zeros(B, H, 0, 64, dtype=q.dtype)
+    o, lse = run_gpu_attn(q, k0, k0)
+    assert (np64(o) == 0).all() and np.isneginf(np64(lse)).all()
+
+
+def test_empty_queries():
+    q = torch.zeros(1, 2, 0, 64, dtype=torch.bfloat16)
+    _, k, v = inputs.attn_inputs(1, 2, 2, 10, 10, 64, "bf16", seed=63)
+    o, lse = run_gpu_attn(q, k, v)
+    assert o.shape == (1, 2, 0, 64)
+
+
+def test_deterministic_and_guarded_outputs():
+    """Two runs agree bit for bit; NaN guards around the output stay untouched."""
+    B, H, S = 2, 4, 1000
+    q, k, v = inputs.attn_inputs(B, H, H, S, S, 64, "bf16", seed=64)
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    n = B * H * S * 64
+    guard = 4096
+    buf = torch.full((n + 2 * guard,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    out = buf[guard:guard + n].view(B, H, S, 64)
+    outs = []
+    for variant in ("causal", "causal"):
+        api.fl_attn_fwd(q, k, v, variant=variant, out=out)
+        torch.cuda.synchronize()
+        outs.append(out.clone())
+    assert torch.equal(outs[0], outs[1])
+    assert torch.isnan(buf[:guard].float()).all() and torch.isnan(buf[guard + n:].float()).all()
+    assert torch.isfinite(out.float()).all()
+
+
+# ---------------------------------------------------------------------------
+# differential attention
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Dv", [64, 128])
+def test_diffattn_small(dtype, causal, Dv):
+    B, H, S = 2, 3, 190
+    q1, q2, k1, k2, v = inputs.diffattn_inputs(B, H, S, 64, Dv, dtype, seed=70)
+    g = [t.to(DEV) for t in (q1, q2, k1, k2, v)]
+    o, l1, l2 = api.fl_diffattn_fwd(*g, lam=0.8, causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl1, rl2 = oracle.diffattn(*(np64(t) for t in (q1, q2, k1, k2, v)), lam=0.8, causal=causal,
+                                   scale=0.125)
+    check(np64(o), ro, dtype, "diffattn")
+    check(np64(l1), rl1, "f32" if dtype == "f32" else "bf16", "lse1")
+    # lambda = 0 is vanilla attention of the first stream
+    o0 = api.fl_diffattn_fwd(*g, lam=0.0, causal=causal)
+    torch.cuda.synchronize()
+    rv, _ = oracle.attn(np64(q1), np64(k1), np64(v), variant="causal" if causal else "vanilla")
+    check(np64(o0), rv, dtype, "diffattn lambda 0")
+
+
+# ---------------------------------------------------------------------------
+# Evoformer gated attention
+
+
+def evo_small(dtype, N_seq=6, N_res=72, H=4, C=32, seed=80):
+    q, k, v, gate, bias, km = inputs.evoformer_inputs(N_seq, N_res, H, C, dtype, seed)
+    km[1, :] = 0          # a fully masked MSA row
+    km[:, 3] = 0          # a fully masked residue column
+    return q, k, v, gate, bias, km
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_evoformer_row(dtype, with_bias):
+    q, k, v, gate, bias, km = evo_small(dtype)
+    pb = bias if with_bias else None
+    o = api.fl_evoformer_gated_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), gate.to(DEV),
+                                        pair_bias=None if pb is None else pb.to(DEV),
+                                        key_mask=km.to(DEV), axis="row")
+    torch.cuda.synchronize()
+    ro = oracle.evoformer(np64(q), np64(k), np64(v), np64(gate),
+                          pair_bias=None if pb is None else np64(pb), key_mask=km.numpy(), axis="row")
+    check(np64(o), ro, dtype, "evoformer row")
+    assert (np64(o)[1] == 0).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("N_seq", [40, 129, 200])
+def test_evoformer_col(dtype, N_seq):
+    q, k, v, gate, _, km = evo_small(dtype, N_seq=N_seq, N_res=24)
+    o = api.fl_evoformer_gated_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), gate.to(DEV),
+                                        key_mask=km.to(DEV), axis="col")
+    torch.cuda.synchronize()
+    ro = oracle.evoformer(np64(q), np64(k), np64(v), np64(gate), key_mask=km.numpy(), axis="col")
+    check(np64(o), ro, dtype, "evoformer col")
+    assert (np64(o)[:, 3] == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# full workload sizes, sampled rows
+
+
+def _full_attn(name, variants, n_rows):
+    wl = inputs.WORKLOADS[name]
+    t = inputs.make(wl)
+    s = wl.shape
+    q, k, v = t["q"].to(DEV), t["k"].to(DEV), t["v"].to(DEV)
+    q64, k64, v64 = np64(t["q"]), np64(t["k"]), np64(t["v"])
+    rows = sample_rows(s["B"], s["Hq"], s["S"], n_rows, seed=len(name))
+    for variant in variants:
+        kw = dict(variant=variant)
+        for key in ("softcap", "alibi_max_bias", "window", "window_causal", "prefix"):
+            if key in wl.params:
+                kw[key] = wl.params[key]
+        docs = t.get("doc_offsets")
+        if variant == "document":
+            kw["doc_offsets"] = docs
+        o, lse = run_gpu_attn(q, k, v, **kw)
+        kw.pop("doc_offsets", None)
+        ro, rl = oracle.attn(q64, k64, v64, rows=rows,
+                             doc_offsets=None if variant != "document" else docs.numpy(), **kw)
+        check(gpu_rows(o, rows), ro, "bf16", "%s %s" % (name, variant))
+        mx, _, _ = errors(np64(lse).reshape(-1)[rows], rl)
+        assert mx < 2e-2, (variant, mx)
+        assert torch.isfinite(o.float()).all()
+
+
+def test_full_mha_s2048_all_variants():
+    _full_attn("mha_bf16_b4_h16_s2048_d64", inputs.ALL_MASK_VARIANTS, 384)
+
+
+def test_full_mha_s4096_all_variants():
+    _full_attn("mha_bf16_b4_h16_s4096_d64", inputs.ALL_MASK_VARIANTS, 256)
+
+
+def test_full_gqa_s16384():
+    _full_attn("gqa_bf16_b1_hq32_hkv8_s16384_d64", ("causal", "sliding_window"), 192)
+
+
+def test_full_diffattn_s4096():
+    wl = inputs.WORKLOADS["diffattn_bf16_b4_h16_s4096_dqk64_dv128"]
+    t = inputs.make(wl)
+    s = wl.shape
+    g = [t[n].to(DEV) for n in ("q1", "q2", "k1", "k2", "v")]
+    c = [np64(t[n]) for n in ("q1", "q2", "k1", "k2", "v")]
+    rows = sample_rows(s["B"], s["H"], s["S"], 192, seed=4)
+    for causal in (False, True):
+        o = api.fl_diffattn_fwd(*g, lam=wl.params["lam"], causal=causal)
+        torch.cuda.synchronize()
+        ro, _, _ = oracle.diffattn(*c, lam=wl.params["lam"], causal=causal, scale=0.125, rows=rows)
+        check(gpu_rows(o, rows), ro, "bf16", "diffattn causal=%s" % causal)
+
+
+def test_full_evoformer():
+    wl = inputs.WORKLOADS["evoformer_bf16_nseq128_nres256_h8_c32"]
+    t = inputs.make(wl)
+    g = {n: t[n].to(DEV) for n in ("q", "k", "v", "gate", "pair_bias", "key_mask")}
+    c = {n: np64(t[n]) for n in ("q", "k", "v", "gate", "pair_bias")}
+    km = t["key_mask"].numpy()
+    N_seq, N_res, H, C = t["q"].shape
+    rng = np.random.default_rng(5)
+    # row-wise: sampled (s, r, h) positions
+    rows = np.unique(rng.choice(N_seq * N_res * H, 2048, replace=False))
+    o = api.fl_evoformer_gated_attn_fwd(g["q"], g["k"], g["v"], g["gate"], pair_bias=g["pair_bias"],
+                                        key_mask=g["key_mask"], axis="row")
+    torch.cuda.synchronize()
+    ro = oracle.evoformer(c["q"], c["k"], c["v"], c["gate"], pair_bias=c["pair_bias"], key_mask=km,
+                          axis="row", rows=rows)
+    check(np64(o).reshape(-1, C)[rows], ro, "bf16", "evoformer row")
+    # column-wise: the oracle indexes the transposed problem (r*N_seq + s)*H + h
+    o = api.fl_evoformer_gated_attn_fwd(g["q"], g["k"], g["v"], g["gate"], key_mask=g["key_mask"],
+                                        axis="col")
+    torch.cuda.synchronize()
+    ro = oracle.evoformer(c["q"], c["k"], c["v"], c["gate"], key_mask=km, axis="col", rows=rows)
+    h = rows % H
+    s_ = (rows // H) % N_seq
+    r_ = rows // (H * N_seq)
+    got = np64(o)[s_, r_, h]
+    check(got, ro, "bf16", "evoformer col")
