@@ -33,6 +33,12 @@ void bhsd(int64_t H, int64_t S, int64_t D, int64_t& sb, int64_t& sh, int64_t& si
 
 int grid_qtiles(int S_q, int rows_per_wg) { return (S_q + rows_per_wg - 1) / rows_per_wg; }
 
+// The matrix-core kernels address one (batch, K/V head) block of K and of V
+// through 32-bit byte offsets.
+bool span_ok(int64_t rows, int64_t row_stride, int64_t width) {
+  return rows <= 0 || ((rows - 1) * row_stride + width) * 2 < ((int64_t)1 << 31);
+}
+
 }  // namespace
 
 extern "C" {
@@ -143,6 +149,7 @@ fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* b
     if ((int64_t)a.n_qt * B * H_q > kMaxGrid) return FL_ERR_SHAPE;
     return launch_status(launch_f32(a, D, D, 1, mod, st));
   }
+  if (!span_ok(S_k, D, D)) return FL_ERR_SHAPE;
   // two 32-row blocks per wave when that still leaves enough work-groups to
   // fill the 256 compute units twice
   const int64_t wg2 = (int64_t)grid_qtiles(S_q, mfma_rows_per_wg(2)) * B * H_q;
@@ -201,6 +208,7 @@ fl_status fl_diffattn_fwd(const void* q1, const void* q2, const void* k1, const 
     if ((int64_t)a.n_qt * B * H > kMaxGrid) return FL_ERR_SHAPE;
     return launch_status(launch_f32(a, D_qk, D_v, 2, MOD_NONE, st));
   }
+  if (!span_ok(S_k, D_v, D_v)) return FL_ERR_SHAPE;
   a.n_qt = grid_qtiles(S_q, mfma_rows_per_wg(1));
   if ((int64_t)a.n_qt * B * H > kMaxGrid) return FL_ERR_SHAPE;
   return launch_status(launch_diff_bf16(a, D_qk, D_v, st));
@@ -270,6 +278,7 @@ fl_status fl_evoformer_gated_attn_fwd(const void* q, const void* k, const void* 
     if ((int64_t)a.n_qt * a.nb * H > kMaxGrid) return FL_ERR_SHAPE;
     return launch_status(launch_f32(a, C, C, 1, MOD_NONE, st));
   }
+  if (!span_ok(L, a.k_si, C)) return FL_ERR_SHAPE;
   const int qb = L > 128 ? 2 : 1;
   a.n_qt = grid_qtiles(L, mfma_rows_per_wg(qb));
   if ((int64_t)a.n_qt * a.nb * H > kMaxGrid) return FL_ERR_SHAPE;

@@ -103,7 +103,8 @@ typedef struct {
  *   lse  NULL or [B, H_q, S_q] float32 natural-log logsumexp of the scores
  * Requires H_q % H_kv == 0; S_q == S_k for the positional masks (causal,
  * sliding window, PrefixLM, document).  D: 64 for FL_BF16; 32, 64 or 128
- * for FL_F32.
+ * for FL_F32.  FL_BF16 also requires S_k * D * 2 < 2^31 (one K/V head block
+ * is addressed with 32-bit byte offsets); larger S_k returns FL_ERR_SHAPE.
  */
 fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* bias,
                       void* o, float* lse, int B, int H_q, int H_kv, int S_q, int S_k,
