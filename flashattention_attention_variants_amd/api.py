@@ -53,11 +53,13 @@ _lib = None
 
 
 def load_library(path: str | None = None):
-    """Load the shared library (once); raises if it has not been built."""
+    """Load the shared library (once); raises if it has not been built.
+
+    FLATTN_LIB, when set, names another build of the same library."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("FLATTN_LIB") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError("libflattn.so is not built (%s); run "
                            "`python -m flashattention_attention_variants_amd.build`" % p)

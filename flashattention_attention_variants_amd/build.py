@@ -38,6 +38,17 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
+def _check_stubs(objs: list[str]) -> None:
+    """Every kernel launch stub an object references must be defined in it
+    (clang can drop a stub silently when the host pass rejects a kernel)."""
+    for o in objs:
+        r = subprocess.run(["nm", o], capture_output=True, text=True)
+        missing = [l.split()[-1] for l in r.stdout.splitlines()
+                   if l.split()[0] == "U" and "__device_stub__" in l]
+        if missing:
+            raise RuntimeError("%s: kernel stubs not emitted: %s" % (o, ", ".join(missing[:3])))
+
+
 def build(jobs: int | None = None, extra: list[str] | None = None, verbose: bool = False) -> str:
     """Compile every HIP source and link the library; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
@@ -45,6 +56,7 @@ def build(jobs: int | None = None, extra: list[str] | None = None, verbose: bool
     jobs = jobs or max(1, min(len(srcs), os.cpu_count() or 1, 8))
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra or []), srcs))
+    _check_stubs(objs)
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

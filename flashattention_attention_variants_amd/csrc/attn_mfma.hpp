@@ -50,18 +50,28 @@ struct MfmaCfg {
   static constexpr int NW = 4;               // waves per work-group
   static constexpr int BM = NW * 32 * QB;    // query rows per work-group
   static constexpr int BN = 64;              // keys per tile
-  static constexpr int KP = DQK + 8;         // LDS row pitch of K (bf16): conflict-free b128 reads
-  static constexpr int VP = DV + 16;         // LDS row pitch of V (bf16): conflict-free tr reads
-  static constexpr int K_ELEMS = BN * KP;
-  static constexpr int V_ELEMS = BN * VP;
+  // K and V tiles sit in LDS row-major without padding; the 16-byte chunks
+  // of a row are XOR-swizzled by the row index so that the operand reads
+  // (eight consecutive K rows per 128-byte b128 group; four V rows x two
+  // chunks per transposed-read group) hit distinct banks.
+  static constexpr int KCPR = DQK / 8;       // 16-byte chunks per K row
+  static constexpr int VCPR = DV / 8;        // 16-byte chunks per V row
+  static constexpr int K_ELEMS = BN * DQK;
+  static constexpr int V_ELEMS = BN * DV;
   static constexpr int STAGE = NS * K_ELEMS + V_ELEMS;
+  static constexpr int STAGES = 3;           // tiles t (in use), t+1 (landed), t+2 (in flight)
+  __device__ static constexpr int kswz(int row) { return KCPR == 4 ? (row >> 1) & 3 : row & 7; }
+  __device__ static constexpr int vswz(int row) { return VCPR == 4 ? 2 * ((row >> 1) & 1) : 2 * (row & 3); }
   static constexpr int KCH = BN * DQK / 8 / (NW * 64);  // 16-byte K chunks per thread
   static constexpr int VCH = BN * DV / 8 / (NW * 64);   // 16-byte V chunks per thread
   // plain scores: no modification, bias or key mask; the scale then folds
   // into the exponent (one fma per score)
   static constexpr bool PLAIN = (MOD == MOD_NONE) && !BIAS && !KMASK;
   // one stream fits 2 waves per SIMD; two streams need the whole register file
-  static constexpr int WAVES_PER_EU = NS == 1 ? 2 : 1;
+#ifndef FL_QB1_WAVES
+#define FL_QB1_WAVES 2
+#endif
+  static constexpr int WAVES_PER_EU = NS == 1 ? (QB == 1 ? FL_QB1_WAVES : 2) : 1;
   static_assert(DQK % 16 == 0 && DV % 32 == 0, "head dims");
   static_assert(KCH >= 1 && VCH >= 1, "tile too small for the work-group");
 };
@@ -75,6 +85,17 @@ __device__ __forceinline__ bf16x8 load16(__amdgpu_buffer_rsrc_t rs, int byte_off
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0));
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds + 16*l (lds is wave-uniform).  The builtin exists only in the device
+// pass; keeping it out of the host pass keeps the kernel's host-side launch
+// stub intact.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, void* lds, int byte_off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
+                                           byte_off, 0, 0, 0);
+#endif
+}
+
 // Buffer resource over [base, base + bytes); 0x00020000 is the raw 32-bit
 // data-format word of gfx9 buffer descriptors.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -82,13 +103,42 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
+#ifndef FL_SCHED_INTERLEAVE
+#define FL_SCHED_INTERLEAVE 1
+#endif
+#ifndef FL_SCHED_VALU_PER_MFMA
+#define FL_SCHED_VALU_PER_MFMA 4
+#endif
+
+// Scheduling shape of one pipeline unit's basic block (the previous unit's
+// P.V products, this unit's successor's S^T products, this unit's
+// exponentials): operand reads from LDS first, then each matrix instruction
+// followed by a few independent vector instructions, so the matrix core runs
+// while the wave keeps issuing vector work.
+__device__ __forceinline__ void interleave_hint() {
+#if FL_SCHED_INTERLEAVE == 1
+  __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, FL_SCHED_VALU_PER_MFMA, 0);  // a few VALU
+  }
+#elif FL_SCHED_INTERLEAVE == 2
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+#endif
+}
+
 template <class C>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_EU)))
 void attn_mfma_kernel(KernelArgs a) {
   constexpr int BN = C::BN, DQK = C::DQK, DV = C::DV, NS = C::NS, QB = C::QB;
-  constexpr int KP = C::KP, VP = C::VP;
-  __shared__ __attribute__((aligned(16))) bf16 lds[2 * C::STAGE];
-  __shared__ __attribute__((aligned(16))) float kmadd[C::KMASK ? 2 * BN : 4];
+  __shared__ __attribute__((aligned(16))) bf16 lds[C::STAGES * C::STAGE];
+  __shared__ __attribute__((aligned(16))) float kmadd[C::KMASK ? C::STAGES * BN : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -124,46 +174,79 @@ void attn_mfma_kernel(KernelArgs a) {
 
   // ---- Q operands in registers ---------------------------------------------
   // B operand of S^T = K Q^T: lane (c, g) holds Q[row c][16t + 8g .. +7].
+  // Plain scores: Q is pre-multiplied by scale*log2(e) (one bf16 rounding), so
+  // S^T comes out in base-2 units.
   bf16x8 qreg[NS][QB][DQK / 16];
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
+  for (int s = 0; s < NS; ++s) {
+    // rows past S_q read as zeros through the bounds-checked resource
+    const bf16* qh = (const bf16*)a.q[s] + b * a.q_sb + h * a.q_sh;
+    const int64_t q_row_b = a.q_si * 2;
+    const int64_t q_span = (int64_t)(a.sq - 1) * q_row_b + DQK * 2 - (int64_t)wq0 * q_row_b;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qh + (int64_t)wq0 * a.q_si, q_span);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const int qi = wq0 + 32 * qb + c;
-      const bf16* qp = (const bf16*)a.q[s] + b * a.q_sb + h * a.q_sh + (int64_t)qi * a.q_si;
 #pragma unroll
       for (int t = 0; t < DQK / 16; ++t) {
-        bf16x8 z = {};
-        qreg[s][qb][t] = qi < a.sq ? *(const bf16x8*)(qp + 16 * t + 8 * g) : z;
+        qreg[s][qb][t] = load16(qrs, (32 * qb + c) * (int)q_row_b + 32 * t + 16 * g);
+        if constexpr (C::PLAIN) {
+          f32x8 f = __builtin_convertvector(qreg[s][qb][t], f32x8);
+          qreg[s][qb][t] = __builtin_convertvector(f * a.scale_log2, bf16x8);
+        }
       }
     }
+  }
 
   // ---- per-row softmax state -------------------------------------------------
   f32x16 oacc[NS][QB][DV / 32];
   float m_run[NS][QB], l_run[NS][QB];
+  bool m_set[NS][QB];
+  // Plain scores: one more k-step of the S^T product adds -m to every score
+  // (A operand: ones in k-slots 0..2 of lane half 0; B operand: -m split into
+  // three bf16 parts hi + mid + lo, exact in the fp32 accumulation), so
+  // p = 2^S needs no vector arithmetic before the exponential.
+  bf16x8 qext[NS][QB];
+  const bf16x8 kext = g == 0 ? bf16x8{(bf16)1.0f, (bf16)1.0f, (bf16)1.0f, (bf16)0.0f, (bf16)0.0f,
+                                      (bf16)0.0f, (bf16)0.0f, (bf16)0.0f}
+                             : bf16x8{};
 #pragma unroll
   for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      m_run[s][qb] = kNegInf;
+      // plain: m = 0 is a placeholder until the row's first allowed keys set it
+      m_run[s][qb] = C::PLAIN ? 0.0f : kNegInf;
+      m_set[s][qb] = false;
       l_run[s][qb] = 0.0f;
+      qext[s][qb] = bf16x8{};
 #pragma unroll
       for (int db = 0; db < DV / 32; ++db) oacc[s][qb][db] = f32x16{};
     }
+  auto set_qext = [&](int s, int qb, float m) {
+    const float nm = -m;
+    const bf16 hi = (bf16)nm;
+    const bf16 mid = (bf16)(nm - (float)hi);
+    const bf16 lo = (bf16)(nm - (float)hi - (float)mid);
+    qext[s][qb] = g == 0 ? bf16x8{hi, mid, lo, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f,
+                                  (bf16)0.0f}
+                         : bf16x8{};
+  };
 
-  // Scores live in base 2: plain scores keep q.k and fold scale*log2(e) into
-  // the exponent; modified scores are converted to base-2 units first.
-  const float cf = C::PLAIN ? a.scale_log2 : 1.0f;
-  // Lazy rescale: the running max used in the exponent only moves when a
-  // score exceeds it by more than 8 (base 2), so p <= 256 and most tiles
-  // skip the accumulator rescale.  Exact: numerator and denominator share it.
-  const float thr = 8.0f / cf;
+  // Scores live in base 2.  Modified scores are converted to base-2 units
+  // after the product and use a lazy rescale: the running max used in the
+  // exponent only moves when a score exceeds it by more than 8, so p <= 256
+  // and most tiles skip the accumulator rescale.  Exact: numerator and
+  // denominator share the reference.
+  const float thr = 8.0f;
   const float alibi_l2 = C::MOD == MOD_ALIBI ? alibi_slope_log2(a, h) : 0.0f;
 
-  // ---- global -> register -> LDS tile movement -------------------------------
-  // Each (b, K/V head) block is addressed through a bounds-checked buffer
-  // resource re-based at every tile, so keys past S_k read as zeros with no
-  // per-lane predicate.
+  // ---- global -> LDS tile movement ---------------------------------------------
+  // K and V tiles go from global memory straight into LDS (buffer loads with
+  // the LDS flag: no registers, no LDS store instructions), two tiles ahead of
+  // the one being consumed.  Each (b, K/V head) block is addressed through a
+  // bounds-checked buffer resource re-based at every tile, so keys past S_k
+  // read as zeros.  One load instruction of a wave fills 1 KiB of LDS in lane
+  // order, so the swizzled layout is realised by choosing, per lane, which
+  // global 16-byte chunk to fetch.
   const char* kblk[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s)
@@ -173,108 +256,182 @@ void attn_mfma_kernel(KernelArgs a) {
   const int64_t k_span = a.sk > 0 ? (int64_t)(a.sk - 1) * k_row_b + DQK * 2 : 0;
   const int64_t v_span = a.sk > 0 ? (int64_t)(a.sk - 1) * v_row_b + DV * 2 : 0;
 
-  int k_off[C::KCH], k_lds[C::KCH], v_off[C::VCH], v_lds[C::VCH];
+  int k_off[C::KCH], v_off[C::VCH];
 #pragma unroll
   for (int i = 0; i < C::KCH; ++i) {
-    const int chunk = tid + 256 * i;
-    const int key = chunk / (DQK / 8), col = chunk % (DQK / 8);
-    k_off[i] = key * (int)k_row_b + 16 * col;
-    k_lds[i] = key * KP + 8 * col;
+    const int q = (i * 4 + w) * 64 + lane;  // 16-byte slot in the K tile
+    const int row = q / C::KCPR, phys = q % C::KCPR;
+    k_off[i] = row * (int)k_row_b + 16 * (phys ^ C::kswz(row));
   }
 #pragma unroll
   for (int i = 0; i < C::VCH; ++i) {
-    const int chunk = tid + 256 * i;
-    const int key = chunk / (DV / 8), col = chunk % (DV / 8);
-    v_off[i] = key * (int)v_row_b + 16 * col;
-    v_lds[i] = key * VP + 8 * col;
+    const int q = (i * 4 + w) * 64 + lane;
+    const int row = q / C::VCPR, phys = q % C::VCPR;
+    v_off[i] = row * (int)v_row_b + 16 * (phys ^ C::vswz(row));
   }
-
-  bf16x8 kpre[NS][C::KCH], vpre[C::VCH];
   float kmpre = 0.0f;
 
-  auto load_tile = [&](int kt) {
+  // issue the loads of tile kt into LDS stage `stage`
+  auto load_tile = [&](int kt, int stage) {
     const int64_t j0 = (int64_t)kt * BN;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(kblk[s] + j0 * k_row_b, k_span - j0 * k_row_b);
-#pragma unroll
-      for (int i = 0; i < C::KCH; ++i) kpre[s][i] = load16(rs, k_off[i]);
-    }
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(vblk + j0 * v_row_b, v_span - j0 * v_row_b);
-#pragma unroll
-    for (int i = 0; i < C::VCH; ++i) vpre[i] = load16(rs, v_off[i]);
     if (C::KMASK && tid < BN) {
       const int j = (int)j0 + tid;
       kmpre = (j < a.sk && (!a.kmask || a.kmask[b * a.km_sb + (int64_t)j * a.km_sj] != 0))
                   ? 0.0f
                   : kNegInf;
     }
-  };
-
-  auto store_tile = [&](int stage) {
     bf16* ks = lds + stage * C::STAGE;
-    bf16* vs = ks + NS * C::K_ELEMS;
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+    for (int s = 0; s < NS; ++s) {
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(kblk[s] + j0 * k_row_b, k_span - j0 * k_row_b);
 #pragma unroll
-      for (int i = 0; i < C::KCH; ++i) *(bf16x8*)(ks + s * C::K_ELEMS + k_lds[i]) = kpre[s][i];
+      for (int i = 0; i < C::KCH; ++i) lds_load16(rs, ks + s * C::K_ELEMS + (i * 4 + w) * 512, k_off[i]);
+    }
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(vblk + j0 * v_row_b, v_span - j0 * v_row_b);
 #pragma unroll
-    for (int i = 0; i < C::VCH; ++i) *(bf16x8*)(vs + v_lds[i]) = vpre[i];
+    for (int i = 0; i < C::VCH; ++i) lds_load16(rs, ks + NS * C::K_ELEMS + (i * 4 + w) * 512, v_off[i]);
+  };
+  // the key-mask column of a tile travels through a register
+  auto store_kmask = [&](int stage) {
     if (C::KMASK && tid < BN) kmadd[stage * BN + tid] = kmpre;
   };
 
-  // LDS element offsets of this lane's operand reads
-  const int k_rd = c * KP + 8 * g;  // + 32kb*KP + 16t
-  // transposed V read: lane i of each 16-lane block points at row (i/4) of a
-  // 4-key group and 4 d-columns (i%4) of the block's 16 columns
-  const int v_rd = (4 * g + ((c & 15) >> 2)) * VP + 16 * (c >> 4) + 4 * (c & 3);  // + 16st*VP + 32db
+  // LDS element offsets of this lane's operand reads.  K: row 32kb + c,
+  // logical 16-byte chunk 2t + g.
+  int k_rd[DQK / 16];
+#pragma unroll
+  for (int t = 0; t < DQK / 16; ++t) k_rd[t] = c * DQK + 8 * ((2 * t + g) ^ C::kswz(c));  // + 32kb*DQK
+  // Transposed V read: lane i of each 16-lane block points at row i/4 of a
+  // 4-key group and 4 d-columns 4*(i%4) of the block's 16 columns.  The row
+  // index mod 4 fixes the swizzle, so it is the same for every 4-key group.
+  const int v_row = 4 * g + ((c & 15) >> 2);
+  int v_rd[DV / 32];
+#pragma unroll
+  for (int db = 0; db < DV / 32; ++db) {
+    const int d = 32 * db + 16 * (c >> 4) + 4 * (c & 3);
+    v_rd[db] = v_row * DV + 8 * ((d >> 3) ^ C::vswz(v_row)) + (d & 7);  // + 16st*DV (+ 8*DV)
+  }
 
   // ---- one key tile: S^T, softmax update, O^T += V^T P^T ---------------------
-  // Work units u = (stream s, query block qb) run as a two-stage pipeline:
-  // the S^T products of unit u+1 are issued before the softmax of unit u, so
-  // the matrix cores work while the vector ALUs exponentiate, and P.V of unit
-  // u follows its softmax at once so P dies early.
-  auto compute_tile = [&](int stage, int kt, auto masked_tag) {
+  // Work units u = (stream s, 32-key half kb, query block qb) run as a
+  // two-stage pipeline: the S^T product of unit u+1 is issued before the
+  // softmax of unit u, so the matrix cores work while the vector ALUs
+  // exponentiate, and P.V of unit u follows its softmax at once so P dies
+  // early.  The running reference of a row never needs a tile-wide maximum,
+  // so the two key halves of a tile are independent units.
+  auto compute_tile = [&](int stage, int kt, const bf16x8 (&vop)[2][DV / 32][2], auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    constexpr int U = NS * QB;
+    constexpr int U = NS * 2 * QB;
     const bf16* ks = lds + stage * C::STAGE;
     const bf16* vs = ks + NS * C::K_ELEMS;
     const int j0 = kt * BN;
 
-    bf16x8 kop[2][DQK / 16];  // K operands of the current stream
-    auto read_k = [&](int s) {
+    bf16x8 kop[DQK / 16];  // K operands of the current (stream, key half)
+    auto read_k = [&](int s, int kb) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t = 0; t < DQK / 16; ++t)
-          kop[kb][t] = *(const bf16x8*)(ks + s * C::K_ELEMS + k_rd + 32 * kb * KP + 16 * t);
+      for (int t = 0; t < DQK / 16; ++t)
+        kop[t] = *(const bf16x8*)(ks + s * C::K_ELEMS + k_rd[t] + 32 * kb * DQK);
     };
-    auto qk = [&](int u, f32x16 (&acc)[2]) {
-      const int s = u / QB, qb = u % QB;
-      if (qb == 0) read_k(s);
+    auto qk = [&](int s, int qb, f32x16& acc) {
+      acc = f32x16{};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        acc[kb] = f32x16{};
+      for (int t = 0; t < DQK / 16; ++t)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[t], qreg[s][qb][t], acc, 0, 0, 0);
+      if constexpr (C::PLAIN)  // + (-m): the running-reference subtraction
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kext, qext[s][qb], acc, 0, 0, 0);
+    };
+    auto mask = [&](f32x16& acc, int kb, int qb) {
 #pragma unroll
-        for (int t = 0; t < DQK / 16; ++t)
-          acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kb][t], qreg[s][qb][t], acc[kb], 0, 0, 0);
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + 32 * kb + 4 * g + acc_row(r);
+        acc[r] = (j >= row_lo[qb] && j <= row_hi[qb]) ? acc[r] : kNegInf;
       }
     };
+    // p = 2^(x - shift) of a unit's 16 scores, rounded to bf16 in the
+    // B-operand order of the P.V product (16-key steps 2kb and 2kb+1);
+    // returns this lane's sum of the rounded values.
+    auto exp_pack = [&](const f32x16& x, bf16x8 (&pk)[2], float shift) {
+      float part[2] = {0.0f, 0.0f};  // two partial sums keep the add chain short
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        f32x8 p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = fast_exp2(x[8 * h2 + e] - shift);
+        pk[h2] = __builtin_convertvector(p, bf16x8);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          bf16x2 pr = {pk[h2][e], pk[h2][e + 1]};
+          const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+          part[h2] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, part[h2], false);
+        }
+      }
+      return part[0] + part[1];
+    };
 
-    f32x16 sacc[2][2];  // [pipeline slot][32-key block]
-    qk(0, sacc[0]);
+    f32x16 sacc[2];  // [pipeline slot]
+    read_k(0, 0);
+    qk(0, 0, sacc[0]);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int s = u / QB, qb = u % QB;
-      if (u + 1 < U) qk(u + 1, sacc[(u + 1) & 1]);
-      f32x16 (&sc)[2] = sacc[u & 1];
+      const int s = u / (2 * QB), kb = (u / QB) % 2, qb = u % QB;
+      if (u + 1 < U) {
+        const int s1 = (u + 1) / (2 * QB), kb1 = ((u + 1) / QB) % 2, qb1 = (u + 1) % QB;
+        if (qb1 == 0) read_k(s1, kb1);
+        qk(s1, qb1, sacc[(u + 1) & 1]);
+      }
+      f32x16& sc = sacc[u & 1];
       const int qi = wq0 + 32 * qb + c;
+      const int jb = j0 + 32 * kb + 4 * g;  // key of register 0 in this lane
+      bf16x8 pk[2];
 
-      // score modification, bias, key mask, positional mask
-      float xm = kNegInf;
+      if constexpr (C::PLAIN) {
+        // S^T already holds (score - m) in base 2.
+        if constexpr (MASKED) mask(sc, kb, qb);
+        float lsum = exp_pack(sc, pk, 0.0f);
+        // The reference m is revisited only when it is unset for a row that
+        // has allowed keys here, or when the unit's terms grew past 2^64
+        // (inf included): then both halves of the row agree on a new
+        // reference, the accumulator is rescaled and the scores are
+        // recomputed and re-exponentiated.  Wave-uniform, rarely taken.
+        const bool has_key = row_hi[qb] >= j0 + 32 * kb && row_lo[qb] <= j0 + 32 * kb + 31 &&
+                             row_lo[qb] <= row_hi[qb];
+        const bool redo = (!m_set[s][qb] && has_key) || !(lsum <= 0x1p64f);
+        interleave_hint();
+        if (__builtin_amdgcn_ballot_w64(redo)) {
+          f32x16 rs = f32x16{};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int jb = j0 + 32 * kb + 4 * g;  // key of register 0 in this lane
+          for (int t = 0; t < DQK / 16; ++t) {
+            const bf16x8 ka = *(const bf16x8*)(ks + s * C::K_ELEMS + k_rd[t] + 32 * kb * DQK);
+            rs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s][qb][t], rs, 0, 0, 0);
+          }
+          rs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kext, qext[s][qb], rs, 0, 0, 0);
+          if constexpr (MASKED) mask(rs, kb, qb);
+          float xm = kNegInf;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xm = fmaxf(xm, rs[r]);
+          xm = fmaxf(xm, __shfl_xor(xm, 32));
+          // move when the reference is unset, or when terms reach 2^32
+          const bool move = xm != kNegInf && (!m_set[s][qb] || xm > 32.0f);
+          const float shift = move ? xm : 0.0f;
+          const float alpha = !move ? 1.0f : (m_set[s][qb] ? fast_exp2(-shift) : 0.0f);
+          l_run[s][qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DV / 32; ++db) oacc[s][qb][db] *= alpha;
+          if (move) {
+            m_run[s][qb] += shift;
+            m_set[s][qb] = true;
+          }
+          set_qext(s, qb, m_run[s][qb]);
+          // the next unit's scores, already issued, may belong to the same rows
+          if (u + 1 < U && (u + 1) % QB == qb && (u + 1) / (2 * QB) == s) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[(u + 1) & 1][r] -= shift;
+          }
+          lsum = exp_pack(rs, pk, shift);
+        }
+        l_run[s][qb] += lsum;
+      } else {
+        // score modification, bias, key mask, positional mask
         float bias_v[16];
         if constexpr (C::BIAS) {
           const int qi_c = min(qi, a.sq - 1);
@@ -297,101 +454,120 @@ void attn_mfma_kernel(KernelArgs a) {
             for (int e = 0; e < 4; ++e) km_v[4 * r4 + e] = kv[e];
           }
         }
+        float xm = kNegInf;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = sc[kb][r];
+          float x = sc[r];
           if constexpr (C::MOD == MOD_ALIBI) {
             const float dist = (float)(qi - jb - acc_row(r));
             x = x * a.scale_log2 - alibi_l2 * __builtin_fabsf(dist);
           } else if constexpr (C::MOD == MOD_SOFTCAP) {
             x = softcap_log2(a, x);
-          } else if constexpr (!C::PLAIN) {
+          } else {
             x = x * a.scale_log2;
           }
           if constexpr (C::BIAS) x += bias_v[r];
           if constexpr (C::KMASK) x += km_v[r];
-          if constexpr (MASKED) {
-            const int j = jb + acc_row(r);
-            x = (j >= row_lo[qb] && j <= row_hi[qb]) ? x : kNegInf;
-          }
-          sc[kb][r] = x;
-          xm = fmaxf(xm, x);
+          sc[r] = x;
         }
-      }
-      // xm covers this lane's half of the row's keys; the other half sits in
-      // the lane 32 apart.  Both lanes of a row must use the same running
-      // max, so the halves are combined only when some lane of the wave
-      // would move it (a wave-uniform, rarely taken branch).
-      const float m_old = m_run[s][qb];
-      if (__builtin_amdgcn_ballot_w64(xm > m_old + thr)) {
-        const float xf = fmaxf(xm, __shfl_xor(xm, 32));
-        const bool move = xf > m_old + thr;
-        const float m_new = move ? xf : m_old;
-        const float alpha = !move ? 1.0f : (m_old == kNegInf ? 0.0f : fast_exp2((m_old - m_new) * cf));
-        l_run[s][qb] *= alpha;
+        if constexpr (MASKED) mask(sc, kb, qb);
 #pragma unroll
-        for (int db = 0; db < DV / 32; ++db) oacc[s][qb][db] *= alpha;
-        m_run[s][qb] = m_new;
-      }
-      const float nm = m_run[s][qb] == kNegInf ? 0.0f : -m_run[s][qb] * cf;
-
-      // p = 2^(x*cf - m*cf), rounded to bf16 in the B-operand order of the
-      // P.V product; the row sum adds the rounded values.
-      bf16x8 pk[4];
-      float lsum = 0.0f;
+        for (int r = 0; r < 16; ++r) xm = fmaxf(xm, sc[r]);
+        // xm covers this lane's half of the row's keys; the other half sits
+        // in the lane 32 apart.  Both lanes of a row must use the same
+        // reference, so the halves are combined only when some lane of the
+        // wave would move it (wave-uniform, rarely taken).
+        const float m_old = m_run[s][qb];
+        interleave_hint();
+        if (__builtin_amdgcn_ballot_w64(xm > m_old + thr)) {
+          const float xf = fmaxf(xm, __shfl_xor(xm, 32));
+          const bool move = xf > m_old + thr;
+          const float m_new = move ? xf : m_old;
+          const float alpha = !move ? 1.0f : (m_old == kNegInf ? 0.0f : fast_exp2(m_old - m_new));
+          l_run[s][qb] *= alpha;
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        f32x8 p;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          p[e] = fast_exp2(__builtin_fmaf(sc[st >> 1][8 * (st & 1) + e], cf, nm));
-        pk[st] = __builtin_convertvector(p, bf16x8);
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          bf16x2 pr = {pk[st][e], pk[st][e + 1]};
-          const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, lsum, false);
+          for (int db = 0; db < DV / 32; ++db) oacc[s][qb][db] *= alpha;
+          m_run[s][qb] = m_new;
         }
+        const float shift = m_run[s][qb] == kNegInf ? 0.0f : m_run[s][qb];
+        l_run[s][qb] += exp_pack(sc, pk, shift);
       }
-      l_run[s][qb] += lsum;
 
-      // O^T += V^T P^T.  A operand of lane (c, g): V^T[d = 32db + c][keys
-      // 16st + 4g + 0..3, 16st + 8 + 4g + 0..3], two transposed 8-byte reads.
+      // O^T += V^T P^T over this unit's 32 keys.  A operand of lane (c, g):
+      // V^T[d = 32db + c][keys 16st + 4g + 0..3, 16st + 8 + 4g + 0..3], two
+      // transposed 8-byte reads made at the start of the tile.
 #pragma unroll
       for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-          const bf16* vp = vs + v_rd + 16 * st * VP + 32 * db;
-          const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
-          const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * VP));
-          const bf16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-          oacc[s][qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk[st], oacc[s][qb][db], 0, 0, 0);
-        }
+        for (int h2 = 0; h2 < 2; ++h2)
+          oacc[s][qb][db] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[kb][db][h2], pk[h2], oacc[s][qb][db], 0, 0, 0);
     }
   };
 
+  // V^T operands of a whole tile (A operands of the P.V products): lane
+  // (c, g) holds V^T[d = 32db + c][keys 16st + 4g + 0..3, 16st + 8 + 4g + 0..3]
+  // for the 16-key step st = 2kb + h2, from two transposed 8-byte reads.
+  auto read_v_tile = [&](int stage, bf16x8 (&vop)[2][DV / 32][2]) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    const bf16* vs = lds + stage * C::STAGE + NS * C::K_ELEMS;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const bf16* vp = vs + v_rd[db] + 16 * (2 * kb + h2) * DV;
+          const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
+          const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * DV));
+          vop[kb][db][h2] = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        }
+  };
+
   // ---- main loop ---------------------------------------------------------------
+  // Tile kt is consumed from stage (kt - kt_lo) % 3 while tile kt+1 has
+  // landed and tile kt+2 is in flight.  The V^T operands of tile kt are read
+  // before tile kt+2's loads are issued (those reads then never wait on
+  // loads still in flight), the K operands as the units need them.  The
+  // barrier at the end of an iteration both publishes tile kt+1 (every wave
+  // waited for its own loads) and frees the stage of tile kt for reuse.
+  constexpr int LOADS = NS * C::KCH + C::VCH;  // LDS-bound loads per thread per tile
+  static_assert(LOADS < 64, "vmcnt range");
+  // Publish a landed tile: wait for this wave's loads of it (leaving the
+  // newest tile's LOADS in flight when asked) and its LDS stores, then the
+  // work-group barrier.  Written out because __syncthreads() also waits for
+  // the tile still in flight.  The memory clobber keeps the compiler from
+  // moving memory accesses across it.
+  auto sync_tile = [&](bool leave_one_tile) {
+    if (leave_one_tile)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LOADS) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
   if (kt_lo < kt_hi) {
-    load_tile(kt_lo);
-    store_tile(0);
-    __syncthreads();
+    load_tile(kt_lo, 0);
+    store_kmask(0);
+    const bool two = kt_lo + 1 < kt_hi;
+    if (two) load_tile(kt_lo + 1, 1);
+    sync_tile(two);
   }
   for (int kt = kt_lo; kt < kt_hi; ++kt) {
-    const int stage = (kt - kt_lo) & 1;
-    const bool more = kt + 1 < kt_hi;
-    if (more) load_tile(kt + 1);
+    const int stage = (kt - kt_lo) % 3;
+    const bool next = kt + 1 < kt_hi, next2 = kt + 2 < kt_hi;
     const int j0 = kt * BN, j1 = j0 + BN - 1;
     const bool empty = wave_idle || j0 > w_hi_max || j1 < w_lo_min;
     const bool full = j0 >= w_lo_max && j1 <= w_hi_min;
+    bf16x8 vop[2][DV / 32][2];
+    if (!empty) read_v_tile(stage, vop);
+    if (next) store_kmask(stage == 2 ? 0 : stage + 1);
+    if (next2) load_tile(kt + 2, stage == 0 ? 2 : stage - 1);
     if (!empty) {
       if (full)
-        compute_tile(stage, kt, std::integral_constant<bool, false>{});
+        compute_tile(stage, kt, vop, std::integral_constant<bool, false>{});
       else
-        compute_tile(stage, kt, std::integral_constant<bool, true>{});
+        compute_tile(stage, kt, vop, std::integral_constant<bool, true>{});
     }
-    if (more) store_tile(stage ^ 1);
-    __syncthreads();
+    if (next) sync_tile(next2);
   }
 
   // ---- epilogue: normalise, combine, gate, store --------------------------------
@@ -405,7 +581,7 @@ void attn_mfma_kernel(KernelArgs a) {
       const int qi = wq0 + 32 * qb + c;
       if (a.lse[s] && g == 0 && qi < a.sq) {
         const float m = m_run[s][qb];
-        const float lse = l > 0.0f ? (m * cf + __builtin_log2f(l)) * kLn2 : kNegInf;
+        const float lse = l > 0.0f ? (m + __builtin_log2f(l)) * kLn2 : kNegInf;
         a.lse[s][b * a.lse_sb + h * a.lse_sh + qi] = lse;
       }
     }

@@ -153,7 +153,11 @@ fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* b
   // two 32-row blocks per wave when that still leaves enough work-groups to
   // fill the 256 compute units twice
   const int64_t wg2 = (int64_t)grid_qtiles(S_q, mfma_rows_per_wg(2)) * B * H_q;
+#ifdef FL_FORCE_QB
+  const int qb = FL_FORCE_QB;
+#else
   const int qb = wg2 >= 512 ? 2 : 1;
+#endif
   a.n_qt = grid_qtiles(S_q, mfma_rows_per_wg(qb));
   if ((int64_t)a.n_qt * B * H_q > kMaxGrid) return FL_ERR_SHAPE;
   return launch_status(launch_attn_bf16(a, qb, mod, bias != nullptr, st));
