@@ -64,9 +64,10 @@ struct MfmaCfg {
   __device__ static constexpr int vswz(int row) { return VCPR == 4 ? 2 * ((row >> 1) & 1) : 2 * (row & 3); }
   static constexpr int KCH = BN * DQK / 8 / (NW * 64);  // 16-byte K chunks per thread
   static constexpr int VCH = BN * DV / 8 / (NW * 64);   // 16-byte V chunks per thread
-  // plain scores: no modification, bias or key mask; the scale then folds
-  // into the exponent (one fma per score)
-  static constexpr bool PLAIN = (MOD == MOD_NONE) && !BIAS && !KMASK;
+  // Folded scores: the scale, the running reference and (for ALiBi) the
+  // distance penalty all enter the S^T product itself.
+  static constexpr bool FOLD = (MOD == MOD_NONE || MOD == MOD_ALIBI) && !BIAS && !KMASK;
+  static constexpr bool ALIBI_FOLD = FOLD && MOD == MOD_ALIBI;
   // one stream fits 2 waves per SIMD; two streams need the whole register file
 #ifndef FL_QB1_WAVES
 #define FL_QB1_WAVES 2
@@ -101,6 +102,47 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, void* lds,
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Four transposed 8-byte LDS reads (ds_read_b64_tr_b16) from one address at
+// immediate byte offsets.  They are written as assembly because the
+// compiler's wait-count pass cannot tell them apart from the tile loads still
+// streaming into other LDS stages and would make them wait for those loads.
+// The results may be used only after lds_fence() has taken them.
+template <int O0, int O1, int O2, int O3>
+__device__ __forceinline__ void ds_read_tr4(uint32_t addr, u32x2& r0, u32x2& r1, u32x2& r2, u32x2& r3) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%5\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %2, %4 offset:%7\n\t"
+      "ds_read_b64_tr_b16 %3, %4 offset:%8"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(addr), "n"(O0), "n"(O1), "n"(O2), "n"(O3));
+}
+
+// Wait for this wave's outstanding LDS reads; the registers pass through the
+// statement, so no use of them can be scheduled before the wait.
+__device__ __forceinline__ void lds_fence(u32x2 (&r)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+}
+__device__ __forceinline__ void lds_fence(u32x2 (&r)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]),
+                 "+v"(r[7]));
+}
+__device__ __forceinline__ void lds_fence(u32x2 (&r)[16]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]),
+                 "+v"(r[7]), "+v"(r[8]), "+v"(r[9]), "+v"(r[10]), "+v"(r[11]), "+v"(r[12]),
+                 "+v"(r[13]), "+v"(r[14]), "+v"(r[15]));
 }
 
 #ifndef FL_SCHED_INTERLEAVE
@@ -174,8 +216,8 @@ void attn_mfma_kernel(KernelArgs a) {
 
   // ---- Q operands in registers ---------------------------------------------
   // B operand of S^T = K Q^T: lane (c, g) holds Q[row c][16t + 8g .. +7].
-  // Plain scores: Q is pre-multiplied by scale*log2(e) (one bf16 rounding), so
-  // S^T comes out in base-2 units.
+  // Folded scores: Q is pre-multiplied by scale*log2(e) (one bf16 rounding),
+  // so S^T comes out in base-2 units.
   bf16x8 qreg[NS][QB][DQK / 16];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -189,7 +231,7 @@ void attn_mfma_kernel(KernelArgs a) {
 #pragma unroll
       for (int t = 0; t < DQK / 16; ++t) {
         qreg[s][qb][t] = load16(qrs, (32 * qb + c) * (int)q_row_b + 32 * t + 16 * g);
-        if constexpr (C::PLAIN) {
+        if constexpr (C::FOLD) {
           f32x8 f = __builtin_convertvector(qreg[s][qb][t], f32x8);
           qreg[s][qb][t] = __builtin_convertvector(f * a.scale_log2, bf16x8);
         }
@@ -201,35 +243,71 @@ void attn_mfma_kernel(KernelArgs a) {
   f32x16 oacc[NS][QB][DV / 32];
   float m_run[NS][QB], l_run[NS][QB];
   bool m_set[NS][QB];
-  // Plain scores: one more k-step of the S^T product adds -m to every score
-  // (A operand: ones in k-slots 0..2 of lane half 0; B operand: -m split into
-  // three bf16 parts hi + mid + lo, exact in the fp32 accumulation), so
-  // p = 2^S needs no vector arithmetic before the exponential.
+  // Folded scores: one more k-step of the S^T product adds the terms of the
+  // score that are not q.k.  Only lane half 0 (k-slots 0..7) carries them;
+  // half 1 of the key-side operand is zero.  For the tile at key j0, key
+  // j = j0 + ck (ck = 32kb + row of the key half) and sigma = +1 on key
+  // blocks wholly at or below the diagonal (j <= i), -1 wholly above:
+  //   k-slot  0      A = 1    B = -m                     (m kept bf16-exact)
+  //   k-slots 1..3   A = 1    B = -sigma*slope*(i - j0)  (3 bf16 parts)
+  //   k-slots 4..6   A = ck   B = sigma*slope            (3 parts)
+  // so S = q.k*scale*log2(e) - m - sigma*slope*(i - j), slope in base-2
+  // units: the running reference and the ALiBi distance penalty.  Each
+  // product is exact (ck < 64 is exact in bf16; three bf16 parts carry an
+  // fp32 value), so p = 2^S needs no vector arithmetic before the
+  // exponential.  The row term is rebuilt once per tile; sigma = -1 flips
+  // the sign bits of slots 1..6.  Blocks that straddle the diagonal take
+  // sigma = +1 and a vector correction for j > i.  Plain scores use slot 0.
   bf16x8 qext[NS][QB];
-  const bf16x8 kext = g == 0 ? bf16x8{(bf16)1.0f, (bf16)1.0f, (bf16)1.0f, (bf16)0.0f, (bf16)0.0f,
-                                      (bf16)0.0f, (bf16)0.0f, (bf16)0.0f}
-                             : bf16x8{};
+  const bf16 one = (bf16)1.0f, zero = (bf16)0.0f;
+  auto split3 = [](float x, bf16& hi, bf16& mid, bf16& lo) {
+    hi = (bf16)x;
+    mid = (bf16)(x - (float)hi);
+    lo = (bf16)(x - (float)hi - (float)mid);
+  };
+  const float alibi_l2 = C::MOD == MOD_ALIBI ? alibi_slope_log2(a, h) : 0.0f;
+  bf16 sl0, sl1, sl2;
+  split3(alibi_l2, sl0, sl1, sl2);
+  // query-side operand for reference m (bf16-exact) and, under ALiBi, the
+  // tile at j0
+  auto set_qext = [&](int s, int qb, float m, int j0) {
+    const bf16 mt = (bf16)(-m);
+    if constexpr (C::ALIBI_FOLD) {
+      bf16 x0, x1, x2;
+      split3(-alibi_l2 * (float)(wq0 + 32 * qb + c - j0), x0, x1, x2);
+      qext[s][qb] = bf16x8{mt, x0, x1, x2, sl0, sl1, sl2, zero};
+    } else {
+      qext[s][qb] = bf16x8{mt, zero, zero, zero, zero, zero, zero, zero};
+    }
+  };
+  // key-side operand of key half kb
+  auto kext = [&](int kb) {
+    if constexpr (C::ALIBI_FOLD) {
+      const bf16 ck = (bf16)(float)(32 * kb + c);
+      return g == 0 ? bf16x8{one, one, one, one, ck, ck, ck, zero} : bf16x8{};
+    } else {
+      return g == 0 ? bf16x8{one, zero, zero, zero, zero, zero, zero, zero} : bf16x8{};
+    }
+  };
+  // sigma = -1: negate k-slots 1..6 of the query-side operand
+  auto flip = [](bf16x8 x) {
+    u32x4 w = __builtin_bit_cast(u32x4, x);
+    w ^= (u32x4){0x80000000u, 0x80008000u, 0x80008000u, 0x00008000u};
+    return __builtin_bit_cast(bf16x8, w);
+  };
 #pragma unroll
   for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      // plain: m = 0 is a placeholder until the row's first allowed keys set it
-      m_run[s][qb] = C::PLAIN ? 0.0f : kNegInf;
+      // folded: m = 0 is a placeholder until the row's first allowed keys set it
+      m_run[s][qb] = C::FOLD ? 0.0f : kNegInf;
       m_set[s][qb] = false;
       l_run[s][qb] = 0.0f;
       qext[s][qb] = bf16x8{};
+      if constexpr (C::FOLD) set_qext(s, qb, 0.0f, 0);
 #pragma unroll
       for (int db = 0; db < DV / 32; ++db) oacc[s][qb][db] = f32x16{};
     }
-  auto set_qext = [&](int s, int qb, float m) {
-    const float nm = -m;
-    const bf16 hi = (bf16)nm;
-    const bf16 mid = (bf16)(nm - (float)hi);
-    const bf16 lo = (bf16)(nm - (float)hi - (float)mid);
-    qext[s][qb] = g == 0 ? bf16x8{hi, mid, lo, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f,
-                                  (bf16)0.0f}
-                         : bf16x8{};
-  };
 
   // Scores live in base 2.  Modified scores are converted to base-2 units
   // after the product and use a lazy rescale: the running max used in the
@@ -237,7 +315,6 @@ void attn_mfma_kernel(KernelArgs a) {
   // and most tiles skip the accumulator rescale.  Exact: numerator and
   // denominator share the reference.
   const float thr = 8.0f;
-  const float alibi_l2 = C::MOD == MOD_ALIBI ? alibi_slope_log2(a, h) : 0.0f;
 
   // ---- global -> LDS tile movement ---------------------------------------------
   // K and V tiles go from global memory straight into LDS (buffer loads with
@@ -319,27 +396,81 @@ void attn_mfma_kernel(KernelArgs a) {
   // exponentiate, and P.V of unit u follows its softmax at once so P dies
   // early.  The running reference of a row never needs a tile-wide maximum,
   // so the two key halves of a tile are independent units.
-  auto compute_tile = [&](int stage, int kt, const bf16x8 (&vop)[2][DV / 32][2], auto masked_tag) {
+  bf16x8 kop[DQK / 16];  // K operands of the current (stream, key half)
+  auto read_k = [&](const bf16* ks, int s, int kb) {
+#pragma unroll
+    for (int t = 0; t < DQK / 16; ++t)
+      kop[t] = *(const bf16x8*)(ks + s * C::K_ELEMS + k_rd[t] + 32 * kb * DQK);
+  };
+  // position of a (key half, query block) unit against the diagonal
+  // (wave-uniform): keys wholly above the rows' diagonal, or straddling it
+  auto above = [&](int j0, int kb, int qb) { return j0 + 32 * kb >= wq0 + 32 * qb + 31; };
+  auto straddles = [&](int j0, int kb, int qb) {
+    return !above(j0, kb, qb) && j0 + 32 * kb + 31 > wq0 + 32 * qb;
+  };
+  // the folded k-step: -m, and the ALiBi penalty with the unit's sign
+  auto fold = [&](int j0, int s, int kb, int qb, f32x16& acc) {
+    const bf16x8 bq = C::ALIBI_FOLD && above(j0, kb, qb) ? flip(qext[s][qb]) : qext[s][qb];
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kext(kb), bq, acc, 0, 0, 0);
+  };
+  // ALiBi on a straddling unit: the sign was +1, so keys past the row got
+  // +slope*(j - i); subtract twice that
+  auto alibi_fix = [&](int j0, f32x16& acc, int kb, int qb) {
+    if constexpr (C::ALIBI_FOLD) {
+      if (straddles(j0, kb, qb)) {
+        const int qi = wq0 + 32 * qb + c;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int dj = j0 + 32 * kb + 4 * g + acc_row(r) - qi;
+          acc[r] = dj > 0 ? acc[r] - 2.0f * alibi_l2 * (float)dj : acc[r];
+        }
+      }
+    }
+  };
+  auto qk = [&](int j0, int s, int kb, int qb, f32x16& acc) {
+    acc = f32x16{};
+#pragma unroll
+    for (int t = 0; t < DQK / 16; ++t)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[t], qreg[s][qb][t], acc, 0, 0, 0);
+    if constexpr (C::FOLD) fold(j0, s, kb, qb, acc);
+  };
+
+  // consume tile kt from LDS stage `stage`
+  auto compute_tile = [&](int stage, int kt, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     constexpr int U = NS * 2 * QB;
     const bf16* ks = lds + stage * C::STAGE;
-    const bf16* vs = ks + NS * C::K_ELEMS;
     const int j0 = kt * BN;
 
-    bf16x8 kop[DQK / 16];  // K operands of the current (stream, key half)
-    auto read_k = [&](int s, int kb) {
+    // V^T operands of one key half (A operands of the P.V products): lane
+    // (c, g) holds V^T[d = 32db + c][keys 16st + 4g + 0..3, 16st + 8 + 4g +
+    // 0..3] for the 16-key step st = 2kb + h2, from two transposed reads.
+    u32x2 vraw[DV / 32 * 4];  // [db][h2][half]
+    bf16x8 vop[DV / 32][2];   // [db][h2]
+    const uint32_t vbase = lds_addr(ks + NS * C::K_ELEMS);
+    auto read_v = [&](int kb) {
 #pragma unroll
-      for (int t = 0; t < DQK / 16; ++t)
-        kop[t] = *(const bf16x8*)(ks + s * C::K_ELEMS + k_rd[t] + 32 * kb * DQK);
+      for (int db = 0; db < DV / 32; ++db) {
+        const uint32_t ad = vbase + 2 * v_rd[db];
+        u32x2* r = vraw + 4 * db;
+        if (kb == 0)
+          ds_read_tr4<0, 16 * DV, 32 * DV, 48 * DV>(ad, r[0], r[1], r[2], r[3]);
+        else
+          ds_read_tr4<64 * DV, 80 * DV, 96 * DV, 112 * DV>(ad, r[0], r[1], r[2], r[3]);
+      }
     };
-    auto qk = [&](int s, int qb, f32x16& acc) {
-      acc = f32x16{};
+    auto take_v = [&]() {
+      lds_fence(vraw);
 #pragma unroll
-      for (int t = 0; t < DQK / 16; ++t)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[t], qreg[s][qb][t], acc, 0, 0, 0);
-      if constexpr (C::PLAIN)  // + (-m): the running-reference subtraction
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kext, qext[s][qb], acc, 0, 0, 0);
+      for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const u32x2 lo = vraw[4 * db + 2 * h2], hi = vraw[4 * db + 2 * h2 + 1];
+          vop[db][h2] = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
+        }
     };
+    read_v(0);
+
     auto mask = [&](f32x16& acc, int kb, int qb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -368,24 +499,32 @@ void attn_mfma_kernel(KernelArgs a) {
       return part[0] + part[1];
     };
 
+    if constexpr (C::ALIBI_FOLD) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) set_qext(s, qb, m_run[s][qb], j0);
+    }
     f32x16 sacc[2];  // [pipeline slot]
-    read_k(0, 0);
-    qk(0, 0, sacc[0]);
+    read_k(ks, 0, 0);
+    qk(j0, 0, 0, 0, sacc[0]);
+    // unit u: key half kb = u / (NS*QB), stream s = (u / QB) % NS, block qb = u % QB
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int s = u / (2 * QB), kb = (u / QB) % 2, qb = u % QB;
+      const int kb = u / (NS * QB), s = (u / QB) % NS, qb = u % QB;
       if (u + 1 < U) {
-        const int s1 = (u + 1) / (2 * QB), kb1 = ((u + 1) / QB) % 2, qb1 = (u + 1) % QB;
-        if (qb1 == 0) read_k(s1, kb1);
-        qk(s1, qb1, sacc[(u + 1) & 1]);
+        const int kb1 = (u + 1) / (NS * QB), s1 = ((u + 1) / QB) % NS, qb1 = (u + 1) % QB;
+        if (qb1 == 0) read_k(ks, s1, kb1);
+        qk(j0, s1, kb1, qb1, sacc[(u + 1) & 1]);
       }
       f32x16& sc = sacc[u & 1];
       const int qi = wq0 + 32 * qb + c;
       const int jb = j0 + 32 * kb + 4 * g;  // key of register 0 in this lane
       bf16x8 pk[2];
 
-      if constexpr (C::PLAIN) {
+      if constexpr (C::FOLD) {
         // S^T already holds (score - m) in base 2.
+        alibi_fix(j0, sc, kb, qb);
         if constexpr (MASKED) mask(sc, kb, qb);
         float lsum = exp_pack(sc, pk, 0.0f);
         // The reference m is revisited only when it is unset for a row that
@@ -404,7 +543,8 @@ void attn_mfma_kernel(KernelArgs a) {
             const bf16x8 ka = *(const bf16x8*)(ks + s * C::K_ELEMS + k_rd[t] + 32 * kb * DQK);
             rs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s][qb][t], rs, 0, 0, 0);
           }
-          rs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kext, qext[s][qb], rs, 0, 0, 0);
+          fold(j0, s, kb, qb, rs);
+          alibi_fix(j0, rs, kb, qb);
           if constexpr (MASKED) mask(rs, kb, qb);
           float xm = kNegInf;
 #pragma unroll
@@ -412,18 +552,21 @@ void attn_mfma_kernel(KernelArgs a) {
           xm = fmaxf(xm, __shfl_xor(xm, 32));
           // move when the reference is unset, or when terms reach 2^32
           const bool move = xm != kNegInf && (!m_set[s][qb] || xm > 32.0f);
-          const float shift = move ? xm : 0.0f;
+          // the new reference is the row maximum rounded to bf16, so that
+          // one k-slot carries it exactly
+          const float m_new = move ? (float)(bf16)(m_run[s][qb] + xm) : m_run[s][qb];
+          const float shift = m_new - m_run[s][qb];
           const float alpha = !move ? 1.0f : (m_set[s][qb] ? fast_exp2(-shift) : 0.0f);
           l_run[s][qb] *= alpha;
 #pragma unroll
           for (int db = 0; db < DV / 32; ++db) oacc[s][qb][db] *= alpha;
           if (move) {
-            m_run[s][qb] += shift;
+            m_run[s][qb] = m_new;
             m_set[s][qb] = true;
           }
-          set_qext(s, qb, m_run[s][qb]);
+          set_qext(s, qb, m_run[s][qb], j0);
           // the next unit's scores, already issued, may belong to the same rows
-          if (u + 1 < U && (u + 1) % QB == qb && (u + 1) / (2 * QB) == s) {
+          if (u + 1 < U && (u + 1) % QB == qb && ((u + 1) / QB) % NS == s) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[(u + 1) & 1][r] -= shift;
           }
@@ -493,44 +636,25 @@ void attn_mfma_kernel(KernelArgs a) {
         l_run[s][qb] += exp_pack(sc, pk, shift);
       }
 
-      // O^T += V^T P^T over this unit's 32 keys.  A operand of lane (c, g):
-      // V^T[d = 32db + c][keys 16st + 4g + 0..3, 16st + 8 + 4g + 0..3], two
-      // transposed 8-byte reads made at the start of the tile.
+      // O^T += V^T P^T over this unit's 32 keys; the V^T operands of a key
+      // half are taken at its first unit and the second half's reads are
+      // issued after the first half's last product.
+      if (s == 0 && qb == 0) take_v();
 #pragma unroll
       for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
           oacc[s][qb][db] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[kb][db][h2], pk[h2], oacc[s][qb][db], 0, 0, 0);
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][h2], pk[h2], oacc[s][qb][db], 0, 0, 0);
+      if (kb == 0 && s == NS - 1 && qb == QB - 1) read_v(1);
     }
   };
 
-  // V^T operands of a whole tile (A operands of the P.V products): lane
-  // (c, g) holds V^T[d = 32db + c][keys 16st + 4g + 0..3, 16st + 8 + 4g + 0..3]
-  // for the 16-key step st = 2kb + h2, from two transposed 8-byte reads.
-  auto read_v_tile = [&](int stage, bf16x8 (&vop)[2][DV / 32][2]) {
-    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-    const bf16* vs = lds + stage * C::STAGE + NS * C::K_ELEMS;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int db = 0; db < DV / 32; ++db)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const bf16* vp = vs + v_rd[db] + 16 * (2 * kb + h2) * DV;
-          const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
-          const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * DV));
-          vop[kb][db][h2] = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        }
-  };
-
   // ---- main loop ---------------------------------------------------------------
-  // Tile kt is consumed from stage (kt - kt_lo) % 3 while tile kt+1 has
-  // landed and tile kt+2 is in flight.  The V^T operands of tile kt are read
-  // before tile kt+2's loads are issued (those reads then never wait on
-  // loads still in flight), the K operands as the units need them.  The
-  // barrier at the end of an iteration both publishes tile kt+1 (every wave
-  // waited for its own loads) and frees the stage of tile kt for reuse.
+  // The it-th tile visited is consumed from stage it % 3 while the next one
+  // lands and the one after is in flight.  The barrier at the end of an
+  // iteration both publishes the next tile (every wave waited for its own
+  // loads) and frees the current stage.
   constexpr int LOADS = NS * C::KCH + C::VCH;  // LDS-bound loads per thread per tile
   static_assert(LOADS < 64, "vmcnt range");
   // Publish a landed tile: wait for this wave's loads of it (leaving the
@@ -544,28 +668,38 @@ void attn_mfma_kernel(KernelArgs a) {
     else
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
-  if (kt_lo < kt_hi) {
-    load_tile(kt_lo, 0);
+  // Tile order: ascending keys, except under ALiBi, where the visit starts
+  // at the work-group's diagonal tile and wraps round.  The scores of a row
+  // peak near its diagonal, so the running reference is set there first
+  // instead of climbing (and being moved) tile after tile.
+  const int n_kt = kt_hi - kt_lo;
+  int kt_start = 0;
+  if constexpr (C::MOD == MOD_ALIBI) kt_start = min(max(q0 / BN - kt_lo, 0), max(n_kt - 1, 0));
+  auto tile_of = [&](int it) {
+    const int x = it + kt_start;
+    return kt_lo + (x >= n_kt ? x - n_kt : x);
+  };
+  if (n_kt > 0) {
+    load_tile(tile_of(0), 0);
     store_kmask(0);
-    const bool two = kt_lo + 1 < kt_hi;
-    if (two) load_tile(kt_lo + 1, 1);
+    const bool two = n_kt > 1;
+    if (two) load_tile(tile_of(1), 1);
     sync_tile(two);
   }
-  for (int kt = kt_lo; kt < kt_hi; ++kt) {
-    const int stage = (kt - kt_lo) % 3;
-    const bool next = kt + 1 < kt_hi, next2 = kt + 2 < kt_hi;
+  for (int it = 0; it < n_kt; ++it) {
+    const int kt = tile_of(it);
+    const int stage = it % 3;
+    const bool next = it + 1 < n_kt, next2 = it + 2 < n_kt;
     const int j0 = kt * BN, j1 = j0 + BN - 1;
     const bool empty = wave_idle || j0 > w_hi_max || j1 < w_lo_min;
     const bool full = j0 >= w_lo_max && j1 <= w_hi_min;
-    bf16x8 vop[2][DV / 32][2];
-    if (!empty) read_v_tile(stage, vop);
     if (next) store_kmask(stage == 2 ? 0 : stage + 1);
-    if (next2) load_tile(kt + 2, stage == 0 ? 2 : stage - 1);
+    if (next2) load_tile(tile_of(it + 2), stage == 0 ? 2 : stage - 1);
     if (!empty) {
       if (full)
-        compute_tile(stage, kt, vop, std::integral_constant<bool, false>{});
+        compute_tile(stage, kt, std::integral_constant<bool, false>{});
       else
-        compute_tile(stage, kt, vop, std::integral_constant<bool, true>{});
+        compute_tile(stage, kt, std::integral_constant<bool, true>{});
     }
     if (next) sync_tile(next2);
   }
