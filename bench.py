@@ -26,8 +26,11 @@ HEADLINE = "mha_bf16_b4_h16_s4096_d64"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle", type=float, default=1.0,
+                    help="seconds of untimed steps before the warmup, so the clocks reach "
+                         "their loaded steady state")
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--variants", default=None, help="comma list (default: all seven)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -36,7 +39,11 @@ def parse():
     ap.add_argument("--report", action="store_true",
                     help="also print one JSON line per workload and variant")
     ap.add_argument("--traffic", default=None,
-                    help="JSON file with HBM bytes per launch measured by rocprofv3 counters")
+                    help="JSON file with HBM bytes per launch measured by rocprofv3 counters "
+                         "(default: profiles/traffic_<workload>.json)")
+    ap.add_argument("--probe-traffic", action="store_true",
+                    help="make only the dispatches the counter runs read: a copy of known "
+                         "size, then one call per variant")
     return ap.parse_args()
 
 
@@ -92,6 +99,24 @@ def main():
             if events is not None:
                 events[vname][1].record()
 
+    if args.probe_traffic:
+        from flashattention_attention_variants_amd import profiling
+        step()
+        src = torch.ones(profiling.PROBE_COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        step()
+        torch.cuda.synchronize()
+        print("probe: copy of %d bytes, then one call each of %s"
+              % (profiling.PROBE_COPY_BYTES, ",".join(variants)), flush=True)
+        return
+
+    t_end = time.perf_counter() + args.settle
+    while time.perf_counter() < t_end:
+        step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -119,10 +144,16 @@ def main():
     dom = max(variants, key=lambda vname: ms[vname])
     achieved = fl[dom] / (ms[dom] * 1e-3) / 1e12
     bound, roof = flops.roofline_tflops(fl[dom], nbytes)
+    # HBM bytes per launch from the committed counter runs, unless the
+    # kernels changed since they were taken
+    from flashattention_attention_variants_amd import profiling
     traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        rec = json.load(open(args.traffic))
-        traffic = rec.get(dom)
+    tpath = args.traffic or os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                         "traffic_%s.json" % wl.name)
+    if os.path.exists(tpath):
+        rec = json.load(open(tpath))
+        if rec.get("kernel_digest") == profiling.kernel_digest() and dom in rec.get("per_variant", {}):
+            traffic = rec["per_variant"][dom]["traffic_bytes"]
     roofline = dict(bound=bound, achieved=round(achieved, 1),
                     peak=flops.PEAK_BF16_TFLOPS if bound == "mfma" else flops.PEAK_HBM_GBS,
                     unit="TFLOP/s" if bound == "mfma" else "GB/s",

@@ -143,6 +143,7 @@ fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* b
     default:
       break;
   }
+  a.head_major = a.iv_kind == IV_FULL;
   hipStream_t st = (hipStream_t)stream;
   if (dtype == FL_F32) {
     a.n_qt = grid_qtiles(S_q, f32_rows_per_wg());
@@ -150,13 +151,23 @@ fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* b
     return launch_status(launch_f32(a, D, D, 1, mod, st));
   }
   if (!span_ok(S_k, D, D)) return FL_ERR_SHAPE;
-  // two 32-row blocks per wave when that still leaves enough work-groups to
-  // fill the 256 compute units twice
+  // Two 32-row blocks per wave halve the LDS operand traffic per product.
+  // Dense rows take them when that still leaves two work-groups per compute
+  // unit.  Under a positional mask the taller tiles cross more partial key
+  // tiles and balance worse, so masked rows take them only when the grid is
+  // deep (eight work-groups per unit); a sliding window, whose rows see few
+  // keys, never does.
   const int64_t wg2 = (int64_t)grid_qtiles(S_q, mfma_rows_per_wg(2)) * B * H_q;
 #ifdef FL_FORCE_QB
   const int qb = FL_FORCE_QB;
 #else
-  const int qb = wg2 >= 512 ? 2 : 1;
+  int qb;
+  if (a.iv_kind == IV_FULL)
+    qb = wg2 >= 512 ? 2 : 1;
+  else if (a.iv_kind == IV_WINDOW_CAUSAL || a.iv_kind == IV_WINDOW_TWO_SIDED)
+    qb = 1;
+  else
+    qb = wg2 >= 2048 ? 2 : 1;
 #endif
   a.n_qt = grid_qtiles(S_q, mfma_rows_per_wg(qb));
   if ((int64_t)a.n_qt * B * H_q > kMaxGrid) return FL_ERR_SHAPE;
@@ -206,6 +217,7 @@ fl_status fl_diffattn_fwd(const void* q1, const void* q2, const void* k1, const 
     a.iv_kind = IV_CAUSAL;
     a.heavy_first = 1;
   }
+  a.head_major = a.iv_kind == IV_FULL;
   hipStream_t st = (hipStream_t)stream;
   if (dtype == FL_F32) {
     a.n_qt = grid_qtiles(S_q, f32_rows_per_wg());

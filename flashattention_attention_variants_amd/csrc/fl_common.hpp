@@ -64,6 +64,7 @@ struct KernelArgs {
   float alibi_max_bias;
   float lambda;
   int heavy_first;             // schedule the most expensive query tiles first
+  int head_major;              // deal a head's query tiles to its XCD consecutively
 };
 
 // Key interval [lo, hi] of query i, clamped to [0, S_k-1] (empty: lo > hi).
@@ -108,19 +109,36 @@ __device__ __forceinline__ void key_interval(const KernelArgs& a, int b, int i, 
 }
 
 // Work-group id -> (b*H + h, query tile).  Work-groups are dealt to the 8
-// XCDs round-robin by id, and each XCD has its own L2; when the (b, h) count
-// is a multiple of 8, every query tile of one (b, h) -- and, with contiguous
-// GQA groups, of one K/V head -- is placed on the same XCD so their K/V
-// reads share that L2.  Within an XCD the tiles go out tile-index-major, so
-// with heavy_first the most expensive tiles of every head start first.
+// XCDs round-robin by id, and each XCD has its own L2.  When the number of
+// K/V heads (b, hk) is a multiple of 8, XCD x takes K/V heads x, x+8, x+16,
+// ... with every query tile of every query head that reads them, so their
+// K/V reads share one L2 and heads of different cost (ALiBi slopes, batch
+// entries) spread over all XCDs.  Dense rows (equal work per tile) go out
+// head-major within an XCD, so the work-groups resident at one time cover
+// few heads and stream the same K/V tiles together.  Masked rows go out
+// tile-index-major, which balances unequal tiles better; with heavy_first
+// the most expensive tiles of every head start first and the grid's tail is
+// made of cheap ones.
 __device__ __forceinline__ void decode_tile(const KernelArgs& a, int bid, int& bh, int& qt) {
   const int nbh = a.nb * a.nh;
+  const int G = a.group, nkv = nbh / G;
   int order;
-  if ((nbh & 7) == 0) {
-    const int hpx = nbh >> 3;
+  if ((nkv & 7) == 0) {
+    const int kpx = nkv >> 3;  // K/V heads per XCD
     const int xcd = bid & 7, slot = bid >> 3;
-    bh = xcd * hpx + slot % hpx;
-    order = slot / hpx;
+    int kv_local, r;
+    if (a.head_major) {
+      kv_local = slot / (G * a.n_qt);
+      const int rem = slot % (G * a.n_qt);
+      r = rem / a.n_qt;
+      order = rem % a.n_qt;
+    } else {
+      order = slot / (kpx * G);
+      const int hi = slot % (kpx * G);
+      kv_local = hi / G;
+      r = hi % G;
+    }
+    bh = (kv_local * 8 + xcd) * G + r;
   } else {
     bh = bid % nbh;
     order = bid / nbh;

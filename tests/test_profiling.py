@@ -1,0 +1,60 @@
+"""Host logic of the rocprofv3 summaries (synthetic CSV files, no GPU)."""
+import csv
+import os
+
+from flashattention_attention_variants_amd import profiling
+
+HEAD = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
+        "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size",
+        "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value",
+        "Start_Timestamp", "End_Timestamp"]
+
+
+def _write_counters(d, counter, rows):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "run_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(HEAD)
+        for i, (name, kib) in enumerate(rows, 1):
+            w.writerow([i, i, "Agent 1", 1, 1, 1, 64, 1, name, 256, 0, 0, 128, 0, 96, counter,
+                        kib, 0, 1])
+
+
+def test_traffic_calibration(tmp_path):
+    variants = ["vanilla", "causal"]
+    attn = "void fl::attn_mfma_kernel<fl::MfmaCfg<64, 64, 1, 2, 0> >(fl::KernelArgs)"
+    copy_kib = profiling.PROBE_COPY_BYTES / 1024
+    # warmup calls, a small unrelated copy, the calibration copy, the measured calls
+    _write_counters(tmp_path / "f", "FETCH_SIZE",
+                    [(attn, 999.0), (attn, 999.0), ("__amd_rocclr_copyBuffer", 3.0),
+                     ("__amd_rocclr_copyBuffer", copy_kib / 2), (attn, 1000.0), (attn, 500.0)])
+    _write_counters(tmp_path / "w", "WRITE_SIZE",
+                    [(attn, 7.0), (attn, 7.0), ("__amd_rocclr_copyBuffer", copy_kib),
+                     (attn, 64.0), (attn, 32.0)])
+    rec = profiling.traffic(str(tmp_path / "f"), str(tmp_path / "w"), variants)
+    assert abs(rec["fetch_factor"] - 2.0) < 1e-12
+    assert abs(rec["write_factor"] - 1.0) < 1e-12
+    pv = rec["per_variant"]
+    assert pv["vanilla"]["fetch_bytes"] == 1000 * 1024 * 2
+    assert pv["causal"]["fetch_bytes"] == 500 * 1024 * 2
+    assert pv["vanilla"]["write_bytes"] == 64 * 1024
+    assert pv["causal"]["traffic_bytes"] == 500 * 1024 * 2 + 32 * 1024
+    assert rec["kernel_digest"] == profiling.kernel_digest()
+
+
+def test_stats_table(tmp_path):
+    d = tmp_path / "kt"
+    os.makedirs(d)
+    with open(d / "run_kernel_stats.csv", "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs",
+                    "StdDev"])
+        w.writerow(["void fl::attn_mfma_kernel<X>(fl::KernelArgs)", 3, 3000, 1000.0, 100.0, 900, 1100,
+                    10.0])
+    t = profiling.stats_table(str(d))
+    assert "`fl::attn_mfma_kernel<X>` | 3 | 1.0 | 0.9 | 1.1 | 100.0% |" in t
+
+
+def test_digest_tracks_sources():
+    a = profiling.kernel_digest()
+    assert a == profiling.kernel_digest() and len(a) == 16
