@@ -255,17 +255,30 @@ def cpu_baseline(t, variants, kws, wl, seconds):
 def report(torch, api, flops, inputs, dev):
     """One JSON line per (workload, variant): time, TFLOP/s, roofline fraction."""
 
-    def timeit(fn, iters=10):
-        for _ in range(3):
+    def timeit(fn, settle=0.3, batches=3, batch_s=0.05):
+        # a short settle at this case's load, then the fastest of a few
+        # timed batches of back-to-back calls
+        t_end = time.perf_counter() + settle
+        n = 0
+        while time.perf_counter() < t_end or n < 3:
             fn()
-        torch.cuda.synchronize()
+            torch.cuda.synchronize()
+            n += 1
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        for _ in range(iters):
-            fn()
+        fn()
         b.record()
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / iters
+        iters = max(5, int(batch_s * 1e3 / max(a.elapsed_time(b), 1e-3)))
+        best = float("inf")
+        for _ in range(batches):
+            a.record()
+            for _ in range(iters):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b) / iters)
+        return best
 
     for name, wl in inputs.WORKLOADS.items():
         t = inputs.make(wl)

@@ -9,11 +9,12 @@
         HBM bytes per launch from two ``rocprofv3 --pmc FETCH_SIZE`` /
         ``--pmc WRITE_SIZE`` runs of ``bench.py --probe-traffic``.  The probe
         first copies a buffer of known size; the counters of that copy give
-        the factor from counter kilobytes to bytes moved (FETCH_SIZE and
-        WRITE_SIZE count 64-byte requests between L2 and the memory fabric, so
-        the factor absorbs request granularity).  Each variant's launch after
-        it is scaled by that factor.  The file records a digest of the kernel
-        sources so that a later build can tell the figures are stale.
+        the factor from counter kilobytes to bytes moved (the counters are
+        derived from request counts between L2 and the memory fabric, whose
+        sizes they assume; the factor absorbs that).  Each variant's launch
+        after the copy is scaled by that factor.  The file records a digest
+        of the kernel and launcher sources so that a later build can tell the
+        figures are stale.
 """
 from __future__ import annotations
 
@@ -33,11 +34,10 @@ PROBE_COPY_BYTES = 512 << 20
 
 
 def kernel_digest() -> str:
-    """sha256 over the kernel sources and the C header (path order)."""
+    """sha256 over the kernel and launcher sources (path order)."""
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hpp")) +
-                   glob.glob(os.path.join(PKG, "csrc", "*.hip")) +
-                   glob.glob(os.path.join(ROOT, "include", "*.h")))
+                   glob.glob(os.path.join(PKG, "csrc", "*.hip")))
     for f in files:
         h.update(os.path.relpath(f, ROOT).encode())
         with open(f, "rb") as fh:

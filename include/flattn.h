@@ -143,8 +143,10 @@ typedef enum { FL_EVO_ROW = 0, FL_EVO_COL = 1 } fl_evo_axis;
  *        keys) of the same tensors, read in place (no transpose); pair_bias
  *        must be NULL; key_mask NULL or [N_seq, N_res], 0 excludes that key.
  *   O[s, r, h, :] = sigmoid(gate[s, r, h, :]) * attention output.
- * scale multiplies q.k only (usually 1/sqrt(C)).  C: 32 or 64 (FL_BF16),
- * 32 or 64 (FL_F32).  With a pair bias, N_res % 8 == 0.
+ * scale multiplies q.k only (usually 1/sqrt(C)).  C = 32 (the AlphaFold2
+ * head width; other widths return FL_ERR_UNSUPPORTED), FL_BF16 or FL_F32.
+ * With a pair bias and FL_BF16, N_res % 8 == 0.  An empty tensor (N_seq or
+ * N_res 0) returns FL_OK without launching.
  */
 fl_status fl_evoformer_gated_attn_fwd(const void* q, const void* k, const void* v,
                                       const void* gate, const void* pair_bias,
