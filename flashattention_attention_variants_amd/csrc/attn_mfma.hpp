@@ -259,6 +259,9 @@ void attn_mfma_kernel(KernelArgs a) {
   // the sign bits of slots 1..6.  Blocks that straddle the diagonal take
   // sigma = +1 and a vector correction for j > i.  Plain scores use slot 0.
   bf16x8 qext[NS][QB];
+  // Wave-uniform: some row of the wave has a reference m != 0, so S^T needs
+  // the folded step (always under ALiBi, whose penalty rides on it).
+  bool need_fold = C::ALIBI_FOLD;
   const bf16 one = (bf16)1.0f, zero = (bf16)0.0f;
   auto split3 = [](float x, bf16& hi, bf16& mid, bf16& lo) {
     hi = (bf16)x;
@@ -299,7 +302,8 @@ void attn_mfma_kernel(KernelArgs a) {
   for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      // folded: m = 0 is a placeholder until the row's first allowed keys set it
+      // folded: m = 0 is a valid reference from the start; it moves only
+      // when terms overflow or a row's terms underflow
       m_run[s][qb] = C::FOLD ? 0.0f : kNegInf;
       m_set[s][qb] = false;
       l_run[s][qb] = 0.0f;
@@ -427,17 +431,20 @@ void attn_mfma_kernel(KernelArgs a) {
       }
     }
   };
-  auto qk = [&](int j0, int s, int kb, int qb, f32x16& acc) {
+  auto qk = [&](int j0, int s, int kb, int qb, f32x16& acc, auto folded_tag) {
     acc = f32x16{};
 #pragma unroll
     for (int t = 0; t < DQK / 16; ++t)
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[t], qreg[s][qb][t], acc, 0, 0, 0);
-    if constexpr (C::FOLD) fold(j0, s, kb, qb, acc);
+    if constexpr (C::FOLD && decltype(folded_tag)::value) fold(j0, s, kb, qb, acc);
   };
 
-  // consume tile kt from LDS stage `stage`
-  auto compute_tile = [&](int stage, int kt, auto masked_tag) {
+  // Consume tile kt from LDS stage `stage`.  Folded scores: FOLDED adds the
+  // extra k-step to every S^T product; without it the tile assumes that
+  // every row of the wave still has the reference m = 0 (see need_fold).
+  auto compute_tile = [&](int stage, int kt, auto masked_tag, auto folded_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr bool FOLDED = decltype(folded_tag)::value;
     constexpr int U = NS * 2 * QB;
     const bf16* ks = lds + stage * C::STAGE;
     const int j0 = kt * BN;
@@ -507,7 +514,7 @@ void attn_mfma_kernel(KernelArgs a) {
     }
     f32x16 sacc[2];  // [pipeline slot]
     read_k(ks, 0, 0);
-    qk(j0, 0, 0, 0, sacc[0]);
+    qk(j0, 0, 0, 0, sacc[0], folded_tag);
     // unit u: key half kb = u / (NS*QB), stream s = (u / QB) % NS, block qb = u % QB
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -515,7 +522,7 @@ void attn_mfma_kernel(KernelArgs a) {
       if (u + 1 < U) {
         const int kb1 = (u + 1) / (NS * QB), s1 = ((u + 1) / QB) % NS, qb1 = (u + 1) % QB;
         if (qb1 == 0) read_k(ks, s1, kb1);
-        qk(j0, s1, kb1, qb1, sacc[(u + 1) & 1]);
+        qk(j0, s1, kb1, qb1, sacc[(u + 1) & 1], folded_tag);
       }
       f32x16& sc = sacc[u & 1];
       const int qi = wq0 + 32 * qb + c;
@@ -527,16 +534,18 @@ void attn_mfma_kernel(KernelArgs a) {
         alibi_fix(j0, sc, kb, qb);
         if constexpr (MASKED) mask(sc, kb, qb);
         float lsum = exp_pack(sc, pk, 0.0f);
-        // The reference m is revisited only when it is unset for a row that
-        // has allowed keys here, or when the unit's terms grew past 2^64
-        // (inf included): then both halves of the row agree on a new
-        // reference, the accumulator is rescaled and the scores are
-        // recomputed and re-exponentiated.  Wave-uniform, rarely taken.
+        // The reference m is revisited only when the unit's terms grew past
+        // 2^64 (inf included), or when a row that has allowed keys here has
+        // no mass at all yet (its terms underflowed): then both halves of the
+        // row agree on a new reference, the accumulator is rescaled and the
+        // scores are recomputed and re-exponentiated.  In a tile without the
+        // folded step, every unit after a reference moved is recomputed the
+        // same way.  Wave-uniform, rarely taken.
         const bool has_key = row_hi[qb] >= j0 + 32 * kb && row_lo[qb] <= j0 + 32 * kb + 31 &&
                              row_lo[qb] <= row_hi[qb];
-        const bool redo = (!m_set[s][qb] && has_key) || !(lsum <= 0x1p64f);
+        const bool redo = (has_key && l_run[s][qb] + lsum == 0.0f) || !(lsum <= 0x1p64f);
         interleave_hint();
-        if (__builtin_amdgcn_ballot_w64(redo)) {
+        if (__builtin_amdgcn_ballot_w64(redo) || (!FOLDED && need_fold)) {
           f32x16 rs = f32x16{};
 #pragma unroll
           for (int t = 0; t < DQK / 16; ++t) {
@@ -550,21 +559,25 @@ void attn_mfma_kernel(KernelArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) xm = fmaxf(xm, rs[r]);
           xm = fmaxf(xm, __shfl_xor(xm, 32));
-          // move when the reference is unset, or when terms reach 2^32
-          const bool move = xm != kNegInf && (!m_set[s][qb] || xm > 32.0f);
+          // move when terms reach 2^32, or when the row (both lane halves,
+          // this unit included) has no mass and its terms are below 2^-32;
+          // both halves of a row decide alike
+          const float lr = l_run[s][qb] + lsum;
+          const float l_row = lr + __shfl_xor(lr, 32);
+          const bool move = xm != kNegInf && (xm > 32.0f || (l_row == 0.0f && xm < -32.0f));
           // the new reference is the row maximum rounded to bf16, so that
           // one k-slot carries it exactly
           const float m_new = move ? (float)(bf16)(m_run[s][qb] + xm) : m_run[s][qb];
           const float shift = m_new - m_run[s][qb];
-          const float alpha = !move ? 1.0f : (m_set[s][qb] ? fast_exp2(-shift) : 0.0f);
+          // (a row without mass has nothing to rescale; moving its reference
+          // down could overflow the factor)
+          const float alpha = !move ? 1.0f : (l_run[s][qb] == 0.0f ? 0.0f : fast_exp2(-shift));
           l_run[s][qb] *= alpha;
 #pragma unroll
           for (int db = 0; db < DV / 32; ++db) oacc[s][qb][db] *= alpha;
-          if (move) {
-            m_run[s][qb] = m_new;
-            m_set[s][qb] = true;
-          }
+          m_run[s][qb] = m_new;
           set_qext(s, qb, m_run[s][qb], j0);
+          if (__builtin_amdgcn_ballot_w64(m_run[s][qb] != 0.0f)) need_fold = true;
           // the next unit's scores, already issued, may belong to the same rows
           if (u + 1 < U && (u + 1) % QB == qb && ((u + 1) / QB) % NS == s) {
 #pragma unroll
@@ -696,10 +709,19 @@ void attn_mfma_kernel(KernelArgs a) {
     if (next) store_kmask(stage == 2 ? 0 : stage + 1);
     if (next2) load_tile(tile_of(it + 2), stage == 0 ? 2 : stage - 1);
     if (!empty) {
-      if (full)
-        compute_tile(stage, kt, std::integral_constant<bool, false>{});
-      else
-        compute_tile(stage, kt, std::integral_constant<bool, true>{});
+      using F = std::integral_constant<bool, false>;
+      using T = std::integral_constant<bool, true>;
+      if (!C::FOLD || C::ALIBI_FOLD || need_fold) {
+        if (full)
+          compute_tile(stage, kt, F{}, T{});
+        else
+          compute_tile(stage, kt, T{}, T{});
+      } else if constexpr (C::FOLD && !C::ALIBI_FOLD) {
+        if (full)
+          compute_tile(stage, kt, F{}, F{});
+        else
+          compute_tile(stage, kt, T{}, F{});
+      }
     }
     if (next) sync_tile(next2);
   }

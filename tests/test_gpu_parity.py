@@ -190,6 +190,35 @@ def test_uniform_scores_mean_of_values():
     assert np.abs(np64(lse) - np.log(np.arange(1, S + 1))[None, None]).max() < 1e-3
 
 
+@pytest.mark.parametrize("variant", ["vanilla", "causal", "alibi", "document"])
+@pytest.mark.parametrize("case", ["sharp", "low"])
+def test_bf16_extreme_scores(variant, case):
+    """Scores far outside the exponential's range, which the running
+    reference has to absorb: 'sharp' scores spread over hundreds of base-2
+    units (terms overflow unless the reference moves up); 'low' puts every
+    score of every row below -190 in base 2 (the terms underflow to no mass
+    unless the reference moves down).  scale * log2(e) = 1/8 keeps the
+    kernel's pre-scaled Q exact, so only P's rounding separates the two
+    sides; O and LSE are compared with the oracle."""
+    B, H, S, D = 1, 2, 300, 64
+    q, k, v = inputs.attn_inputs(B, H, H, S, S, D, "bf16", seed=63)
+    u = torch.full((D,), 1.0 / 8.0)  # unit vector
+    if case == "sharp":
+        q = (q.float() * 30).to(torch.bfloat16)
+    else:
+        k = (k.float() * 0.1 + 20 * u).to(torch.bfloat16)
+        q = (q.float() * 0.1 - 80 * u).to(torch.bfloat16)
+    kw = dict(variant=variant, scale=0.125 / math.log2(math.e))
+    if variant == "document":
+        kw["doc_offsets"] = inputs.doc_offsets(B, S, 3, seed=64)
+    o, lse = run_gpu_attn(q, k, v, **kw)
+    ro, rl = run_oracle_attn(q, k, v, **kw)
+    check(np64(o), ro, "bf16", "%s %s O" % (variant, case))
+    assert np.abs(np64(lse) - rl).max() < 1e-2, np.abs(np64(lse) - rl).max()
+    if case == "low":
+        assert rl.max() < -100  # the scores really are that low
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_fully_masked_rows(dtype):
     """A -inf bias row and an empty key set give O = 0 and LSE = -inf."""
