@@ -9,6 +9,7 @@ from __future__ import annotations
 import concurrent.futures as cf
 import glob
 import os
+import re
 import subprocess
 import sys
 
@@ -31,7 +32,9 @@ FLAGS = [
 
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
+    # -save-temps=obj leaves the device assembly next to the object for the
+    # register check below
+    cmd = [HIPCC, *FLAGS, *extra, "-save-temps=obj", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
@@ -49,6 +52,52 @@ def _check_stubs(objs: list[str]) -> None:
             raise RuntimeError("%s: kernel stubs not emitted: %s" % (o, ", ".join(missing[:3])))
 
 
+def _vregs(tok: str) -> set[int]:
+    m = re.match(r"v\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def _check_lds_transpose_reads(asm: str) -> None:
+    """The transposed LDS reads are inline assembly whose results are valid
+    only after the following `s_waitcnt lgkmcnt(0)`; the compiler does not
+    know that.  Fail if any instruction reads or writes one of their
+    destination registers before that wait (for instance a register copy
+    made under register pressure), which would use data not yet loaded."""
+    pending: dict[int, int] = {}
+    in_asm, kernel = False, ""
+    with open(asm) as fh:
+        for n, line in enumerate(fh, 1):
+            t = line.strip()
+            if re.match(r"^_Z\S+:", t):
+                kernel, pending = t, {}
+            if t.startswith(";;#ASMSTART"):
+                in_asm = True
+                continue
+            if t.startswith(";;#ASMEND"):
+                in_asm = False
+                continue
+            if not t or t[0] in ";.":
+                continue
+            op, *args = t.split()
+            args = [a.strip(",") for a in args]
+            if op == "s_waitcnt" and "lgkmcnt(0)" in t:
+                pending = {}
+                continue
+            if in_asm and op == "ds_read_b64_tr_b16":
+                for r in _vregs(args[0]):
+                    pending[r] = n
+                continue
+            used = set().union(*(_vregs(a) for a in args)) if args else set()
+            hit = used & pending.keys()
+            if hit:
+                raise RuntimeError("%s:%d: %s touches v%d before its LDS transpose read "
+                                   "(line %d) completed, in %s" % (asm, n, t, min(hit),
+                                                                  pending[min(hit)], kernel[:90]))
+
+
 def build(jobs: int | None = None, extra: list[str] | None = None, verbose: bool = False) -> str:
     """Compile every HIP source and link the library; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
@@ -57,6 +106,9 @@ def build(jobs: int | None = None, extra: list[str] | None = None, verbose: bool
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra or []), srcs))
     _check_stubs(objs)
+    for o in objs:
+        for asm in glob.glob(o[:-2] + "-hip-amdgcn-amd-amdhsa-*.s"):
+            _check_lds_transpose_reads(asm)
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

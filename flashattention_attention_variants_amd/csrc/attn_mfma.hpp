@@ -68,6 +68,9 @@ struct MfmaCfg {
   // distance penalty all enter the S^T product itself.
   static constexpr bool FOLD = (MOD == MOD_NONE || MOD == MOD_ALIBI) && !BIAS && !KMASK;
   static constexpr bool ALIBI_FOLD = FOLD && MOD == MOD_ALIBI;
+  // bounded softcap: fixed reference 0
+  static constexpr bool SCAPB = MOD == MOD_SOFTCAP_BOUNDED;
+  static_assert(!SCAPB || (!BIAS && !KMASK), "bounded softcap takes no bias or key mask");
   // one stream fits 2 waves per SIMD; two streams need the whole register file
 #ifndef FL_QB1_WAVES
 #define FL_QB1_WAVES 2
@@ -304,7 +307,7 @@ void attn_mfma_kernel(KernelArgs a) {
     for (int qb = 0; qb < QB; ++qb) {
       // folded: m = 0 is a valid reference from the start; it moves only
       // when terms overflow or a row's terms underflow
-      m_run[s][qb] = C::FOLD ? 0.0f : kNegInf;
+      m_run[s][qb] = (C::FOLD || C::SCAPB) ? 0.0f : kNegInf;
       m_set[s][qb] = false;
       l_run[s][qb] = 0.0f;
       qext[s][qb] = bf16x8{};
@@ -529,7 +532,19 @@ void attn_mfma_kernel(KernelArgs a) {
       const int jb = j0 + 32 * kb + 4 * g;  // key of register 0 in this lane
       bf16x8 pk[2];
 
-      if constexpr (C::FOLD) {
+      if constexpr (C::SCAPB) {
+        // With t = 2 y log2(e) for y = scale q.k / cap, the softcapped
+        // base-2 score is cap log2(e) tanh(y) = c - 2c / (2^t + 1), where
+        // c = cap log2(e) <= 100: the terms 2^score stay within fp32's normal
+        // range with the fixed reference 0.
+        const float c2 = a.softcap_log2;
+        f32x16 x;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          x[r] = fmaf(fast_rcp(fast_exp2(sc[r] * a.softcap_arg) + 1.0f), -2.0f * c2, c2);
+        if constexpr (MASKED) mask(x, kb, qb);
+        l_run[s][qb] += exp_pack(x, pk, 0.0f);
+      } else if constexpr (C::FOLD) {
         // S^T already holds (score - m) in base 2.
         alibi_fix(j0, sc, kb, qb);
         if constexpr (MASKED) mask(sc, kb, qb);

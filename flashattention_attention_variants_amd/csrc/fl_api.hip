@@ -151,6 +151,9 @@ fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* b
     return launch_status(launch_f32(a, D, D, 1, mod, st));
   }
   if (!span_ok(S_k, D, D)) return FL_ERR_SHAPE;
+  // softcap bounds every score by cap, so with a modest cap and no bias the
+  // kernel needs no running reference
+  if (mod == MOD_SOFTCAP && !bias && p->softcap * kLog2e <= 100.0f) mod = MOD_SOFTCAP_BOUNDED;
   // Two 32-row blocks per wave halve the LDS operand traffic per product.
   // Dense rows take them when that still leaves two work-groups per compute
   // unit.  Under a positional mask the taller tiles cross more partial key

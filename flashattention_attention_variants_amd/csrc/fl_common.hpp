@@ -20,7 +20,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 
 // Score modification applied to every score (FlexAttention's score_mod class).
-enum ModKind { MOD_NONE = 0, MOD_ALIBI = 1, MOD_SOFTCAP = 2 };
+// MOD_SOFTCAP_BOUNDED is softcap without a bias or key mask and with
+// cap * log2(e) <= 100: every base-2 score lies in [-100, 100], so the
+// exponentials need no running reference at all.
+enum ModKind { MOD_NONE = 0, MOD_ALIBI = 1, MOD_SOFTCAP = 2, MOD_SOFTCAP_BOUNDED = 3 };
 
 // Every mask variant on the pages allows, for query i, one contiguous run of
 // keys [lo(i), hi(i)], and both ends never decrease as i grows.  That is

@@ -23,6 +23,8 @@ static hipError_t pick_mod(const KernelArgs& a, int mod, bool bias, hipStream_t 
   switch (mod) {
     case MOD_ALIBI: return pick_bias<QB, MOD_ALIBI>(a, bias, st);
     case MOD_SOFTCAP: return pick_bias<QB, MOD_SOFTCAP>(a, bias, st);
+    case MOD_SOFTCAP_BOUNDED:  // chosen only without a bias
+      return go<MfmaCfg<64, 64, 1, QB, MOD_SOFTCAP_BOUNDED, false, false, false>>(a, st);
     default: return pick_bias<QB, MOD_NONE>(a, bias, st);
   }
 }

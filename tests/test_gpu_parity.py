@@ -162,6 +162,23 @@ def test_softcap_small_cap_sharpened():
     assert np.abs(ro - rv).max() > 0.3
 
 
+@pytest.mark.parametrize("cap", [2.0, 30.0, 80.0, 400.0])
+@pytest.mark.parametrize("S", [77, 300])
+def test_softcap_caps_and_extremes(cap, S):
+    """Softcap over a range of caps on both kernel paths (cap log2(e) <= 100
+    needs no running reference; larger caps track one), with scores spread
+    over several hundred units so that large caps leave them far from 0,
+    causal and non-causal, O and LSE against the oracle."""
+    B, H = 1, 2
+    q, k, v = inputs.attn_inputs(B, H, H, S, S, 64, "bf16", seed=65)
+    q = (q.float() * 25).to(torch.bfloat16)
+    for variant in ("softcap",):
+        o, lse = run_gpu_attn(q, k, v, variant=variant, softcap=cap)
+        ro, rl = run_oracle_attn(q, k, v, variant=variant, softcap=cap)
+        check(np64(o), ro, "bf16", "softcap %g S=%d" % (cap, S))
+        assert np.abs(np64(lse) - rl).max() < 2e-2 * max(1.0, np.abs(rl).max() / 64)
+
+
 def test_alibi_closed_form_on_gpu():
     """Q = 0, V = identity (S = D = 64): row i of O is r^|i-j| / Z_i."""
     H, S = 8, 64
