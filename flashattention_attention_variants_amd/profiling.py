@@ -109,27 +109,167 @@ def traffic(dir_fetch: str, dir_write: str, variants: list[str]) -> dict:
     return out
 
 
+ALGO_BYTES_NOTE = ("Algorithmic bytes = Q, K, V read once and O written once (bf16).  "
+                   "`kernel_digest` names the kernel and launcher sources the counters were "
+                   "taken with; bench.py reports `traffic` only while it matches.")
+
+
+def stats_markdown(dirname: str, bench_json: str, workload: str) -> str:
+    """Kernel-trace summary of the default bench command, with the bench's
+    own per-launch timing of the same build beside it."""
+    b = json.load(open(bench_json))
+    out = ["# attn_mfma_kernel -- %s, all variants" % workload, "",
+           "Kernel trace of the default bench command (one step = one call of each variant; "
+           "1 s clock settle, %d warmup and %d timed steps), one MI355X." % (b["warmup"], b["steps"]), "",
+           "```",
+           "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/kt -o run "
+           "-- python3 $REPO/bench.py",
+           "python3 $REPO/bench.py > gpurun_out/bench.json",
+           "python -m flashattention_attention_variants_amd.profiling stats-md gpurun_out/kt "
+           "--bench gpurun_out/bench.json --workload %s" % workload,
+           "```", "", stats_table(dirname), "",
+           "Kernel names: `MfmaCfg<D_qk, D_v, streams, QB, MOD, bias, key mask, gate>` with QB the "
+           "32-query blocks per wave and MOD 0 = none (vanilla, causal, window, PrefixLM, document), "
+           "1 = ALiBi, 2 = softcap with a running reference, 3 = bounded softcap.  One kernel "
+           "instance serves several variants when they differ only in the mask interval; its row "
+           "then mixes their durations.", "",
+           "Bench line of the same build (HIP events on the launch stream, average per launch):", "",
+           "| variant | ms / launch | useful TFLOP/s | % of bf16 peak |", "|---|---:|---:|---:|"]
+    for k, v in b["per_variant"].items():
+        out.append("| %s | %.4f | %.1f | %.1f |" % (k, v["ms"], v["tflops"], 100 * v["frac_bf16_peak"]))
+    r = b["roofline"]
+    out += ["", "Step value %.1f TFLOP/s.  Dominant kernel: %s, %.4f ms per launch." % (
+        b["value"], r["kernel"], r["ms_per_launch"]), ""]
+    return "\n".join(out)
+
+
+def traffic_markdown(rec: dict) -> str:
+    alg = None
+    out = ["# HBM traffic per launch -- attn_mfma_kernel, %s" % rec.get("workload", ""), "",
+           "Two counter runs of the traffic probe (`bench.py --probe-traffic`: one call of each "
+           "variant, a %d-byte device copy, then one more call of each variant), then the summary:"
+           % rec["probe_copy_bytes"], "", "```",
+           "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch -o run "
+           "-- python3 $REPO/bench.py --probe-traffic",
+           "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write -o run "
+           "-- python3 $REPO/bench.py --probe-traffic",
+           "python -m flashattention_attention_variants_amd.profiling traffic gpurun_out/pmc_fetch "
+           "gpurun_out/pmc_write --workload %s --out profiles/traffic_%s.json --md profiles/traffic_%s.md"
+           % (rec.get("workload"), rec.get("workload"), rec.get("workload")), "```", "",
+           "Calibration: the copy of %d bytes read %.0f KiB of FETCH_SIZE and %.0f KiB of WRITE_SIZE, "
+           "so counter KiB are scaled by %.4f (fetch) and %.4f (write) to bytes."
+           % (rec["probe_copy_bytes"], rec["copy_fetch_kib"], rec["copy_write_kib"],
+              rec["fetch_factor"], rec["write_factor"]), ""]
+    if rec.get("algorithmic_bytes"):
+        alg = rec["algorithmic_bytes"]
+    out += ["| variant | kernel | fetch MB | write MB | traffic MB | algorithmic MB | ratio |",
+            "|---|---|---:|---:|---:|---:|---:|"]
+    for k, v in rec["per_variant"].items():
+        out.append("| %s | `%s` | %.1f | %.1f | %.1f | %s | %s |" % (
+            k, v["kernel"].replace("fl::", ""), v["fetch_bytes"] / 1e6, v["write_bytes"] / 1e6,
+            v["traffic_bytes"] / 1e6, "%.1f" % (alg / 1e6) if alg else "-",
+            "%.2f" % (v["traffic_bytes"] / alg) if alg else "-"))
+    out += ["", ALGO_BYTES_NOTE, "", "kernel_digest: %s" % rec["kernel_digest"], ""]
+    return "\n".join(out)
+
+
+COUNTER_PASSES = (
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_ACTIVE_INST_VALU "
+    "SQ_WAVE_CYCLES SQ_INSTS_SALU GRBM_GUI_ACTIVE",
+    "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_WAIT_INST_ANY "
+    "SQ_INSTS_VMEM_RD GRBM_GUI_ACTIVE",
+)
+
+
+def _per_dispatch_all(dirname: str) -> list[dict]:
+    disp: dict[int, dict] = {}
+    for r in _csv(dirname, "counter_collection.csv"):
+        d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [disp[k] for k in sorted(disp)]
+
+
+def counters_markdown(dirs: list[str], variants: list[str], workload: str, units: dict) -> str:
+    """Per-variant counter table of the probe's last call of each variant.
+    MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES over (GRBM_GUI_ACTIVE / 8 XCDs x
+    1024 SIMDs); per-unit figures divide by the number of 32x32 work units."""
+    per = {v: {} for v in variants}
+    for d in dirs:
+        attn = [x for x in _per_dispatch_all(d) if "attn_" in x["name"]][-len(variants):]
+        for v, x in zip(variants, attn):
+            per[v].update(x)
+    out = ["# Counters -- attn_mfma_kernel, %s" % workload, "",
+           "One rocprofv3 --pmc run per counter group over the traffic probe (the last call of each "
+           "variant is read):", "", "```"]
+    for i, grp in enumerate(COUNTER_PASSES):
+        out.append("cd /tmp && rocprofv3 --pmc %s --output-format csv -d $REPO/gpurun_out/ctr%d -o run "
+                   "-- python3 $REPO/bench.py --probe-traffic" % (grp, i + 1))
+    out += ["python -m flashattention_attention_variants_amd.profiling counters-md gpurun_out/ctr1 "
+            "gpurun_out/ctr2 --workload %s" % workload, "```", "",
+            "| variant | MFMA busy | MFMA / unit | VALU / unit | SALU / unit | LDS / unit | "
+            "LDS conflict cycles / LDS instr |", "|---|---:|---:|---:|---:|---:|---:|"]
+    for v in variants:
+        x = per[v]
+        simd = x["GRBM_GUI_ACTIVE"] / 8 * 1024
+        u = units.get(v)
+        f = (lambda c: "%.1f" % (x[c] / u)) if u else (lambda c: "-")
+        out.append("| %s | %.1f%% | %s | %s | %s | %s | %.2f |" % (
+            v, 100 * x["SQ_VALU_MFMA_BUSY_CYCLES"] / simd, f("SQ_INSTS_MFMA"), f("SQ_INSTS_VALU"),
+            f("SQ_INSTS_SALU"), f("SQ_INSTS_LDS"), x["SQ_LDS_BANK_CONFLICT"] / max(x["SQ_INSTS_LDS"], 1)))
+    out += ["", "Units (32 queries x 32 keys x one head) are counted only for the dense variants, "
+            "where every pair is computed.  VALU counts include the MFMA instructions.", ""]
+    return "\n".join(out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("dir")
+    sm = sub.add_parser("stats-md")
+    sm.add_argument("dir")
+    sm.add_argument("--bench", required=True)
+    sm.add_argument("--workload", required=True)
+    c = sub.add_parser("counters-md")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--workload", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("dir_fetch")
     t.add_argument("dir_write")
     t.add_argument("--workload", required=True)
     t.add_argument("--out", required=True)
+    t.add_argument("--md", default=None)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats_table(a.dir))
-    else:
+    elif a.cmd == "counters-md":
         from flashattention_attention_variants_amd import inputs
+        wl = inputs.WORKLOADS[a.workload]
+        sh = wl.shape
+        dense = sh["B"] * sh["Hq"] * (sh["S"] // 32) ** 2
+        units = {v: dense for v in ("vanilla", "alibi", "softcap")}
+        path = os.path.join(ROOT, "profiles", "attn_mfma_kernel_%s_counters.md" % a.workload)
+        with open(path, "w") as fh:
+            fh.write(counters_markdown(a.dirs, list(wl.variants), a.workload, units))
+        print("wrote", path)
+    elif a.cmd == "stats-md":
+        path = os.path.join(ROOT, "profiles", "attn_mfma_kernel_%s_stats.md" % a.workload)
+        with open(path, "w") as fh:
+            fh.write(stats_markdown(a.dir, a.bench, a.workload))
+        print("wrote", path)
+    else:
+        from flashattention_attention_variants_amd import flops, inputs
         wl = inputs.WORKLOADS[a.workload]
         rec = traffic(a.dir_fetch, a.dir_write, list(wl.variants))
         rec["workload"] = a.workload
+        sh = wl.shape
+        rec["algorithmic_bytes"] = flops.attn_bytes(sh["B"], sh["Hq"], sh["Hkv"], sh["S"], sh["S"], sh["D"])
         with open(a.out, "w") as fh:
             json.dump(rec, fh, indent=1)
             fh.write("\n")
+        if a.md:
+            with open(a.md, "w") as fh:
+                fh.write(traffic_markdown(rec))
         print(json.dumps(rec, indent=1))
 
 
