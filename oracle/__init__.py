@@ -54,6 +54,7 @@ class _Params(ctypes.Structure):
         ("prefix", ctypes.c_int),
         ("doc_offsets", ctypes.c_void_p),
         ("n_docs", ctypes.c_int),
+        ("mask", ctypes.c_int),
     ]
 
 
@@ -101,12 +102,14 @@ def _rows(rows, total):
 
 def attn(q, k, v, *, variant="vanilla", scale=None, bias=None, softcap=50.0,
          alibi_max_bias=8.0, window=256, window_causal=True, prefix=512,
-         doc_offsets=None, rows=None, block_keys=0, threads=None):
+         doc_offsets=None, mask=None, rows=None, block_keys=0, threads=None):
     """Attention forward for q [B,Hq,Sq,D], k [B,Hkv,Sk,D], v [B,Hkv,Sk,Dv].
 
     Returns (o, lse).  With ``rows`` (flat indices (b*Hq+h)*Sq+i) the outputs
     are compact [n_rows, Dv] and [n_rows]; otherwise [B,Hq,Sq,Dv] and [B,Hq,Sq].
-    ``block_keys > 0`` selects the online twin.
+    ``mask`` (a mask variant name) composes a mask with the score modification
+    of ``variant`` (vanilla, alibi or softcap).  ``block_keys > 0`` selects
+    the online twin.
     """
     q, k, v, bias = _f64(q), _f64(k), _f64(v), _f64(bias)
     B, Hq, Sq, D = q.shape
@@ -115,14 +118,15 @@ def attn(q, k, v, *, variant="vanilla", scale=None, bias=None, softcap=50.0,
     if bias is not None:
         assert bias.shape == (Hq, Sq, Sk)
     var = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    msk = 0 if mask is None else (VARIANTS[mask] if isinstance(mask, str) else int(mask))
     docs = None
-    if var == DOCUMENT:
+    if var == DOCUMENT or msk == DOCUMENT:
         docs = np.ascontiguousarray(doc_offsets, dtype=np.int32)
         assert docs.ndim == 2 and docs.shape[0] == B
     p = _Params(var, float(scale if scale is not None else 1.0 / np.sqrt(D)), float(softcap),
                 float(alibi_max_bias), int(window), int(bool(window_causal)), int(prefix),
                 None if docs is None else docs.ctypes.data,
-                0 if docs is None else docs.shape[1] - 1)
+                0 if docs is None else docs.shape[1] - 1, msk)
     r, n = _rows(rows, B * Hq * Sq)
     o = np.empty((n, Dv), np.float64)
     lse = np.empty((n,), np.float64)

@@ -40,8 +40,17 @@ static int doc_of(const int32_t* off, int n_docs, int x) {
   return -1;
 }
 
+/* The mask in force: the variant's own, or the one composed with a score
+ * modification.  The pages' point is that variants compose freely (the
+ * gist.science explainer, "Technical Summary: Methodology": arbitrary
+ * attention programs; papers.lqhl.me wiki, "核心方法"); a composed variant
+ * modifies the scores and then masks them, the same order as a single one. */
+static int mask_kind(const oracle_attn_params* p) {
+  return p->variant >= ORACLE_CAUSAL ? p->variant : p->mask;
+}
+
 static int allowed(const oracle_attn_params* p, int b, int i, int j) {
-  switch (p->variant) {
+  switch (mask_kind(p)) {
     case ORACLE_CAUSAL:
       /* top-left aligned: a query sees itself and everything before it */
       return j <= i;
@@ -250,9 +259,13 @@ int oracle_attn_rows(const double* q, const double* k, const double* v,
                      int64_t n_rows, int block_keys, int nthreads) {
   if (!q || !k || !v || !o || !p) return -1;
   if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || Sq < 0 || Sk < 0 || D < 1 || Dv < 1) return -2;
-  if (p->variant == ORACLE_DOCUMENT && (!p->doc_offsets || p->n_docs < 1)) return -3;
+  if (p->variant < ORACLE_VANILLA || p->variant > ORACLE_DOCUMENT) return -3;
+  if (p->mask != ORACLE_VANILLA &&
+      (p->variant >= ORACLE_CAUSAL || p->mask < ORACLE_CAUSAL || p->mask > ORACLE_DOCUMENT))
+    return -3;
+  if (mask_kind(p) == ORACLE_DOCUMENT && (!p->doc_offsets || p->n_docs < 1)) return -3;
   if (p->variant == ORACLE_SOFTCAP && !(p->softcap > 0.0)) return -3;
-  if (p->variant == ORACLE_SLIDING_WINDOW && p->window < 1) return -3;
+  if (mask_kind(p) == ORACLE_SLIDING_WINDOW && p->window < 1) return -3;
   const int64_t total = (int64_t)B * Hq * Sq;
   if (check_rows(rows, n_rows, total)) return -4;
   attn_job J = {q, k, v, bias, o, lse, B, Hq, Hkv, Sq, Sk, D, Dv, p, rows, n_rows, block_keys};

@@ -59,6 +59,10 @@ typedef struct {
   int prefix;               /* ORACLE_PREFIX_LM: j < P or j <= i */
   const int32_t* doc_offsets; /* ORACLE_DOCUMENT: [B][n_docs+1], 0 = o_0 < ... < o_n = S */
   int n_docs;
+  int mask;                 /* ORACLE_VANILLA (none) or a mask kind (CAUSAL, SLIDING_WINDOW,
+                               PREFIX_LM, DOCUMENT) applied together with the score
+                               modification of `variant` (VANILLA, ALIBI, SOFTCAP); must be
+                               VANILLA when `variant` is itself a mask */
 } oracle_attn_params;
 
 /*

@@ -32,8 +32,10 @@ def mask_matrix(variant, Sq, Sk, *, window=1, window_causal=True, prefix=0, offs
 
 
 def attention(q, k, v, *, variant="vanilla", scale=None, bias=None, softcap=50.0,
-              alibi_max_bias=8.0, window=1, window_causal=True, prefix=0, doc_offsets=None):
-    """q [B,Hq,Sq,D], k [B,Hkv,Sk,D], v [B,Hkv,Sk,Dv] -> (o, lse), float64."""
+              alibi_max_bias=8.0, window=1, window_causal=True, prefix=0, doc_offsets=None,
+              mask=None):
+    """q [B,Hq,Sq,D], k [B,Hkv,Sk,D], v [B,Hkv,Sk,Dv] -> (o, lse), float64.
+    ``mask`` composes a mask variant with the score modification of ``variant``."""
     q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
     B, Hq, Sq, D = q.shape
     Hkv, Sk, Dv = k.shape[1], k.shape[2], v.shape[3]
@@ -42,7 +44,7 @@ def attention(q, k, v, *, variant="vanilla", scale=None, bias=None, softcap=50.0
     o = np.zeros((B, Hq, Sq, Dv))
     lse = np.full((B, Hq, Sq), -np.inf)
     for b in range(B):
-        allowed = mask_matrix(variant, Sq, Sk, window=window, window_causal=window_causal,
+        allowed = mask_matrix(mask or variant, Sq, Sk, window=window, window_causal=window_causal,
                               prefix=prefix,
                               offsets=None if doc_offsets is None else doc_offsets[b])
         for h in range(Hq):

@@ -498,3 +498,89 @@ def test_evoformer_special_cases(oracle_mod):
     # every key masked: the row is 0
     none = np.zeros((N, L), np.uint8)
     assert np.abs(oracle_mod.evoformer(q, k, v, g, pair_bias=bias, key_mask=none)).max() == 0.0
+
+
+# --------------------------------------------------------------------------
+# composed variants: a score modification under a mask
+
+MODS = ("vanilla", "alibi", "softcap")
+MASKS = ("causal", "sliding_window", "prefix_lm", "document")
+
+
+def compose_kw(mod, mask, S, rng, B):
+    kw = dict(variant=mod, mask=mask)
+    kw.update({k: v for k, v in kw_for(mask, S, rng, B).items() if k != "variant"})
+    if mod == "softcap":
+        kw.update(softcap=1.5)  # small, so the cap matters
+    if mod == "alibi":
+        kw.update(alibi_max_bias=8.0)
+    return kw
+
+
+@pytest.mark.parametrize("mod", MODS)
+@pytest.mark.parametrize("mask", MASKS)
+@pytest.mark.parametrize("S", [5, 33])
+def test_composed_matches_bruteforce(oracle_mod, mod, mask, S):
+    rng = np.random.default_rng(200 + S + 7 * MASKS.index(mask) + 31 * MODS.index(mod))
+    B, Hq, Hkv, D, Dv = 2, 4, 2, 8, 6
+    q, k, v = rnd(rng, B, Hq, S, D, scale=2.0), rnd(rng, B, Hkv, S, D), rnd(rng, B, Hkv, S, Dv)
+    kw = compose_kw(mod, mask, S, rng, B)
+    o, lse = oracle_mod.attn(q, k, v, **kw)
+    o_bf, lse_bf = bf.attention(q, k, v, **kw)
+    np.testing.assert_allclose(o, o_bf, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_bf, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("mask", MASKS)
+def test_composed_special_cases(oracle_mod, mask):
+    """vanilla under a mask is that mask's variant; softcap with a huge cap
+    under a mask is the mask alone."""
+    rng = np.random.default_rng(300 + MASKS.index(mask))
+    B, S = 2, 24
+    q, k, v = rnd(rng, B, 2, S, 8), rnd(rng, B, 2, S, 8), rnd(rng, B, 2, S, 5)
+    kw = {k_: v_ for k_, v_ in kw_for(mask, S, rng, B).items() if k_ != "variant"}
+    plain = oracle_mod.attn(q, k, v, variant=mask, **kw)
+    same = oracle_mod.attn(q, k, v, variant="vanilla", mask=mask, **kw)
+    np.testing.assert_array_equal(plain[0], same[0])
+    big = oracle_mod.attn(q, k, v, variant="softcap", softcap=1e7, mask=mask, **kw)
+    np.testing.assert_allclose(big[0], plain[0], atol=1e-9)
+
+
+def test_alibi_under_causal_equals_sdpa_bias(oracle_mod):
+    """ALiBi composed with the causal mask is softmax(qk/sqrt(d) + slope*(j-i))
+    over j <= i: SDPA in float64 with that additive float mask."""
+    rng = np.random.default_rng(310)
+    S, H = 17, 4
+    q, k, v = rnd(rng, 1, H, S, 8), rnd(rng, 1, H, S, 8), rnd(rng, 1, H, S, 6)
+    o, _ = oracle_mod.attn(q, k, v, variant="alibi", mask="causal")
+    i, j = np.arange(S)[:, None], np.arange(S)[None, :]
+    slopes = 2.0 ** (-8.0 * (np.arange(H) + 1) / H)
+    bias = np.where(j <= i, slopes[:, None, None] * (j - i), -np.inf)
+    np.testing.assert_allclose(o, sdpa(q, k, v, attn_mask=torch.from_numpy(bias)[None]), atol=1e-12)
+
+
+def test_alibi_causal_uniform_scores_closed_form(oracle_mod):
+    """Q = 0 under ALiBi and the causal mask: row i weights key j <= i by
+    r^(i-j) with r = e^(-slope), so O_i = sum r^(i-j) v_j / sum r^(i-j)."""
+    S, H = 40, 2
+    q = np.zeros((1, H, S, 4))
+    k = np.ones((1, H, S, 4))
+    v = np.random.default_rng(311).standard_normal((1, H, S, 3))
+    o, lse = oracle_mod.attn(q, k, v, variant="alibi", mask="causal", alibi_max_bias=3.0)
+    for h in range(H):
+        r = math.exp(-(2.0 ** (-3.0 * (h + 1) / H)))
+        for i in (0, 1, 7, S - 1):
+            w = r ** (i - np.arange(i + 1))
+            np.testing.assert_allclose(o[0, h, i], w @ v[0, h, : i + 1] / w.sum(), atol=1e-12)
+            assert abs(lse[0, h, i] - math.log(w.sum())) < 1e-12
+
+
+def test_composed_rejects_bad_arguments(oracle_mod):
+    rng = np.random.default_rng(312)
+    q = k = v = rnd(rng, 1, 1, 4, 4)
+    with pytest.raises(ValueError):
+        oracle_mod.attn(q, k, v, variant="causal", mask="prefix_lm")  # a mask variant takes no mask
+    with pytest.raises(ValueError):
+        oracle_mod.attn(q, k, v, variant="alibi", mask="softcap")  # not a mask
+    with pytest.raises(ValueError):
+        oracle_mod.attn(q, k, v, variant="softcap", mask="sliding_window", window=0)
