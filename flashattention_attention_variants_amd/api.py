@@ -46,6 +46,7 @@ class AttnParams(ctypes.Structure):
         ("prefix", ctypes.c_int32),
         ("n_docs", ctypes.c_int32),
         ("doc_offsets", ctypes.c_void_p),
+        ("mask", ctypes.c_int32),
     ]
 
 
@@ -115,11 +116,13 @@ def _stream(stream):
 
 def fl_attn_fwd(q, k, v, *, variant="vanilla", scale=None, bias=None, softcap=50.0,
                 alibi_max_bias=8.0, window=256, window_causal=True, prefix=512,
-                doc_offsets=None, out=None, lse=None, return_lse=False, stream=None):
+                doc_offsets=None, mask=None, out=None, lse=None, return_lse=False, stream=None):
     """softmax(score_mod(scale q k^T) + bias) v for q [B,Hq,Sq,D], k/v [B,Hkv,Sk,D].
 
-    Returns ``o`` or ``(o, lse)``; ``lse`` [B,Hq,Sq] float32 is computed when
-    given or when ``return_lse``.
+    ``mask`` (a mask variant name) composes a mask with the score
+    modification of ``variant`` (vanilla, alibi or softcap).  Returns ``o``
+    or ``(o, lse)``; ``lse`` [B,Hq,Sq] float32 is computed when given or when
+    ``return_lse``.
     """
     q = _dev(q, "q")
     dt = q.dtype
@@ -134,13 +137,14 @@ def fl_attn_fwd(q, k, v, *, variant="vanilla", scale=None, bias=None, softcap=50
         lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=q.device)
     _dev(lse, "lse", torch.float32)
     var = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    msk = 0 if mask is None else (VARIANTS[mask] if isinstance(mask, str) else int(mask))
     docs = None
-    if var == VARIANTS["document"]:
+    if VARIANTS["document"] in (var, msk):
         docs = _dev(doc_offsets, "doc_offsets", torch.int32)
     p = AttnParams(var, float(scale if scale is not None else 1.0 / math.sqrt(D)), float(softcap),
                    float(alibi_max_bias), int(window), int(bool(window_causal)), int(prefix),
                    0 if docs is None else docs.shape[-1] - 1,
-                   None if docs is None else docs.data_ptr())
+                   None if docs is None else docs.data_ptr(), msk)
     st = load_library().fl_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(out), _ptr(lse),
                                     B, Hq, Hkv, Sq, Sk, D, _dtype_code(q), ctypes.byref(p),
                                     _stream(stream))

@@ -68,15 +68,19 @@ fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* b
   if (dtype != FL_BF16 && dtype != FL_F32) return FL_ERR_UNSUPPORTED;
   if (p->variant < FL_VANILLA || p->variant > FL_DOCUMENT) return FL_ERR_PARAM;
   if (!isfinite(p->scale)) return FL_ERR_PARAM;
-  const bool positional = p->variant == FL_CAUSAL || p->variant == FL_SLIDING_WINDOW ||
-                          p->variant == FL_PREFIX_LM || p->variant == FL_DOCUMENT;
-  if (positional && S_q != S_k) return FL_ERR_SHAPE;
+  // the mask in force: the variant's own, or one composed with a score
+  // modification (vanilla, ALiBi, softcap)
+  const bool variant_is_mask = p->variant >= FL_CAUSAL;
+  if (p->mask != FL_VANILLA && (variant_is_mask || p->mask < FL_CAUSAL || p->mask > FL_DOCUMENT))
+    return FL_ERR_PARAM;
+  const int mask = variant_is_mask ? p->variant : p->mask;
+  if (mask != FL_VANILLA && S_q != S_k) return FL_ERR_SHAPE;
   if (p->variant == FL_SOFTCAP && !(p->softcap > 0.0f && isfinite(p->softcap))) return FL_ERR_PARAM;
   if (p->variant == FL_ALIBI && !(p->alibi_max_bias >= 0.0f && isfinite(p->alibi_max_bias)))
     return FL_ERR_PARAM;
-  if (p->variant == FL_SLIDING_WINDOW && p->window < 1) return FL_ERR_PARAM;
-  if (p->variant == FL_PREFIX_LM && p->prefix < 0) return FL_ERR_PARAM;
-  if (p->variant == FL_DOCUMENT) {
+  if (mask == FL_SLIDING_WINDOW && p->window < 1) return FL_ERR_PARAM;
+  if (mask == FL_PREFIX_LM && p->prefix < 0) return FL_ERR_PARAM;
+  if (mask == FL_DOCUMENT) {
     if (p->n_docs < 1) return FL_ERR_PARAM;
     if (!p->doc_offsets) return FL_ERR_NULL;
   }
@@ -112,16 +116,15 @@ fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* b
   a.sk = S_k;
   a.scale_log2 = p->scale * kLog2e;
   int mod = MOD_NONE;
-  switch (p->variant) {
-    case FL_ALIBI:
-      mod = MOD_ALIBI;
-      a.alibi_max_bias = p->alibi_max_bias;
-      break;
-    case FL_SOFTCAP:
-      mod = MOD_SOFTCAP;
-      a.softcap_arg = 2.0f * p->scale * kLog2e / p->softcap;
-      a.softcap_log2 = p->softcap * kLog2e;
-      break;
+  if (p->variant == FL_ALIBI) {
+    mod = MOD_ALIBI;
+    a.alibi_max_bias = p->alibi_max_bias;
+  } else if (p->variant == FL_SOFTCAP) {
+    mod = MOD_SOFTCAP;
+    a.softcap_arg = 2.0f * p->scale * kLog2e / p->softcap;
+    a.softcap_log2 = p->softcap * kLog2e;
+  }
+  switch (mask) {
     case FL_CAUSAL:
       a.iv_kind = IV_CAUSAL;
       a.heavy_first = 1;

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define FL_ABI_VERSION 1
+#define FL_ABI_VERSION 2
 
 typedef enum {
   FL_OK = 0,
@@ -64,7 +64,10 @@ typedef enum { FL_BF16 = 0, FL_F32 = 1 } fl_dtype;
  *   FL_DOCUMENT        query and key lie in the same document of
  *                      doc_offsets (block diagonal, not causal).
  * s is the scaled score scale * q.k; the score modification acts on s, the
- * bias is added after it, and masked keys are excluded.
+ * bias is added after it, and masked keys are excluded.  A score
+ * modification composes with any mask through fl_attn_params.mask (the
+ * pages' premise that variants compose freely: gist.science explainer,
+ * "Technical Summary: Methodology"; papers.lqhl.me wiki, "核心方法").
  */
 typedef enum {
   FL_VANILLA = 0,
@@ -90,6 +93,14 @@ typedef struct {
                                  on the host (it is device memory); offsets
                                  outside [0, S] are clamped, never followed
                                  out of bounds. */
+  int32_t mask;            /* A mask composed with the score modification of
+                              `variant` (FL_VANILLA, FL_ALIBI or FL_SOFTCAP):
+                              FL_VANILLA for none, or FL_CAUSAL,
+                              FL_SLIDING_WINDOW, FL_PREFIX_LM, FL_DOCUMENT with
+                              their parameters above.  The score is modified,
+                              the bias added, then the mask applied.  Must be
+                              FL_VANILLA when `variant` is itself a mask
+                              (FL_ERR_PARAM otherwise).  Added in ABI 2. */
 } fl_attn_params;
 
 /*
@@ -102,7 +113,7 @@ typedef struct {
  *   o    [B, H_q, S_q, D]    output, same dtype as q
  *   lse  NULL or [B, H_q, S_q] float32 natural-log logsumexp of the scores
  * Requires H_q % H_kv == 0; S_q == S_k for the positional masks (causal,
- * sliding window, PrefixLM, document).  D: 64 for FL_BF16; 32, 64 or 128
+ * sliding window, PrefixLM, document), as variants or composed.  D: 64 for FL_BF16; 32, 64 or 128
  * for FL_F32.  FL_BF16 also requires S_k * D * 2 < 2^31 (one K/V head block
  * is addressed with 32-bit byte offsets); larger S_k returns FL_ERR_SHAPE.
  */

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.fl_abi_version() == 1
+    assert lib.fl_abi_version() == 2
     for s in range(7):
         assert lib.fl_status_str(s)
     assert lib.fl_status_str(99) == b"unknown status"
@@ -48,7 +48,7 @@ MISALIGNED = P(0x10008)
 
 
 def params(variant=0, **kw):
-    p = api.AttnParams(variant, 0.125, 50.0, 8.0, 256, 1, 512, 0, None)
+    p = api.AttnParams(variant, 0.125, 50.0, 8.0, 256, 1, 512, 0, None, 0)
     for k, v in kw.items():
         setattr(p, k, v)
     return p
@@ -83,6 +83,14 @@ def test_attn_validation(lib):
     assert attn(lib, params(scale=float("nan"))) == api.FL_ERR_PARAM
     for var in (3, 4, 5):  # positional masks need S_q == S_k
         assert attn(lib, params(variant=var), Sq=8, Sk=16) == api.FL_ERR_SHAPE
+    # a composed mask: only with a score modification, only a mask kind
+    assert attn(lib, params(variant=3, mask=4)) == api.FL_ERR_PARAM
+    assert attn(lib, params(variant=1, mask=2)) == api.FL_ERR_PARAM
+    assert attn(lib, params(variant=2, mask=7)) == api.FL_ERR_PARAM
+    assert attn(lib, params(variant=1, mask=3), Sq=8, Sk=16) == api.FL_ERR_SHAPE
+    assert attn(lib, params(variant=2, mask=4, window=0)) == api.FL_ERR_PARAM
+    assert attn(lib, params(variant=0, mask=5, prefix=-1)) == api.FL_ERR_PARAM
+    assert attn(lib, params(variant=1, mask=6, n_docs=2)) == api.FL_ERR_NULL
     # nothing to write: success without touching the pointers
     assert attn(lib, params(), q=None, k=None, v=None, o=None, B=0) == api.FL_OK
     assert attn(lib, params(), q=None, k=None, v=None, o=None, Sq=0) == api.FL_OK

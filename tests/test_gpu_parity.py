@@ -342,6 +342,77 @@ def test_evoformer_col(dtype, N_seq):
 
 
 # ---------------------------------------------------------------------------
+# a score modification composed with a mask
+
+
+MODS = ("vanilla", "alibi", "softcap")
+MASKS = ("causal", "sliding_window", "prefix_lm", "document")
+
+
+def composed_kw(mod, mask, S, B, seed, window_causal=True):
+    kw = variant_kw(mod, S, B, seed)
+    m = variant_kw(mask, S, B, seed, window_causal=window_causal)
+    m["mask"] = m.pop("variant")
+    kw.update(m)
+    return kw
+
+
+@pytest.mark.parametrize("S", [77, 300, 513])
+@pytest.mark.parametrize("mask", MASKS)
+@pytest.mark.parametrize("mod", MODS)
+def test_bf16_composed(mod, mask, S):
+    B, Hq, Hkv, D = 2, 4, 2, 64
+    seed = 400 + S + 7 * MASKS.index(mask) + 31 * MODS.index(mod)
+    q, k, v = inputs.attn_inputs(B, Hq, Hkv, S, S, D, "bf16", seed=seed)
+    kw = composed_kw(mod, mask, S, B, seed + 1)
+    o, lse = run_gpu_attn(q, k, v, **kw)
+    ro, rl = run_oracle_attn(q, k, v, **kw)
+    check(np64(o), ro, "bf16", "%s+%s S=%d" % (mod, mask, S))
+    mx, _, _ = errors(np64(lse), rl)
+    assert mx <= 2e-2, "lse %g" % mx
+
+
+@pytest.mark.parametrize("mask", MASKS)
+@pytest.mark.parametrize("mod", ["alibi", "softcap"])
+def test_f32_composed(mod, mask):
+    B, Hq, Hkv, S, D = 2, 4, 2, 150, 64
+    seed = 500 + 7 * MASKS.index(mask) + 31 * MODS.index(mod)
+    q, k, v = inputs.attn_inputs(B, Hq, Hkv, S, S, D, "f32", seed=seed)
+    kw = composed_kw(mod, mask, S, B, seed + 1)
+    o, lse = run_gpu_attn(q, k, v, **kw)
+    ro, rl = run_oracle_attn(q, k, v, **kw)
+    check(np64(o), ro, "f32", "%s+%s" % (mod, mask))
+    check(np64(lse), rl, "f32", "%s+%s lse" % (mod, mask))
+
+
+@pytest.mark.parametrize("mod", ["alibi", "softcap"])
+def test_bf16_composed_two_sided_window_and_bias(mod):
+    # a two-sided window puts ALiBi keys on both sides of the diagonal; a bias
+    # sends the modified scores through the general path
+    B, H, S = 1, 4, 336  # bf16 bias rows are whole 16-byte groups
+    q, k, v = inputs.attn_inputs(B, H, H, S, S, 64, "bf16", seed=77)
+    kw = composed_kw(mod, "sliding_window", S, B, 78, window_causal=False)
+    o, lse = run_gpu_attn(q, k, v, **kw)
+    ro, rl = run_oracle_attn(q, k, v, **kw)
+    check(np64(o), ro, "bf16", "%s two-sided" % mod)
+    bias = inputs.bias_inputs(H, S, S, "bf16", seed=79)
+    kw = composed_kw(mod, "causal", S, B, 80)
+    o, lse = run_gpu_attn(q, k, v, bias=bias, **kw)
+    ro, rl = run_oracle_attn(q, k, v, bias=bias, **kw)
+    check(np64(o), ro, "bf16", "%s causal + bias" % mod)
+
+
+def test_composed_equals_variant_when_trivial():
+    # vanilla scores under a composed causal mask are the causal variant, bit
+    # for bit: the same kernel instance runs
+    B, H, S = 1, 2, 300
+    q, k, v = inputs.attn_inputs(B, H, H, S, S, 64, "bf16", seed=81)
+    a, la = run_gpu_attn(q, k, v, variant="vanilla", mask="causal")
+    b, lb = run_gpu_attn(q, k, v, variant="causal")
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+# ---------------------------------------------------------------------------
 # full workload sizes, sampled rows
 
 
@@ -376,6 +447,28 @@ def test_full_mha_s2048_all_variants():
 
 def test_full_mha_s4096_all_variants():
     _full_attn("mha_bf16_b4_h16_s4096_d64", inputs.ALL_MASK_VARIANTS, 256)
+
+
+def test_full_mha_s4096_composed():
+    wl = inputs.WORKLOADS["mha_bf16_b4_h16_s4096_d64"]
+    t = inputs.make(wl)
+    s = wl.shape
+    q, k, v = t["q"].to(DEV), t["k"].to(DEV), t["v"].to(DEV)
+    q64, k64, v64 = np64(t["q"]), np64(t["k"]), np64(t["v"])
+    rows = sample_rows(s["B"], s["Hq"], s["S"], 192, seed=9)
+    docs = t["doc_offsets"]
+    for mod, mask in (("alibi", "causal"), ("softcap", "causal"), ("softcap", "sliding_window"),
+                      ("alibi", "document"), ("softcap", "prefix_lm")):
+        kw = dict(variant=mod, mask=mask)
+        for key in ("softcap", "alibi_max_bias", "window", "window_causal", "prefix"):
+            if key in wl.params:
+                kw[key] = wl.params[key]
+        o, lse = run_gpu_attn(q, k, v, doc_offsets=docs if mask == "document" else None, **kw)
+        ro, rl = oracle.attn(q64, k64, v64, rows=rows,
+                             doc_offsets=docs.numpy() if mask == "document" else None, **kw)
+        check(gpu_rows(o, rows), ro, "bf16", "%s+%s" % (mod, mask))
+        mx, _, _ = errors(np64(lse).reshape(-1)[rows], rl)
+        assert mx < 2e-2, (mod, mask, mx)
 
 
 def test_full_gqa_s16384():
