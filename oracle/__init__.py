@@ -74,8 +74,11 @@ def _load():
                                              D, D, I, P, I64, I]
         lib.oracle_evoformer_row.argtypes = [P, P, P, P, P, P, P, I, I, I, I, D, P, I64, I]
         lib.oracle_evoformer_col.argtypes = [P, P, P, P, P, P, I, I, I, I, D, P, I64, I]
-        for f in (lib.oracle_attn_rows, lib.oracle_diffattn_rows,
-                  lib.oracle_evoformer_row, lib.oracle_evoformer_col):
+        lib.oracle_decode_rows.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I,
+                                           ctypes.POINTER(_Params), P, I64, I, I]
+        lib.oracle_merge_rows.argtypes = [P, P, P, P, I, I64, I]
+        for f in (lib.oracle_attn_rows, lib.oracle_diffattn_rows, lib.oracle_evoformer_row,
+                  lib.oracle_evoformer_col, lib.oracle_decode_rows, lib.oracle_merge_rows):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -138,6 +141,52 @@ def attn(q, k, v, *, variant="vanilla", scale=None, bias=None, softcap=50.0,
     if rows is None:
         return o.reshape(B, Hq, Sq, Dv), lse.reshape(B, Hq, Sq)
     return o, lse
+
+
+def decode(q, k_cache, v_cache, seqlens, *, variant="vanilla", scale=None, softcap=50.0,
+           alibi_max_bias=8.0, window=256, window_causal=True, prefix=512, mask=None, rows=None,
+           block_keys=0, threads=None):
+    """Decode attention against a KV cache: q [B,Hq,Sq,D] are the Sq newest
+    tokens of each sequence, k_cache/v_cache [B,Hkv,S_cap,D/Dv] hold
+    seqlens[b] tokens, so query i sits at position seqlens[b] - Sq + i.
+    Returns (o, lse) shaped like :func:`attn`."""
+    q, k, v = _f64(q), _f64(k_cache), _f64(v_cache)
+    B, Hq, Sq, D = q.shape
+    _, Hkv, S_cap, Dv = v.shape
+    assert k.shape == (B, Hkv, S_cap, D)
+    L = np.ascontiguousarray(seqlens, dtype=np.int32)
+    assert L.shape == (B,)
+    var = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    msk = 0 if mask is None else (VARIANTS[mask] if isinstance(mask, str) else int(mask))
+    p = _Params(var, float(scale if scale is not None else 1.0 / np.sqrt(D)), float(softcap),
+                float(alibi_max_bias), int(window), int(bool(window_causal)), int(prefix),
+                None, 0, msk)
+    r, n = _rows(rows, B * Hq * Sq)
+    o = np.empty((n, Dv), np.float64)
+    lse = np.empty((n,), np.float64)
+    rc = _load().oracle_decode_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(L), _ptr(o), _ptr(lse),
+                                    B, Hq, Hkv, Sq, S_cap, D, Dv, ctypes.byref(p), _ptr(r), n,
+                                    int(block_keys), threads or default_threads())
+    if rc:
+        raise ValueError("oracle_decode_rows rejected its arguments (%d)" % rc)
+    if rows is None:
+        return o.reshape(B, Hq, Sq, Dv), lse.reshape(B, Hq, Sq)
+    return o, lse
+
+
+def merge(o_parts, lse_parts):
+    """Merge partial results over disjoint key sets: o_parts [P, ..., Dv],
+    lse_parts [P, ...] -> (o [..., Dv], lse [...])."""
+    op, lp = _f64(o_parts), _f64(lse_parts)
+    assert op.shape[:-1] == lp.shape and op.ndim >= 2
+    P, Dv = op.shape[0], op.shape[-1]
+    n = int(np.prod(lp.shape[1:], dtype=np.int64))
+    o = np.empty((n, Dv), np.float64)
+    lse = np.empty((n,), np.float64)
+    rc = _load().oracle_merge_rows(_ptr(op), _ptr(lp), _ptr(o), _ptr(lse), P, n, Dv)
+    if rc:
+        raise ValueError("oracle_merge_rows rejected its arguments (%d)" % rc)
+    return o.reshape(lp.shape[1:] + (Dv,)), lse.reshape(lp.shape[1:])
 
 
 def diffattn(q1, q2, k1, k2, v, *, scale=None, lam=0.8, causal=False, rows=None,

@@ -100,7 +100,29 @@ typedef struct {
   const int64_t* rows;
   int64_t n_rows;
   int block_keys;
+  const int32_t* seqlens; /* decode: tokens held in each batch entry's cache */
 } attn_job;
+
+/* Where a query row sits and how many keys it may look at.  In a prefill
+ * call query i is position i and all S_k keys exist.  In a decode call the
+ * cache of batch entry b holds L_b tokens (0 <= L_b <= S_k), the S_q new
+ * queries are its last S_q tokens, so query i sits at position L_b - S_q + i,
+ * and keys at or past L_b do not exist.  The pages name decode-phase
+ * KV-cache attention only as serving work they leave untested (papers.lqhl.me
+ * wiki, "假设压力测试", serving path); the cache convention taken is the
+ * usual one, the new tokens appended before they attend. */
+static void row_geometry(const attn_job* J, int b, int i, int* pos, int* n_keys) {
+  if (!J->seqlens) {
+    *pos = i;
+    *n_keys = J->Sk;
+    return;
+  }
+  int L = J->seqlens[b];
+  if (L < 0) L = 0;
+  if (L > J->Sk) L = J->Sk;
+  *pos = L - J->Sq + i;
+  *n_keys = L;
+}
 
 static void attn_row_two_pass(const attn_job* J, int64_t flat, double* out,
                               double* lse_out, double* s_buf,
@@ -115,14 +137,16 @@ static void attn_row_two_pass(const attn_job* J, int64_t flat, double* out,
   const double* kb = J->k + ((int64_t)b * J->Hkv + hk) * Sk * D;
   const double* vb = J->v + ((int64_t)b * J->Hkv + hk) * Sk * Dv;
   const double* bias_row = J->bias ? J->bias + ((int64_t)h * Sq + i) * Sk : NULL;
+  int pos, nk;
+  row_geometry(J, b, i, &pos, &nk);
 
   /* pass 1: scores of the allowed keys and their maximum */
   double m = -INFINITY;
   int any = 0;
-  for (int j = 0; j < Sk; ++j) {
-    ok[j] = (unsigned char)allowed(J->p, b, i, j);
+  for (int j = 0; j < nk; ++j) {
+    ok[j] = (unsigned char)allowed(J->p, b, pos, j);
     if (!ok[j]) continue;
-    s_buf[j] = score(J->p, qi, kb + (int64_t)j * D, D, h, Hq, i, j, bias_row);
+    s_buf[j] = score(J->p, qi, kb + (int64_t)j * D, D, h, Hq, pos, j, bias_row);
     if (s_buf[j] > m) m = s_buf[j];
     any = 1;
   }
@@ -134,7 +158,7 @@ static void attn_row_two_pass(const attn_job* J, int64_t flat, double* out,
   }
   /* pass 2: sum of exponentials and the weighted sum of values */
   double l = 0.0;
-  for (int j = 0; j < Sk; ++j) {
+  for (int j = 0; j < nk; ++j) {
     if (!ok[j]) continue;
     const double e = exp(s_buf[j] - m);
     l += e;
@@ -164,16 +188,18 @@ static void attn_row_online(const attn_job* J, int64_t flat, double* out,
   const double* kb = J->k + ((int64_t)b * J->Hkv + hk) * Sk * D;
   const double* vb = J->v + ((int64_t)b * J->Hkv + hk) * Sk * Dv;
   const double* bias_row = J->bias ? J->bias + ((int64_t)h * Sq + i) * Sk : NULL;
+  int pos, nk;
+  row_geometry(J, b, i, &pos, &nk);
 
   double m = -INFINITY, l = 0.0;
   for (int d = 0; d < Dv; ++d) out[d] = 0.0;
-  for (int j0 = 0; j0 < Sk; j0 += nb) {
-    const int j1 = j0 + nb < Sk ? j0 + nb : Sk;
+  for (int j0 = 0; j0 < nk; j0 += nb) {
+    const int j1 = j0 + nb < nk ? j0 + nb : nk;
     double mb = -INFINITY;
     for (int j = j0; j < j1; ++j) {
-      ok[j] = (unsigned char)allowed(J->p, b, i, j);
+      ok[j] = (unsigned char)allowed(J->p, b, pos, j);
       if (!ok[j]) continue;
-      s_buf[j] = score(J->p, qi, kb + (int64_t)j * D, D, h, Hq, i, j, bias_row);
+      s_buf[j] = score(J->p, qi, kb + (int64_t)j * D, D, h, Hq, pos, j, bias_row);
       if (s_buf[j] > mb) mb = s_buf[j];
     }
     if (mb == -INFINITY) continue; /* nothing allowed in this block */
@@ -268,8 +294,69 @@ int oracle_attn_rows(const double* q, const double* k, const double* v,
   if (mask_kind(p) == ORACLE_SLIDING_WINDOW && p->window < 1) return -3;
   const int64_t total = (int64_t)B * Hq * Sq;
   if (check_rows(rows, n_rows, total)) return -4;
-  attn_job J = {q, k, v, bias, o, lse, B, Hq, Hkv, Sq, Sk, D, Dv, p, rows, n_rows, block_keys};
+  attn_job J = {q, k, v, bias, o, lse, B, Hq, Hkv, Sq, Sk, D, Dv, p, rows, n_rows, block_keys,
+               NULL};
   run_rows(&J, nthreads);
+  return 0;
+}
+
+int oracle_decode_rows(const double* q, const double* k_cache, const double* v_cache,
+                       const int32_t* seqlens, double* o, double* lse,
+                       int B, int Hq, int Hkv, int Sq, int S_cap, int D, int Dv,
+                       const oracle_attn_params* p, const int64_t* rows,
+                       int64_t n_rows, int block_keys, int nthreads) {
+  if (!q || !k_cache || !v_cache || !seqlens || !o || !p) return -1;
+  if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || Sq < 0 || S_cap < 0 || D < 1 || Dv < 1)
+    return -2;
+  if (p->variant < ORACLE_VANILLA || p->variant > ORACLE_PREFIX_LM) return -3;
+  if (p->mask != ORACLE_VANILLA &&
+      (p->variant >= ORACLE_CAUSAL || p->mask < ORACLE_CAUSAL || p->mask > ORACLE_PREFIX_LM))
+    return -3;
+  if (p->variant == ORACLE_SOFTCAP && !(p->softcap > 0.0)) return -3;
+  if (mask_kind(p) == ORACLE_SLIDING_WINDOW && p->window < 1) return -3;
+  const int64_t total = (int64_t)B * Hq * Sq;
+  if (check_rows(rows, n_rows, total)) return -4;
+  attn_job J = {q, k_cache, v_cache, NULL, o, lse, B, Hq, Hkv, Sq, S_cap, D, Dv, p, rows,
+               n_rows, block_keys, seqlens};
+  run_rows(&J, nthreads);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Merge of partial results over disjoint key sets.  Each part p carries the */
+/* softmax-normalised output O_p and log-sum-exp LSE_p of its keys; the      */
+/* whole is LSE = ln sum_p e^LSE_p and O = sum_p e^(LSE_p - LSE) O_p: the    */
+/* rescaling identity the single-pass rewrite rests on (gist.science         */
+/* explainer, "Technical Summary: Methodology", semantic fusion; papers.     */
+/* lqhl.me wiki, "关键观察", observation 2), applied to whole parts.  Parts  */
+/* with LSE = -inf hold no key and weigh nothing; if every part is empty the */
+/* row gets O = 0 and LSE = -inf.                                            */
+
+int oracle_merge_rows(const double* o_parts, const double* lse_parts, double* o, double* lse,
+                      int n_parts, int64_t n_rows, int Dv) {
+  if (!o_parts || !lse_parts || !o || n_parts < 1 || n_rows < 0 || Dv < 1) return -1;
+  for (int64_t r = 0; r < n_rows; ++r) {
+    double m = -INFINITY;
+    for (int p = 0; p < n_parts; ++p) {
+      const double x = lse_parts[(int64_t)p * n_rows + r];
+      if (x > m) m = x;
+    }
+    double* out = o + r * Dv;
+    for (int d = 0; d < Dv; ++d) out[d] = 0.0;
+    if (m == -INFINITY) {
+      if (lse) lse[r] = -INFINITY;
+      continue;
+    }
+    double l = 0.0;
+    for (int p = 0; p < n_parts; ++p) l += exp(lse_parts[(int64_t)p * n_rows + r] - m);
+    const double whole = m + log(l);
+    for (int p = 0; p < n_parts; ++p) {
+      const double w = exp(lse_parts[(int64_t)p * n_rows + r] - whole);
+      const double* op = o_parts + ((int64_t)p * n_rows + r) * Dv;
+      for (int d = 0; d < Dv; ++d) out[d] += w * op[d];
+    }
+    if (lse) lse[r] = whole;
+  }
   return 0;
 }
 

@@ -81,6 +81,30 @@ int oracle_attn_rows(const double* q, const double* k, const double* v,
                      int block_keys, int nthreads);
 
 /*
+ * Decode rows against a KV cache.  q [B,Hq,Sq,D] holds the Sq newest tokens
+ * of each batch entry; k_cache [B,Hkv,S_cap,D], v_cache [B,Hkv,S_cap,Dv]
+ * hold seqlens[b] valid tokens (clamped to [0, S_cap]; the new tokens are
+ * the last Sq of them), so query i sits at position seqlens[b] - Sq + i and
+ * keys j >= seqlens[b] do not exist.  Masks and ALiBi distances use these
+ * positions.  Variants: vanilla, ALiBi, softcap, causal, sliding window,
+ * PrefixLM, and a mask composed with a score modification; no bias, no
+ * document mask.  Rows, outputs and block_keys as for oracle_attn_rows.
+ */
+int oracle_decode_rows(const double* q, const double* k_cache, const double* v_cache,
+                       const int32_t* seqlens, double* o, double* lse,
+                       int B, int Hq, int Hkv, int Sq, int S_cap, int D, int Dv,
+                       const oracle_attn_params* p, const int64_t* rows,
+                       int64_t n_rows, int block_keys, int nthreads);
+
+/*
+ * Merge of partial results over disjoint key sets: o_parts [n_parts][n_rows][Dv]
+ * (each normalised over its own keys), lse_parts [n_parts][n_rows] (natural
+ * log, -inf for a part with no key).  o [n_rows][Dv]; lse [n_rows] or NULL.
+ */
+int oracle_merge_rows(const double* o_parts, const double* lse_parts, double* o, double* lse,
+                      int n_parts, int64_t n_rows, int Dv);
+
+/*
  * Differential attention rows: O = softmax(s(Q1,K1)) V - lambda * softmax(s(Q2,K2)) V
  * with the same scale, the same V and the same (optional causal) mask on both
  * maps.  q1,q2 [B,H,Sq,Dqk]; k1,k2 [B,H,Sk,Dqk]; v [B,H,Sk,Dv]; o [n_rows,Dv];

@@ -66,3 +66,50 @@ def attention(q, k, v, *, variant="vanilla", scale=None, bias=None, softcap=50.0
             o[b, h] = p @ vv
             lse[b, h] = l
     return o, lse
+
+
+def decode_attention(q, k_cache, v_cache, seqlens, *, variant="vanilla", scale=None, softcap=50.0,
+                     alibi_max_bias=8.0, window=1, window_causal=True, prefix=0, mask=None):
+    """Decode against a KV cache, by brute force: for each batch entry the
+    cache is cut to its length L, the Sq queries are given the positions of
+    the last Sq tokens (L - Sq .. L - 1), and the mask and ALiBi distances are
+    built from those position vectors."""
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k_cache, v_cache))
+    B, Hq, Sq, D = q.shape
+    Hkv, S_cap, Dv = k.shape[1], k.shape[2], v.shape[3]
+    G = Hq // Hkv
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    kind = mask or variant
+    o = np.zeros((B, Hq, Sq, Dv))
+    lse = np.full((B, Hq, Sq), -np.inf)
+    for b in range(B):
+        L = int(min(max(seqlens[b], 0), S_cap))
+        qpos = np.arange(L - Sq, L)
+        kpos = np.arange(L)
+        rel = qpos[:, None] - kpos[None, :]  # query position minus key position
+        if kind in ("vanilla", "alibi", "softcap"):
+            allowed = np.ones((Sq, L), bool)
+        elif kind == "causal":
+            allowed = rel >= 0
+        elif kind == "sliding_window":
+            allowed = (rel >= 0) & (rel < window) if window_causal else np.abs(rel) < window
+        elif kind == "prefix_lm":
+            allowed = (rel >= 0) | (kpos[None, :] < prefix)
+        else:
+            raise ValueError(kind)
+        for h in range(Hq):
+            s = scale * (q[b, h] @ k[b, h // G, :L].T)
+            if variant == "alibi":
+                s = s - 2.0 ** (-alibi_max_bias * (h + 1) / Hq) * np.abs(rel)
+            if variant == "softcap":
+                s = softcap * np.tanh(s / softcap)
+            s = np.where(allowed, s, -np.inf)
+            rows = allowed.any(1)
+            l = np.full(Sq, -np.inf)
+            if rows.any():
+                l[rows] = logsumexp(s[rows], axis=1)
+                p = np.zeros_like(s)
+                p[rows] = np.exp(s[rows] - l[rows, None])
+                o[b, h] = p @ v[b, h // G, :L]
+            lse[b, h] = l
+    return o, lse

@@ -6,6 +6,7 @@ CPU), a closed form, or an invariant of softmax attention, chosen so that a
 dropped term, a wrong sign, an off-by-one mask or a transposed operand fails
 at least one of them.  No GPU needed.
 """
+import functools
 import math
 
 import numpy as np
@@ -14,6 +15,9 @@ import torch
 import torch.nn.functional as F
 
 from tests import _bruteforce as bf
+
+# absolute tolerances only: numpy's default rtol of 1e-7 would hide small relative errors
+assert_close = functools.partial(np.testing.assert_allclose, rtol=0)
 
 VARIANTS = ("vanilla", "alibi", "softcap", "causal", "sliding_window", "prefix_lm", "document")
 
@@ -59,8 +63,8 @@ def test_matches_bruteforce(oracle_mod, variant, S):
     kw = kw_for(variant, S, rng, B)
     o, lse = oracle_mod.attn(q, k, v, **kw)
     o_bf, lse_bf = bf.attention(q, k, v, **kw)
-    np.testing.assert_allclose(o, o_bf, rtol=0, atol=1e-12)
-    np.testing.assert_allclose(lse, lse_bf, rtol=1e-12, atol=1e-12)
+    assert_close(o, o_bf, rtol=0, atol=1e-12)
+    assert_close(lse, lse_bf, rtol=1e-12, atol=1e-12)
 
 
 @pytest.mark.parametrize("window_causal", [True, False])
@@ -71,8 +75,8 @@ def test_window_bruteforce(oracle_mod, window, window_causal):
     kw = dict(variant="sliding_window", window=window, window_causal=window_causal)
     o, lse = oracle_mod.attn(q, k, v, **kw)
     o_bf, lse_bf = bf.attention(q, k, v, **kw)
-    np.testing.assert_allclose(o, o_bf, atol=1e-12)
-    np.testing.assert_allclose(lse, lse_bf, atol=1e-12)
+    assert_close(o, o_bf, atol=1e-12)
+    assert_close(lse, lse_bf, atol=1e-12)
 
 
 def test_bias_bruteforce(oracle_mod):
@@ -81,8 +85,8 @@ def test_bias_bruteforce(oracle_mod):
     bias = rnd(rng, 3, 9, 11)
     o, lse = oracle_mod.attn(q, k, v, bias=bias, scale=0.7)
     o_bf, lse_bf = bf.attention(q, k, v, bias=bias, scale=0.7)
-    np.testing.assert_allclose(o, o_bf, atol=1e-12)
-    np.testing.assert_allclose(lse, lse_bf, atol=1e-12)
+    assert_close(o, o_bf, atol=1e-12)
+    assert_close(lse, lse_bf, atol=1e-12)
 
 
 # --------------------------------------------------------------------------
@@ -98,21 +102,21 @@ def test_vanilla_equals_sdpa(oracle_mod):
     rng = np.random.default_rng(11)
     q, k, v = rnd(rng, 2, 3, 17, 16), rnd(rng, 2, 3, 23, 16), rnd(rng, 2, 3, 23, 16)
     o, _ = oracle_mod.attn(q, k, v, scale=0.3)
-    np.testing.assert_allclose(o, sdpa(q, k, v, scale=0.3), atol=1e-12)
+    assert_close(o, sdpa(q, k, v, scale=0.3), atol=1e-12)
 
 
 def test_causal_equals_sdpa(oracle_mod):
     rng = np.random.default_rng(12)
     q, k, v = rnd(rng, 1, 2, 31, 8), rnd(rng, 1, 2, 31, 8), rnd(rng, 1, 2, 31, 8)
     o, _ = oracle_mod.attn(q, k, v, variant="causal")
-    np.testing.assert_allclose(o, sdpa(q, k, v, is_causal=True), atol=1e-12)
+    assert_close(o, sdpa(q, k, v, is_causal=True), atol=1e-12)
 
 
 def test_gqa_equals_sdpa(oracle_mod):
     rng = np.random.default_rng(13)
     q, k, v = rnd(rng, 2, 8, 13, 8), rnd(rng, 2, 2, 13, 8), rnd(rng, 2, 2, 13, 8)
     o, _ = oracle_mod.attn(q, k, v, variant="causal")
-    np.testing.assert_allclose(o, sdpa(q, k, v, is_causal=True, enable_gqa=True), atol=1e-12)
+    assert_close(o, sdpa(q, k, v, is_causal=True, enable_gqa=True), atol=1e-12)
 
 
 def test_bias_equals_sdpa_float_mask(oracle_mod):
@@ -121,7 +125,7 @@ def test_bias_equals_sdpa_float_mask(oracle_mod):
     bias = rnd(rng, 2, 10, 12, scale=3.0)
     o, _ = oracle_mod.attn(q, k, v, bias=bias)
     ref = sdpa(q, k, v, attn_mask=torch.from_numpy(bias)[None])
-    np.testing.assert_allclose(o, ref, atol=1e-12)
+    assert_close(o, ref, atol=1e-12)
 
 
 # --------------------------------------------------------------------------
@@ -137,8 +141,8 @@ def test_online_twin_equals_two_pass(oracle_mod, variant, block):
     kw = kw_for(variant, S, rng)
     o2, l2 = oracle_mod.attn(q, k, v, **kw)
     o1, l1 = oracle_mod.attn(q, k, v, block_keys=block, **kw)
-    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-13)
-    np.testing.assert_allclose(l1, l2, rtol=1e-12, atol=1e-13)
+    assert_close(o1, o2, rtol=1e-12, atol=1e-13)
+    assert_close(l1, l2, rtol=1e-12, atol=1e-13)
 
 
 def test_merge_of_key_halves(oracle_mod):
@@ -150,8 +154,8 @@ def test_merge_of_key_halves(oracle_mod):
     ob, lb = oracle_mod.attn(q, k[:, :, 13:], v[:, :, 13:])
     lm = np.logaddexp(la, lb)
     om = np.exp(la - lm)[..., None] * oa + np.exp(lb - lm)[..., None] * ob
-    np.testing.assert_allclose(lm, l, atol=1e-12)
-    np.testing.assert_allclose(om, o, atol=1e-12)
+    assert_close(lm, l, atol=1e-12)
+    assert_close(om, o, atol=1e-12)
 
 
 # --------------------------------------------------------------------------
@@ -169,7 +173,7 @@ def test_probability_rows(oracle_mod, variant):
     kw = kw_for(variant, S, rng)
     p, _ = oracle_mod.attn(q, k, v, **kw)
     assert (p >= 0).all()
-    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-12)
+    assert_close(p.sum(-1), 1.0, atol=1e-12)
     allowed = bf.mask_matrix(variant, S, S, window=kw.get("window", 1), prefix=kw.get("prefix", 0),
                              offsets=None if variant != "document" else kw["doc_offsets"][0])
     assert (p[0, :, ~allowed] == 0).all()
@@ -220,8 +224,8 @@ def test_uniform_scores_give_mean_of_allowed_values(oracle_mod, variant):
     o, lse = oracle_mod.attn(q, k, v, **kw)
     csum = np.concatenate([np.zeros((1, 3)), np.cumsum(v[0, 0], 0)])
     mean = (csum[hi + 1] - csum[lo]) / (hi - lo + 1)[:, None]
-    np.testing.assert_allclose(o[0, 0], mean, atol=1e-12)
-    np.testing.assert_allclose(lse[0, 0], np.log(hi - lo + 1), atol=1e-12)
+    assert_close(o[0, 0], mean, atol=1e-12)
+    assert_close(lse[0, 0], np.log(hi - lo + 1), atol=1e-12)
 
 
 def test_window_one_returns_own_value(oracle_mod):
@@ -229,7 +233,7 @@ def test_window_one_returns_own_value(oracle_mod):
     q, k, v = rnd(rng, 1, 2, 19, 8), rnd(rng, 1, 2, 19, 8), rnd(rng, 1, 2, 19, 4)
     for causal in (True, False):
         o, lse = oracle_mod.attn(q, k, v, variant="sliding_window", window=1, window_causal=causal)
-        np.testing.assert_allclose(o, v, atol=1e-14)
+        assert_close(o, v, atol=1e-14)
 
 
 def test_unit_documents_return_own_value(oracle_mod):
@@ -238,7 +242,7 @@ def test_unit_documents_return_own_value(oracle_mod):
     q, k, v = rnd(rng, 2, 1, S, 8), rnd(rng, 2, 1, S, 8), rnd(rng, 2, 1, S, 4)
     offs = np.tile(np.arange(S + 1, dtype=np.int32), (2, 1))
     o, _ = oracle_mod.attn(q, k, v, variant="document", doc_offsets=offs)
-    np.testing.assert_allclose(o, v, atol=1e-14)
+    assert_close(o, v, atol=1e-14)
 
 
 def test_mask_algebra(oracle_mod):
@@ -247,12 +251,12 @@ def test_mask_algebra(oracle_mod):
     q, k, v = rnd(rng, 1, 2, S, 8, scale=2), rnd(rng, 1, 2, S, 8), rnd(rng, 1, 2, S, 4)
     A = lambda **kw: oracle_mod.attn(q, k, v, **kw)[0]
     van, cau = A(variant="vanilla"), A(variant="causal")
-    np.testing.assert_allclose(A(variant="sliding_window", window=S, window_causal=False), van, atol=1e-13)
-    np.testing.assert_allclose(A(variant="sliding_window", window=S + 5, window_causal=True), cau, atol=1e-13)
-    np.testing.assert_allclose(A(variant="prefix_lm", prefix=0), cau, atol=1e-13)
-    np.testing.assert_allclose(A(variant="prefix_lm", prefix=1), cau, atol=1e-13)
-    np.testing.assert_allclose(A(variant="prefix_lm", prefix=S), van, atol=1e-13)
-    np.testing.assert_allclose(A(variant="document", doc_offsets=np.array([[0, S]], np.int32)), van,
+    assert_close(A(variant="sliding_window", window=S, window_causal=False), van, atol=1e-13)
+    assert_close(A(variant="sliding_window", window=S + 5, window_causal=True), cau, atol=1e-13)
+    assert_close(A(variant="prefix_lm", prefix=0), cau, atol=1e-13)
+    assert_close(A(variant="prefix_lm", prefix=1), cau, atol=1e-13)
+    assert_close(A(variant="prefix_lm", prefix=S), van, atol=1e-13)
+    assert_close(A(variant="document", doc_offsets=np.array([[0, S]], np.int32)), van,
                                atol=1e-13)
     # a window that is too small must differ from causal
     assert np.abs(A(variant="sliding_window", window=S - 1, window_causal=True) - cau).max() > 1e-6
@@ -293,7 +297,7 @@ def test_alibi_vanishing_slopes_is_vanilla(oracle_mod):
     """A huge max_bias drives every slope 2^(-max_bias*(h+1)/H) to ~0."""
     rng = np.random.default_rng(51)
     q, k, v = rnd(rng, 1, 3, 14, 8), rnd(rng, 1, 3, 14, 8), rnd(rng, 1, 3, 14, 8)
-    np.testing.assert_allclose(oracle_mod.attn(q, k, v, variant="alibi", alibi_max_bias=3000.0)[0],
+    assert_close(oracle_mod.attn(q, k, v, variant="alibi", alibi_max_bias=3000.0)[0],
                                oracle_mod.attn(q, k, v)[0], atol=1e-13)
     # max_bias = 0 gives slope 1 on every head, which is not vanilla
     assert np.abs(oracle_mod.attn(q, k, v, variant="alibi", alibi_max_bias=0.0)[0]
@@ -315,13 +319,13 @@ def test_alibi_on_causal_side_equals_sdpa_bias(oracle_mod):
     # restrict both to the causal half and renormalise
     pn = np.where(j <= i, p, 0.0)
     pn = pn / pn.sum(-1, keepdims=True)
-    np.testing.assert_allclose(pn, pc, atol=1e-12)
+    assert_close(pn, pc, atol=1e-12)
 
 
 def test_softcap_large_cap_is_vanilla(oracle_mod):
     rng = np.random.default_rng(61)
     q, k, v = rnd(rng, 1, 2, 16, 8), rnd(rng, 1, 2, 16, 8), rnd(rng, 1, 2, 16, 8)
-    np.testing.assert_allclose(oracle_mod.attn(q, k, v, variant="softcap", softcap=1e6)[0],
+    assert_close(oracle_mod.attn(q, k, v, variant="softcap", softcap=1e6)[0],
                                oracle_mod.attn(q, k, v)[0], atol=1e-9)
 
 
@@ -351,8 +355,8 @@ def test_gqa_equals_repeated_mha(oracle_mod):
     for variant in ("vanilla", "causal", "alibi"):
         og, lg = oracle_mod.attn(q, k, v, variant=variant)
         om, lm = oracle_mod.attn(q, np.repeat(k, 3, 1), np.repeat(v, 3, 1), variant=variant)
-        np.testing.assert_allclose(og, om, atol=1e-14)
-        np.testing.assert_allclose(lg, lm, atol=1e-14)
+        assert_close(og, om, atol=1e-14)
+        assert_close(lg, lm, atol=1e-14)
 
 
 def test_linear_in_v_and_key_permutation(oracle_mod):
@@ -362,10 +366,10 @@ def test_linear_in_v_and_key_permutation(oracle_mod):
     o1, _ = oracle_mod.attn(q, k, v1)
     o2, _ = oracle_mod.attn(q, k, v2)
     o3, _ = oracle_mod.attn(q, k, 2.0 * v1 - 3.0 * v2)
-    np.testing.assert_allclose(o3, 2.0 * o1 - 3.0 * o2, atol=1e-12)
+    assert_close(o3, 2.0 * o1 - 3.0 * o2, atol=1e-12)
     perm = rng.permutation(13)
     op, _ = oracle_mod.attn(q, k[:, :, perm], v1[:, :, perm])
-    np.testing.assert_allclose(op, o1, atol=1e-13)
+    assert_close(op, o1, atol=1e-13)
 
 
 def test_fully_masked_rows(oracle_mod):
@@ -378,7 +382,7 @@ def test_fully_masked_rows(oracle_mod):
     assert (o[0, 0, 2] == 0).all() and lse[0, 0, 2] == -np.inf
     assert np.isfinite(o).all() and np.isfinite(np.delete(lse[0, 0], 2)).all()
     o1, lse1 = oracle_mod.attn(q, k, v, bias=bias, block_keys=2)
-    np.testing.assert_allclose(o1, o, atol=1e-13)
+    assert_close(o1, o, atol=1e-13)
     assert lse1[0, 0, 2] == -np.inf
 
 
@@ -388,8 +392,8 @@ def test_row_sampling_matches_full(oracle_mod):
     o, lse = oracle_mod.attn(q, k, v, variant="causal")
     rows = np.array([0, 5, 17, 71, 40])
     os_, ls = oracle_mod.attn(q, k, v, variant="causal", rows=rows)
-    np.testing.assert_allclose(os_, o.reshape(-1, 3)[rows], atol=0)
-    np.testing.assert_allclose(ls, lse.reshape(-1)[rows], atol=0)
+    assert_close(os_, o.reshape(-1, 3)[rows], atol=0)
+    assert_close(ls, lse.reshape(-1)[rows], atol=0)
 
 
 def test_rejects_bad_arguments(oracle_mod):
@@ -415,16 +419,16 @@ def test_diffattn_pins(oracle_mod):
         o, l1, l2 = oracle_mod.diffattn(q1, q2, k1, k2, v, lam=0.8, causal=causal, scale=0.125)
         ref = sdpa(q1, k1, v, scale=0.125, is_causal=causal) - 0.8 * sdpa(q2, k2, v, scale=0.125,
                                                                            is_causal=causal)
-        np.testing.assert_allclose(o, ref, atol=1e-12)
+        assert_close(o, ref, atol=1e-12)
         # lambda = 0 is vanilla attention of the first stream
         o0, _, _ = oracle_mod.diffattn(q1, q2, k1, k2, v, lam=0.0, causal=causal, scale=0.125)
-        np.testing.assert_allclose(o0, sdpa(q1, k1, v, scale=0.125, is_causal=causal), atol=1e-12)
+        assert_close(o0, sdpa(q1, k1, v, scale=0.125, is_causal=causal), atol=1e-12)
         # identical streams with lambda = 1 cancel exactly
         oz, _, _ = oracle_mod.diffattn(q1, q1, k1, k1, v, lam=1.0, causal=causal, scale=0.125)
         assert np.abs(oz).max() == 0.0
         # per-stream LSE equals the vanilla oracle's
         _, lv = oracle_mod.attn(q2, k2, v, variant="causal" if causal else "vanilla", scale=0.125)
-        np.testing.assert_allclose(l2, lv, atol=1e-14)
+        assert_close(l2, lv, atol=1e-14)
 
 
 # --------------------------------------------------------------------------
@@ -460,7 +464,7 @@ def test_evoformer_row_equals_sdpa(oracle_mod):
     rng = np.random.default_rng(91)
     q, k, v, g, bias, km = evo_inputs(rng, 3, 10, 2, 4)
     o = oracle_mod.evoformer(q, k, v, g, pair_bias=bias, key_mask=km)
-    np.testing.assert_allclose(o, evo_sdpa_row(q, k, v, g, bias, km), atol=1e-12)
+    assert_close(o, evo_sdpa_row(q, k, v, g, bias, km), atol=1e-12)
 
 
 def test_evoformer_col_equals_row_on_transposed(oracle_mod):
@@ -470,7 +474,7 @@ def test_evoformer_col_equals_row_on_transposed(oracle_mod):
     o = oracle_mod.evoformer(q, k, v, g, key_mask=km, axis="col")
     T = lambda a: a.transpose(1, 0, 2, 3)
     ref = T(evo_sdpa_row(T(q), T(k), T(v), T(g), None, km.T))
-    np.testing.assert_allclose(o, ref, atol=1e-12)
+    assert_close(o, ref, atol=1e-12)
 
 
 def test_evoformer_special_cases(oracle_mod):
@@ -479,22 +483,22 @@ def test_evoformer_special_cases(oracle_mod):
     q, k, v, g, bias, km = evo_inputs(rng, N, L, H, C)
     # no bias, no mask, sigmoid(+40) = 1: plain attention with scale 1/sqrt(C)
     o = oracle_mod.evoformer(q, k, v, np.full_like(g, 40.0))
-    np.testing.assert_allclose(o, evo_sdpa_row(q, k, v, np.full_like(g, 40.0), None, None), atol=1e-12)
+    assert_close(o, evo_sdpa_row(q, k, v, np.full_like(g, 40.0), None, None), atol=1e-12)
     t = lambda a: np.ascontiguousarray(a.transpose(0, 2, 1, 3))
     plain = sdpa(t(q), t(k), t(v)).transpose(0, 2, 1, 3)
-    np.testing.assert_allclose(o, plain * sigmoid(40.0), atol=1e-12)
+    assert_close(o, plain * sigmoid(40.0), atol=1e-12)
     # G = 0 halves the output
     o0 = oracle_mod.evoformer(q, k, v, np.zeros_like(g))
-    np.testing.assert_allclose(o0, plain / 2, atol=1e-12)
+    assert_close(o0, plain / 2, atol=1e-12)
     # a bias constant along the key axis changes nothing
     row_const = np.broadcast_to(rnd(rng, H, L, 1) * 5, (H, L, L)).copy()
     oc = oracle_mod.evoformer(q, k, v, g, pair_bias=row_const)
-    np.testing.assert_allclose(oc, oracle_mod.evoformer(q, k, v, g), atol=1e-12)
+    assert_close(oc, oracle_mod.evoformer(q, k, v, g), atol=1e-12)
     # a single unmasked key returns sigmoid(G) * v_j
     one = np.zeros((N, L), np.uint8)
     one[:, 4] = 1
     o1 = oracle_mod.evoformer(q, k, v, g, pair_bias=bias, key_mask=one)
-    np.testing.assert_allclose(o1, sigmoid(g) * v[:, 4:5, :, :], atol=1e-14)
+    assert_close(o1, sigmoid(g) * v[:, 4:5, :, :], atol=1e-14)
     # every key masked: the row is 0
     none = np.zeros((N, L), np.uint8)
     assert np.abs(oracle_mod.evoformer(q, k, v, g, pair_bias=bias, key_mask=none)).max() == 0.0
@@ -527,8 +531,8 @@ def test_composed_matches_bruteforce(oracle_mod, mod, mask, S):
     kw = compose_kw(mod, mask, S, rng, B)
     o, lse = oracle_mod.attn(q, k, v, **kw)
     o_bf, lse_bf = bf.attention(q, k, v, **kw)
-    np.testing.assert_allclose(o, o_bf, rtol=0, atol=1e-12)
-    np.testing.assert_allclose(lse, lse_bf, rtol=1e-12, atol=1e-12)
+    assert_close(o, o_bf, rtol=0, atol=1e-12)
+    assert_close(lse, lse_bf, rtol=1e-12, atol=1e-12)
 
 
 @pytest.mark.parametrize("mask", MASKS)
@@ -543,7 +547,7 @@ def test_composed_special_cases(oracle_mod, mask):
     same = oracle_mod.attn(q, k, v, variant="vanilla", mask=mask, **kw)
     np.testing.assert_array_equal(plain[0], same[0])
     big = oracle_mod.attn(q, k, v, variant="softcap", softcap=1e7, mask=mask, **kw)
-    np.testing.assert_allclose(big[0], plain[0], atol=1e-9)
+    assert_close(big[0], plain[0], atol=1e-9)
 
 
 def test_alibi_under_causal_equals_sdpa_bias(oracle_mod):
@@ -556,7 +560,7 @@ def test_alibi_under_causal_equals_sdpa_bias(oracle_mod):
     i, j = np.arange(S)[:, None], np.arange(S)[None, :]
     slopes = 2.0 ** (-8.0 * (np.arange(H) + 1) / H)
     bias = np.where(j <= i, slopes[:, None, None] * (j - i), -np.inf)
-    np.testing.assert_allclose(o, sdpa(q, k, v, attn_mask=torch.from_numpy(bias)[None]), atol=1e-12)
+    assert_close(o, sdpa(q, k, v, attn_mask=torch.from_numpy(bias)[None]), atol=1e-12)
 
 
 def test_alibi_causal_uniform_scores_closed_form(oracle_mod):
@@ -571,7 +575,7 @@ def test_alibi_causal_uniform_scores_closed_form(oracle_mod):
         r = math.exp(-(2.0 ** (-3.0 * (h + 1) / H)))
         for i in (0, 1, 7, S - 1):
             w = r ** (i - np.arange(i + 1))
-            np.testing.assert_allclose(o[0, h, i], w @ v[0, h, : i + 1] / w.sum(), atol=1e-12)
+            assert_close(o[0, h, i], w @ v[0, h, : i + 1] / w.sum(), atol=1e-12)
             assert abs(lse[0, h, i] - math.log(w.sum())) < 1e-12
 
 
