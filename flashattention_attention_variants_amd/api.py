@@ -23,8 +23,10 @@ FL_BF16, FL_F32 = 0, 1
 VARIANTS = {"vanilla": 0, "alibi": 1, "softcap": 2, "causal": 3, "sliding_window": 4,
             "prefix_lm": 5, "document": 6}
 EVO_AXES = {"row": 0, "col": 1}
-SYMBOLS = ("fl_attn_fwd", "fl_diffattn_fwd", "fl_evoformer_gated_attn_fwd", "fl_status_str",
-           "fl_abi_version")
+KV_LAYOUTS = {"bhsd": 0, "bshd": 1}
+SYMBOLS = ("fl_attn_fwd", "fl_diffattn_fwd", "fl_evoformer_gated_attn_fwd", "fl_attn_decode_fwd",
+           "fl_attn_decode_workspace_size", "fl_attn_decode_num_splits", "fl_attn_merge",
+           "fl_status_str", "fl_abi_version")
 
 
 class FlError(RuntimeError):
@@ -65,11 +67,19 @@ def load_library(path: str | None = None):
         raise RuntimeError("libflattn.so is not built (%s); run "
                            "`python -m flashattention_attention_variants_amd.build`" % p)
     lib = ctypes.CDLL(p)
-    V, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    V, I, F, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64, ctypes.c_size_t
     lib.fl_attn_fwd.argtypes = [V, V, V, V, V, V, I, I, I, I, I, I, I, ctypes.POINTER(AttnParams), V]
     lib.fl_diffattn_fwd.argtypes = [V, V, V, V, V, V, V, V, I, I, I, I, I, I, I, F, F, I, V]
     lib.fl_evoformer_gated_attn_fwd.argtypes = [V, V, V, V, V, V, V, I, I, I, I, I, I, F, V]
-    for f in (lib.fl_attn_fwd, lib.fl_diffattn_fwd, lib.fl_evoformer_gated_attn_fwd):
+    lib.fl_attn_decode_fwd.argtypes = [V, V, V, V, V, V, V, SZ, I, I, I, I, I, I, I, I, I,
+                                       ctypes.POINTER(AttnParams), I, V]
+    lib.fl_attn_decode_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    lib.fl_attn_decode_workspace_size.restype = I64
+    lib.fl_attn_decode_num_splits.argtypes = [I, I, I, I, I, I]
+    lib.fl_attn_decode_num_splits.restype = I
+    lib.fl_attn_merge.argtypes = [V, V, V, V, I, I64, I, I, V]
+    for f in (lib.fl_attn_fwd, lib.fl_diffattn_fwd, lib.fl_evoformer_gated_attn_fwd,
+              lib.fl_attn_decode_fwd, lib.fl_attn_merge):
         f.restype = ctypes.c_int
     lib.fl_status_str.argtypes = [I]
     lib.fl_status_str.restype = ctypes.c_char_p
@@ -136,19 +146,107 @@ def fl_attn_fwd(q, k, v, *, variant="vanilla", scale=None, bias=None, softcap=50
     if lse is None and return_lse:
         lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=q.device)
     _dev(lse, "lse", torch.float32)
-    var = VARIANTS[variant] if isinstance(variant, str) else int(variant)
-    msk = 0 if mask is None else (VARIANTS[mask] if isinstance(mask, str) else int(mask))
     docs = None
-    if VARIANTS["document"] in (var, msk):
+    if VARIANTS["document"] in (VARIANTS.get(variant, variant), VARIANTS.get(mask, mask)):
         docs = _dev(doc_offsets, "doc_offsets", torch.int32)
-    p = AttnParams(var, float(scale if scale is not None else 1.0 / math.sqrt(D)), float(softcap),
-                   float(alibi_max_bias), int(window), int(bool(window_causal)), int(prefix),
-                   0 if docs is None else docs.shape[-1] - 1,
-                   None if docs is None else docs.data_ptr(), msk)
+    p = _params(variant, mask, scale, D, softcap, alibi_max_bias, window, window_causal, prefix,
+                docs)
     st = load_library().fl_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(out), _ptr(lse),
                                     B, Hq, Hkv, Sq, Sk, D, _dtype_code(q), ctypes.byref(p),
                                     _stream(stream))
     _check("fl_attn_fwd", st)
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def _params(variant, mask, scale, D, softcap, alibi_max_bias, window, window_causal, prefix,
+            docs=None):
+    var = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    msk = 0 if mask is None else (VARIANTS[mask] if isinstance(mask, str) else int(mask))
+    return AttnParams(var, float(scale if scale is not None else 1.0 / math.sqrt(D)), float(softcap),
+                      float(alibi_max_bias), int(window), int(bool(window_causal)), int(prefix),
+                      0 if docs is None else docs.shape[-1] - 1,
+                      None if docs is None else docs.data_ptr(), msk)
+
+
+def fl_attn_decode_workspace_size(B, Hq, Hkv, Sq, max_seqlen, D=64, num_splits=0):
+    """Bytes of device workspace :func:`fl_attn_decode_fwd` needs (0: none)."""
+    n = load_library().fl_attn_decode_workspace_size(B, Hq, Hkv, Sq, max_seqlen, D, num_splits)
+    if n < 0:
+        raise ValueError("invalid decode sizes")
+    return int(n)
+
+
+def fl_attn_decode_num_splits(B, Hq, Hkv, Sq, max_seqlen, num_splits=0):
+    """Key ranges per (sequence, K/V head) the decode call uses."""
+    n = load_library().fl_attn_decode_num_splits(B, Hq, Hkv, Sq, max_seqlen, num_splits)
+    if n < 0:
+        raise ValueError("invalid decode sizes")
+    return int(n)
+
+
+def fl_attn_decode_fwd(q, k_cache, v_cache, cache_seqlens, *, max_seqlen=None, layout="bhsd",
+                       variant="vanilla", mask=None, scale=None, softcap=50.0, alibi_max_bias=8.0,
+                       window=256, window_causal=True, prefix=512, num_splits=0, workspace=None,
+                       out=None, lse=None, return_lse=False, stream=None):
+    """Decode attention of q [B,Hq,Sq,D] (the Sq newest tokens) against a KV
+    cache ([B,Hkv,S_cap,D] for layout "bhsd", [B,S_cap,Hkv,D] for "bshd")
+    holding cache_seqlens[b] (int32, on the GPU) tokens per sequence.
+
+    ``max_seqlen`` bounds the lengths (default: the cache capacity).  A
+    workspace of :func:`fl_attn_decode_workspace_size` bytes (a uint8 GPU
+    tensor) is allocated here when not given.
+    """
+    q = _dev(q, "q")
+    dt = q.dtype
+    k_cache, v_cache = _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt)
+    seqlens = _dev(cache_seqlens, "cache_seqlens", torch.int32)
+    B, Hq, Sq, D = q.shape
+    lay = KV_LAYOUTS[layout]
+    if lay == 0:
+        _, Hkv, S_cap, _ = k_cache.shape
+    else:
+        _, S_cap, Hkv, _ = k_cache.shape
+    if max_seqlen is None:
+        max_seqlen = S_cap
+    if out is None:
+        out = torch.empty(B, Hq, Sq, D, dtype=dt, device=q.device)
+    _dev(out, "out", dt)
+    if lse is None and return_lse:
+        lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=q.device)
+    _dev(lse, "lse", torch.float32)
+    need = load_library().fl_attn_decode_workspace_size(B, Hq, Hkv, Sq, int(max_seqlen), D,
+                                                        int(num_splits))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", torch.uint8)
+    p = _params(variant, mask, scale, D, softcap, alibi_max_bias, window, window_causal, prefix)
+    st = load_library().fl_attn_decode_fwd(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(out), _ptr(lse), _ptr(workspace),
+        0 if workspace is None else workspace.numel(), B, Hq, Hkv, Sq, S_cap, int(max_seqlen), D,
+        lay, _dtype_code(q), ctypes.byref(p), int(num_splits), _stream(stream))
+    _check("fl_attn_decode_fwd", st)
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def fl_attn_merge(o_parts, lse_parts, *, out_dtype=torch.bfloat16, out=None, lse=None,
+                  return_lse=False, stream=None):
+    """Merge partial results o_parts [P, ..., D] (float32, each normalised over
+    its keys) with lse_parts [P, ...] (float32, natural log) into o [..., D]."""
+    o_parts = _dev(o_parts, "o_parts", torch.float32)
+    lse_parts = _dev(lse_parts, "lse_parts", torch.float32)
+    if tuple(o_parts.shape[:-1]) != tuple(lse_parts.shape) or o_parts.dim() < 2:
+        raise ValueError("o_parts must be lse_parts' shape plus a head dimension")
+    P, D = o_parts.shape[0], o_parts.shape[-1]
+    rows = lse_parts[0].numel()
+    if out is None:
+        out = torch.empty(tuple(o_parts.shape[1:]), dtype=out_dtype, device=o_parts.device)
+    _dev(out, "out", out_dtype)
+    if lse is None and return_lse:
+        lse = torch.empty(tuple(lse_parts.shape[1:]), dtype=torch.float32, device=o_parts.device)
+    _dev(lse, "lse", torch.float32)
+    st = load_library().fl_attn_merge(_ptr(o_parts), _ptr(lse_parts), _ptr(out), _ptr(lse), P, rows,
+                                      D, _dtype_code(out), _stream(stream))
+    _check("fl_attn_merge", st)
     return (out, lse) if (return_lse or lse is not None) else out
 
 

@@ -37,7 +37,8 @@
 
 namespace fl {
 
-template <int DQK_, int DV_, int NS_, int QB_, int MOD_, bool BIAS_, bool KMASK_, bool GATE_>
+template <int DQK_, int DV_, int NS_, int QB_, int MOD_, bool BIAS_, bool KMASK_, bool GATE_,
+          bool DEC_ = false>
 struct MfmaCfg {
   static constexpr int DQK = DQK_;   // q/k head dim (multiple of 16)
   static constexpr int DV = DV_;     // v head dim (multiple of 32)
@@ -47,6 +48,9 @@ struct MfmaCfg {
   static constexpr bool BIAS = BIAS_;
   static constexpr bool KMASK = KMASK_;
   static constexpr bool GATE = GATE_;
+  // decode against a KV cache: packed GQA rows, per-sequence lengths, key
+  // splits (see KernelArgs)
+  static constexpr bool DEC = DEC_;
   static constexpr int NW = 4;               // waves per work-group
   static constexpr int BM = NW * 32 * QB;    // query rows per work-group
   static constexpr int BN = 64;              // keys per tile
@@ -71,6 +75,7 @@ struct MfmaCfg {
   // bounded softcap: fixed reference 0
   static constexpr bool SCAPB = MOD == MOD_SOFTCAP_BOUNDED;
   static_assert(!SCAPB || (!BIAS && !KMASK), "bounded softcap takes no bias or key mask");
+  static_assert(!DEC || (QB == 1 && NS == 1 && !BIAS && !KMASK && !GATE), "decode form");
   // one stream fits 2 waves per SIMD; two streams need the whole register file
 #ifndef FL_QB1_WAVES
 #define FL_QB1_WAVES 2
@@ -189,32 +194,85 @@ void attn_mfma_kernel(KernelArgs a) {
   const int lane = tid & 63, w = tid >> 6;
   const int c = lane & 31, g = lane >> 5;
 
-  int bh, qt;
-  decode_tile(a, blockIdx.x, bh, qt);
+  int bh, qt, split = 0;
+  if constexpr (C::DEC) {
+    split = blockIdx.x % a.n_split;
+    const int rest = blockIdx.x / a.n_split;
+    qt = rest % a.n_qt;
+    bh = rest / a.n_qt;
+  } else {
+    decode_tile(a, blockIdx.x, bh, qt);
+  }
   const int b = bh / a.nh, h = bh % a.nh, hk = h / a.group;
   const int q0 = qt * C::BM;
   const int qlast = min(q0 + C::BM, a.sq) - 1;
 
+  // ---- positions of the rows ---------------------------------------------------
+  // A row's position is its index, except in decode, where the packed row r
+  // is new token r % S_new of its head at position len - S_new + r % S_new.
+  int len = a.sk;
+  if constexpr (C::DEC) len = min(max(a.seqlens[b], 0), a.max_len);
+  auto pos_of = [&](int r) { return C::DEC ? len - a.sq_new + r % a.sq_new : r; };
+  // smallest and largest position among rows r0..r1 (r0 <= r1)
+  auto pos_range = [&](int r0, int r1, int& pmin, int& pmax) {
+    if constexpr (C::DEC) {
+      const int n = a.sq_new, i0 = r0 % n, i1 = r1 % n;
+      const bool all = r1 - r0 + 1 >= n || i0 > i1;
+      pmin = len - n + (all ? 0 : i0);
+      pmax = len - n + (all ? n - 1 : i1);
+    } else {
+      pmin = r0;
+      pmax = r1;
+    }
+  };
+  // key interval of the query at position x (only the first len keys exist)
+  auto interval = [&](int x, int& lo, int& hi) {
+    key_interval(a, b, x, lo, hi);
+    if constexpr (C::DEC) hi = min(hi, len - 1);
+  };
+
   // ---- key-tile range of the work-group (union over its rows) -------------
-  int lo_first, hi_first, lo_last, hi_last;
-  key_interval(a, b, q0, lo_first, hi_first);
-  key_interval(a, b, qlast, lo_last, hi_last);
-  const int kt_lo = lo_first / BN;
-  const int kt_hi = hi_last >= lo_first ? (hi_last + BN) / BN : kt_lo;
+  // Every interval kind has both ends non-decreasing in the position, so the
+  // union over a set of rows runs from the smallest position's start to the
+  // largest position's end.
+  int p_first, p_last, lo_first, hi_first, lo_last, hi_last;
+  pos_range(q0, qlast, p_first, p_last);
+  interval(p_first, lo_first, hi_first);
+  interval(p_last, lo_last, hi_last);
+  int kt_lo = lo_first / BN;
+  int kt_hi = hi_last >= lo_first ? (hi_last + BN) / BN : kt_lo;
+  if constexpr (C::DEC) {
+    // this work-group's share of the keys
+    kt_lo = max(kt_lo, split * a.split_tiles);
+    kt_hi = max(min(kt_hi, (split + 1) * a.split_tiles), kt_lo);
+  }
 
   // ---- this wave's rows and their key intervals ----------------------------
   const int wq0 = q0 + w * 32 * QB;
   const int wq1 = min(wq0 + 32 * QB, a.sq) - 1;  // last valid row of the wave
-  int w_lo_min, w_hi_min, w_lo_max, w_hi_max;
-  key_interval(a, b, min(wq0, a.sq - 1), w_lo_min, w_hi_min);
-  key_interval(a, b, max(wq1, 0), w_lo_max, w_hi_max);
+  int wp_min, wp_max, w_lo_min, w_hi_min, w_lo_max, w_hi_max;
+  pos_range(min(wq0, a.sq - 1), max(wq1, min(wq0, a.sq - 1)), wp_min, wp_max);
+  interval(wp_min, w_lo_min, w_hi_min);
+  interval(wp_max, w_lo_max, w_hi_max);
   const bool wave_idle = wq0 >= a.sq;
 
   int row_lo[QB], row_hi[QB];
+  // positions of this lane's row and of the first and last row of each
+  // 32-row block (the block's place against the diagonal)
+  int lane_pos[QB], blk_pmin[QB], blk_pmax[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qi = min(wq0 + 32 * qb + c, a.sq - 1);  // rows past S_q copy the last row
-    key_interval(a, b, qi, row_lo[qb], row_hi[qb]);
+    interval(pos_of(qi), row_lo[qb], row_hi[qb]);
+    if constexpr (C::DEC) {
+      lane_pos[qb] = pos_of(qi);
+      const int r0 = min(wq0 + 32 * qb, a.sq - 1);
+      pos_range(r0, max(min(wq0 + 32 * qb + 31, a.sq - 1), r0), blk_pmin[qb], blk_pmax[qb]);
+    } else {
+      lane_pos[qb] = wq0 + 32 * qb + c;
+      blk_pmin[qb] = wq0 + 32 * qb;
+      blk_pmax[qb] = wq0 + 32 * qb + 31;
+    }
   }
 
   // ---- Q operands in registers ---------------------------------------------
@@ -271,7 +329,9 @@ void attn_mfma_kernel(KernelArgs a) {
     mid = (bf16)(x - (float)hi);
     lo = (bf16)(x - (float)hi - (float)mid);
   };
-  const float alibi_l2 = C::MOD == MOD_ALIBI ? alibi_slope_log2(a, h) : 0.0f;
+  // decode rows of one K/V head belong to G query heads with their own slopes
+  const int h_alibi = C::DEC ? hk * a.grp + min(wq0 + c, a.sq - 1) / a.sq_new : h;
+  const float alibi_l2 = C::MOD == MOD_ALIBI ? alibi_slope_log2(a, h_alibi) : 0.0f;
   bf16 sl0, sl1, sl2;
   split3(alibi_l2, sl0, sl1, sl2);
   // query-side operand for reference m (bf16-exact) and, under ALiBi, the
@@ -280,7 +340,7 @@ void attn_mfma_kernel(KernelArgs a) {
     const bf16 mt = (bf16)(-m);
     if constexpr (C::ALIBI_FOLD) {
       bf16 x0, x1, x2;
-      split3(-alibi_l2 * (float)(wq0 + 32 * qb + c - j0), x0, x1, x2);
+      split3(-alibi_l2 * (float)(lane_pos[qb] - j0), x0, x1, x2);
       qext[s][qb] = bf16x8{mt, x0, x1, x2, sl0, sl1, sl2, zero};
     } else {
       qext[s][qb] = bf16x8{mt, zero, zero, zero, zero, zero, zero, zero};
@@ -337,8 +397,10 @@ void attn_mfma_kernel(KernelArgs a) {
     kblk[s] = (const char*)((const bf16*)a.k[s] + b * a.k_sb + hk * a.k_sh);
   const char* vblk = (const char*)((const bf16*)a.v + b * a.v_sb + hk * a.v_sh);
   const int64_t k_row_b = a.k_si * 2, v_row_b = a.v_si * 2;
-  const int64_t k_span = a.sk > 0 ? (int64_t)(a.sk - 1) * k_row_b + DQK * 2 : 0;
-  const int64_t v_span = a.sk > 0 ? (int64_t)(a.sk - 1) * v_row_b + DV * 2 : 0;
+  // (decode: only the first len rows exist; cache slots past them may hold
+  // anything, NaN included, and must not reach even a zero-weighted product)
+  const int64_t k_span = len > 0 ? (int64_t)(len - 1) * k_row_b + DQK * 2 : 0;
+  const int64_t v_span = len > 0 ? (int64_t)(len - 1) * v_row_b + DV * 2 : 0;
 
   int k_off[C::KCH], v_off[C::VCH];
 #pragma unroll
@@ -411,9 +473,9 @@ void attn_mfma_kernel(KernelArgs a) {
   };
   // position of a (key half, query block) unit against the diagonal
   // (wave-uniform): keys wholly above the rows' diagonal, or straddling it
-  auto above = [&](int j0, int kb, int qb) { return j0 + 32 * kb >= wq0 + 32 * qb + 31; };
+  auto above = [&](int j0, int kb, int qb) { return j0 + 32 * kb >= blk_pmax[qb]; };
   auto straddles = [&](int j0, int kb, int qb) {
-    return !above(j0, kb, qb) && j0 + 32 * kb + 31 > wq0 + 32 * qb;
+    return !above(j0, kb, qb) && j0 + 32 * kb + 31 > blk_pmin[qb];
   };
   // the folded k-step: -m, and the ALiBi penalty with the unit's sign
   auto fold = [&](int j0, int s, int kb, int qb, f32x16& acc) {
@@ -425,7 +487,7 @@ void attn_mfma_kernel(KernelArgs a) {
   auto alibi_fix = [&](int j0, f32x16& acc, int kb, int qb) {
     if constexpr (C::ALIBI_FOLD) {
       if (straddles(j0, kb, qb)) {
-        const int qi = wq0 + 32 * qb + c;
+        const int qi = lane_pos[qb];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int dj = j0 + 32 * kb + 4 * g + acc_row(r) - qi;
@@ -630,7 +692,7 @@ void attn_mfma_kernel(KernelArgs a) {
         for (int r = 0; r < 16; ++r) {
           float x = sc[r];
           if constexpr (C::MOD == MOD_ALIBI) {
-            const float dist = (float)(qi - jb - acc_row(r));
+            const float dist = (float)(lane_pos[qb] - jb - acc_row(r));
             x = x * a.scale_log2 - alibi_l2 * __builtin_fabsf(dist);
           } else if constexpr (C::MOD == MOD_SOFTCAP) {
             x = softcap_log2(a, x);
@@ -702,7 +764,7 @@ void attn_mfma_kernel(KernelArgs a) {
   // instead of climbing (and being moved) tile after tile.
   const int n_kt = kt_hi - kt_lo;
   int kt_start = 0;
-  if constexpr (C::MOD == MOD_ALIBI) kt_start = min(max(q0 / BN - kt_lo, 0), max(n_kt - 1, 0));
+  if constexpr (C::MOD == MOD_ALIBI) kt_start = min(max(p_first / BN - kt_lo, 0), max(n_kt - 1, 0));
   auto tile_of = [&](int it) {
     const int x = it + kt_start;
     return kt_lo + (x >= n_kt ? x - n_kt : x);
@@ -742,6 +804,31 @@ void attn_mfma_kernel(KernelArgs a) {
   }
 
   // ---- epilogue: normalise, combine, gate, store --------------------------------
+  if constexpr (C::DEC) {
+    if (a.n_split > 1) {
+      // one key range of a split decode: normalised float32 output and
+      // natural-log LSE of this range (0 and -inf when it held no key)
+      const float l = l_run[0][0] + __shfl_xor(l_run[0][0], 32);
+      const float iv = l > 0.0f ? 1.0f / l : 0.0f;
+      const int qi = wq0 + c;
+      if (qi < a.sq) {
+        const int64_t prow = ((int64_t)(split * a.nb + b) * a.nh + h) * a.sq + qi;
+        if (g == 0)
+          a.lse_part[prow] = l > 0.0f ? (m_run[0][0] + __builtin_log2f(l)) * kLn2 : kNegInf;
+        float* op = a.o_part + prow * DV;
+#pragma unroll
+        for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int d = 32 * db + 8 * r4 + 4 * g;
+            const f32x4 ov = {oacc[0][0][db][4 * r4] * iv, oacc[0][0][db][4 * r4 + 1] * iv,
+                              oacc[0][0][db][4 * r4 + 2] * iv, oacc[0][0][db][4 * r4 + 3] * iv};
+            *(f32x4*)(op + d) = ov;
+          }
+      }
+      return;
+    }
+  }
   float inv[NS][QB];
 #pragma unroll
   for (int s = 0; s < NS; ++s)

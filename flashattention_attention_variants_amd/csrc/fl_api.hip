@@ -39,6 +39,44 @@ bool span_ok(int64_t rows, int64_t row_stride, int64_t width) {
   return rows <= 0 || ((rows - 1) * row_stride + width) * 2 < ((int64_t)1 << 31);
 }
 
+// Decode: key ranges per (sequence, K/V head).  Enough work-groups to give
+// every compute unit several (256 units), but no range shorter than eight
+// 64-key tiles, whose partial results would cost more to merge than they
+// save.  A request is capped at the number of tiles.
+constexpr int kDecodeTargetWgs = 2048;
+constexpr int kDecodeMinTiles = 8;
+constexpr int kDecodeMaxSplits = 256;
+
+bool decode_sizes_ok(int B, int H_q, int H_kv, int S_q, int max_seqlen) {
+  return B >= 0 && H_q >= 1 && H_kv >= 1 && H_q % H_kv == 0 && S_q >= 0 && max_seqlen >= 0 &&
+         S_q <= kMaxSeq && max_seqlen <= kMaxSeq && (int64_t)(H_q / H_kv) * S_q <= kMaxSeq;
+}
+
+void decode_split(int B, int H_q, int H_kv, int S_q, int max_seqlen, int requested, int& n_split,
+                  int& split_tiles) {
+  const int n_tiles = max_seqlen > 0 ? (max_seqlen + 63) / 64 : 1;
+  const int64_t n_qt = grid_qtiles((H_q / H_kv) * S_q, mfma_rows_per_wg(1));
+  int s;
+  if (requested > 0) {
+    s = requested < n_tiles ? requested : n_tiles;
+  } else {
+    const int64_t base = (int64_t)B * H_kv * n_qt > 0 ? (int64_t)B * H_kv * n_qt : 1;
+    const int64_t want = (kDecodeTargetWgs + base - 1) / base;
+    const int64_t cap = n_tiles / kDecodeMinTiles > 1 ? n_tiles / kDecodeMinTiles : 1;
+    s = (int)(want < cap ? want : cap);
+    s = s < 1 ? 1 : (s > kDecodeMaxSplits ? kDecodeMaxSplits : s);
+  }
+  split_tiles = (n_tiles + s - 1) / s;
+  n_split = (n_tiles + split_tiles - 1) / split_tiles;
+}
+
+int64_t decode_workspace(int B, int H_q, int S_q, int D, int n_split) {
+  if (n_split <= 1) return 0;
+  const int64_t rows = (int64_t)B * H_q * S_q;
+  const int64_t o_bytes = (int64_t)n_split * rows * D * 4;
+  return o_bytes + ((int64_t)n_split * rows * 4 + 15) / 16 * 16;
+}
+
 }  // namespace
 
 extern "C" {
@@ -111,6 +149,7 @@ fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* b
   a.bias_sh = (int64_t)S_q * S_k;
   a.nb = B;
   a.nh = H_q;
+  a.alibi_nh = H_q;
   a.group = H_q / H_kv;
   a.sq = S_q;
   a.sk = S_k;
@@ -307,6 +346,151 @@ fl_status fl_evoformer_gated_attn_fwd(const void* q, const void* k, const void* 
   a.n_qt = grid_qtiles(L, mfma_rows_per_wg(qb));
   if ((int64_t)a.n_qt * a.nb * H > kMaxGrid) return FL_ERR_SHAPE;
   return launch_status(launch_evo_bf16(a, C, qb, pair_bias != nullptr, st));
+}
+
+int fl_attn_decode_num_splits(int B, int H_q, int H_kv, int S_q, int max_seqlen, int num_splits) {
+  if (!decode_sizes_ok(B, H_q, H_kv, S_q, max_seqlen) || num_splits < 0) return -1;
+  int n_split, split_tiles;
+  decode_split(B, H_q, H_kv, S_q, max_seqlen, num_splits, n_split, split_tiles);
+  return n_split;
+}
+
+int64_t fl_attn_decode_workspace_size(int B, int H_q, int H_kv, int S_q, int max_seqlen, int D,
+                                      int num_splits) {
+  if (!decode_sizes_ok(B, H_q, H_kv, S_q, max_seqlen) || D < 1 || num_splits < 0) return -1;
+  int n_split, split_tiles;
+  decode_split(B, H_q, H_kv, S_q, max_seqlen, num_splits, n_split, split_tiles);
+  return decode_workspace(B, H_q, S_q, D, n_split);
+}
+
+fl_status fl_attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* cache_seqlens, void* o, float* lse, void* workspace,
+                             size_t workspace_bytes, int B, int H_q, int H_kv, int S_q, int S_cap,
+                             int max_seqlen, int D, fl_kv_layout layout, fl_dtype dtype,
+                             const fl_attn_params* p, int num_splits, void* stream) {
+  if (!p) return FL_ERR_NULL;
+  if (!decode_sizes_ok(B, H_q, H_kv, S_q, max_seqlen) || S_cap < 0 || S_cap > kMaxSeq || D < 1)
+    return FL_ERR_SHAPE;
+  if (layout != FL_KV_BHSD && layout != FL_KV_BSHD) return FL_ERR_PARAM;
+  if (dtype != FL_BF16 || D != 64) return FL_ERR_UNSUPPORTED;
+  if (p->variant < FL_VANILLA || p->variant > FL_DOCUMENT) return FL_ERR_PARAM;
+  if (!isfinite(p->scale) || num_splits < 0) return FL_ERR_PARAM;
+  if (max_seqlen > S_cap) return FL_ERR_PARAM;
+  const bool variant_is_mask = p->variant >= FL_CAUSAL;
+  if (p->mask != FL_VANILLA && (variant_is_mask || p->mask < FL_CAUSAL || p->mask > FL_DOCUMENT))
+    return FL_ERR_PARAM;
+  const int mask = variant_is_mask ? p->variant : p->mask;
+  if (mask == FL_DOCUMENT) return FL_ERR_UNSUPPORTED;
+  if (p->variant == FL_SOFTCAP && !(p->softcap > 0.0f && isfinite(p->softcap))) return FL_ERR_PARAM;
+  if (p->variant == FL_ALIBI && !(p->alibi_max_bias >= 0.0f && isfinite(p->alibi_max_bias)))
+    return FL_ERR_PARAM;
+  if (mask == FL_SLIDING_WINDOW && p->window < 1) return FL_ERR_PARAM;
+  if (mask == FL_PREFIX_LM && p->prefix < 0) return FL_ERR_PARAM;
+  if ((int64_t)B * H_q * S_q == 0) return FL_OK;  // no output element
+  if (!q || !o || !cache_seqlens || (S_cap > 0 && (!k_cache || !v_cache))) return FL_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(cache_seqlens, 4) || !aligned(workspace, 16))
+    return FL_ERR_ALIGN;
+
+  const int G = H_q / H_kv;
+  int n_split, split_tiles;
+  decode_split(B, H_q, H_kv, S_q, max_seqlen, num_splits, n_split, split_tiles);
+  const int64_t ws = decode_workspace(B, H_q, S_q, D, n_split);
+  if (ws > 0 && !workspace) return FL_ERR_NULL;
+  if ((int64_t)workspace_bytes < ws) return FL_ERR_PARAM;
+
+  KernelArgs a;
+  init_args(a);
+  a.q[0] = q;
+  a.k[0] = k_cache;
+  a.v = v_cache;
+  a.o = o;
+  a.lse[0] = lse;
+  // the G query heads of a K/V head are one packed head of G * S_q rows
+  a.q_si = D;
+  a.q_sh = (int64_t)G * S_q * D;
+  a.q_sb = (int64_t)H_q * S_q * D;
+  a.o_si = a.q_si;
+  a.o_sh = a.q_sh;
+  a.o_sb = a.q_sb;
+  a.lse_sh = (int64_t)G * S_q;
+  a.lse_sb = (int64_t)H_q * S_q;
+  if (layout == FL_KV_BHSD) {
+    bhsd(H_kv, S_cap, D, a.k_sb, a.k_sh, a.k_si);
+  } else {
+    a.k_si = (int64_t)H_kv * D;
+    a.k_sh = D;
+    a.k_sb = (int64_t)S_cap * H_kv * D;
+  }
+  a.v_sb = a.k_sb;
+  a.v_sh = a.k_sh;
+  a.v_si = a.k_si;
+  if (!span_ok(S_cap, a.k_si, D)) return FL_ERR_SHAPE;
+  a.nb = B;
+  a.nh = H_kv;
+  a.alibi_nh = H_q;
+  a.group = 1;
+  a.grp = G;
+  a.sq = G * S_q;
+  a.sq_new = S_q;
+  a.sk = S_cap;
+  a.max_len = max_seqlen;
+  a.seqlens = cache_seqlens;
+  a.scale_log2 = p->scale * kLog2e;
+  int mod = MOD_NONE;
+  if (p->variant == FL_ALIBI) {
+    mod = MOD_ALIBI;
+    a.alibi_max_bias = p->alibi_max_bias;
+  } else if (p->variant == FL_SOFTCAP) {
+    mod = p->softcap * kLog2e <= 100.0f ? MOD_SOFTCAP_BOUNDED : MOD_SOFTCAP;
+    a.softcap_arg = 2.0f * p->scale * kLog2e / p->softcap;
+    a.softcap_log2 = p->softcap * kLog2e;
+  }
+  // wider windows and prefixes than every distance present change nothing
+  const int far = (max_seqlen > S_q ? max_seqlen : S_q) + 1;
+  switch (mask) {
+    case FL_CAUSAL:
+      a.iv_kind = IV_CAUSAL;
+      break;
+    case FL_SLIDING_WINDOW:
+      a.iv_kind = p->window_causal ? IV_WINDOW_CAUSAL : IV_WINDOW_TWO_SIDED;
+      a.window = p->window > far ? far : p->window;
+      break;
+    case FL_PREFIX_LM:
+      a.iv_kind = IV_PREFIX;
+      a.prefix = p->prefix > max_seqlen ? max_seqlen : p->prefix;
+      break;
+    default:
+      break;
+  }
+  a.n_qt = grid_qtiles(G * S_q, mfma_rows_per_wg(1));
+  a.n_split = n_split;
+  a.split_tiles = split_tiles;
+  if ((int64_t)a.n_qt * B * H_kv * n_split > kMaxGrid) return FL_ERR_SHAPE;
+  const int64_t rows = (int64_t)B * H_q * S_q;
+  if (n_split > 1) {
+    a.o_part = (float*)workspace;
+    a.lse_part = (float*)((char*)workspace + (int64_t)n_split * rows * D * 4);
+    if ((rows + 3) / 4 > kMaxGrid) return FL_ERR_SHAPE;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const fl_status rc = launch_status(launch_decode_bf16(a, mod, st));
+  if (rc != FL_OK || n_split == 1) return rc;
+  return launch_status(launch_merge(a.o_part, a.lse_part, n_split, rows, D, o, true, lse, st));
+}
+
+fl_status fl_attn_merge(const float* o_parts, const float* lse_parts, void* o, float* lse,
+                        int n_parts, int64_t n_rows, int D, fl_dtype out_dtype, void* stream) {
+  if (n_parts < 1 || n_rows < 0 || D < 1) return FL_ERR_SHAPE;
+  if (out_dtype != FL_BF16 && out_dtype != FL_F32) return FL_ERR_UNSUPPORTED;
+  if (n_rows == 0) return FL_OK;
+  if ((n_rows + 3) / 4 > kMaxGrid) return FL_ERR_SHAPE;
+  if (!o_parts || !lse_parts || !o) return FL_ERR_NULL;
+  if (!aligned(o_parts, 4) || !aligned(lse_parts, 4) || !aligned(lse, 4) ||
+      !aligned(o, out_dtype == FL_BF16 ? 2 : 4))
+    return FL_ERR_ALIGN;
+  return launch_status(launch_merge(o_parts, lse_parts, n_parts, n_rows, D, o,
+                                    out_dtype == FL_BF16, lse, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -68,6 +68,21 @@ struct KernelArgs {
   float lambda;
   int heavy_first;             // schedule the most expensive query tiles first
   int head_major;              // deal a head's query tiles to its XCD consecutively
+  int alibi_nh;                // query heads in the ALiBi slope formula
+  // Decode against a KV cache.  The rows of K/V head hk are the G*S_new
+  // query rows of its G query heads, packed: row r is new token r % S_new of
+  // query head hk*G + r / S_new (contiguous in [B, H_q, S_new, D]).  Batch
+  // entry b's cache holds seqlens[b] tokens (clamped to [0, max_len]) and
+  // the new tokens are its last S_new, so row r sits at position
+  // len - S_new + r % S_new.  The keys of each (b, hk) are cut into n_split
+  // ranges of split_tiles 64-key tiles; with n_split > 1 each range writes
+  // its normalised output and log-sum-exp to o_part / lse_part in float32
+  // ([n_split][B*H_q*S_new][D] and [n_split][B*H_q*S_new]) for a merge.
+  const int32_t* seqlens;
+  int max_len, sq_new, grp;
+  int n_split, split_tiles;
+  float* o_part;
+  float* lse_part;
 };
 
 // Key interval [lo, hi] of query i, clamped to [0, S_k-1] (empty: lo > hi).
@@ -161,7 +176,7 @@ __device__ __forceinline__ float sigmoid(float x) {
 // ALiBi slope of query head h: 2^(-max_bias * (h+1) / H), in log2 units of
 // the exponent (times log2 e) so it can be applied to base-2 scores.
 __device__ __forceinline__ float alibi_slope_log2(const KernelArgs& a, int h) {
-  return fast_exp2(-a.alibi_max_bias * (float)(h + 1) / (float)a.nh) * kLog2e;
+  return fast_exp2(-a.alibi_max_bias * (float)(h + 1) / (float)a.alibi_nh) * kLog2e;
 }
 
 // cap * tanh(y) in log2 units, from t = 2*y*log2(e):

@@ -18,6 +18,15 @@ hipError_t launch_diff_bf16(const KernelArgs& a, int dqk, int dv, hipStream_t st
 // bf16 Evoformer gated attention, C = 32: qb = 1 or 2, bias = pair bias.
 hipError_t launch_evo_bf16(const KernelArgs& a, int c, int qb, bool bias, hipStream_t st);
 
+// bf16 decode against a KV cache, D = 64 (KernelArgs' decode fields set):
+// grid = B * H_kv * n_qt * n_split work-groups.
+hipError_t launch_decode_bf16(const KernelArgs& a, int mod, hipStream_t st);
+
+// Merge of n_parts partial results per row (merge.hpp) into o (bf16 or
+// float32) and lse (may be NULL).
+hipError_t launch_merge(const float* o_part, const float* lse_part, int n_parts, int64_t n_rows,
+                        int D, void* o, bool out_bf16, float* lse, hipStream_t st);
+
 // float32 path: (dqk, dv, ns, mod) as built in inst_f32.hip.
 hipError_t launch_f32(const KernelArgs& a, int dqk, int dv, int ns, int mod, hipStream_t st);
 

@@ -84,6 +84,46 @@ def evoformer_bytes(N_seq, N_res, H, C, axis, elem=2) -> int:
     return b
 
 
+def decode_keys(mask, L: int, S_q: int, *, window: int = 256, window_causal=True,
+                prefix: int = 512):
+    """(allowed pairs, keys any row needs) of one (sequence, head) in decode:
+    the S_q queries sit at positions L-S_q .. L-1 and see keys 0 .. L-1.
+    ``mask`` is None (no mask) or a mask variant name."""
+    pairs, lo_u, hi_u = 0, None, None
+    for pos in range(L - S_q, L):
+        if mask in (None, "vanilla", "alibi", "softcap"):
+            lo, hi = 0, L - 1
+        elif mask == "causal":
+            lo, hi = 0, pos
+        elif mask == "sliding_window":
+            lo = pos - window + 1
+            hi = pos if window_causal else pos + window - 1
+        elif mask == "prefix_lm":
+            lo, hi = 0, max(pos, prefix - 1)
+        else:
+            raise ValueError(mask)
+        lo, hi = max(lo, 0), min(hi, L - 1)
+        if lo > hi:
+            continue
+        pairs += hi - lo + 1
+        lo_u = lo if lo_u is None else min(lo_u, lo)
+        hi_u = hi if hi_u is None else max(hi_u, hi)
+    return pairs, (0 if lo_u is None else hi_u - lo_u + 1)
+
+
+def decode_work(mask, lengths, Hq, Hkv, S_q, D, elem=2, lse=False, **kw):
+    """(useful FLOPs, algorithmic bytes) of a decode call: the K/V rows some
+    query needs, read once per K/V head, plus q and o."""
+    f, b = 0, 0
+    for L in lengths:
+        pairs, keys = decode_keys(mask, int(L), S_q, **kw)
+        f += 2 * pairs * 2 * D * Hq
+        b += elem * keys * 2 * D * Hkv
+    rows = len(lengths) * Hq * S_q
+    b += elem * 2 * rows * D + (4 * rows if lse else 0)
+    return f, b
+
+
 def roofline_tflops(flops: float, nbytes: float, peak_tflops=PEAK_BF16_TFLOPS,
                     hbm_gbs=PEAK_HBM_GBS):
     """(bound, attainable TFLOP/s) of a kernel with that work and traffic."""

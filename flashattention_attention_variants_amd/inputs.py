@@ -91,12 +91,30 @@ def evoformer_inputs(N_seq, N_res, H, C, dtype="bf16", seed=0, masked_frac=0.05)
     return q, k, v, gate, bias, key_mask
 
 
+def cache_lengths(B: int, lo: int, hi: int, seed: int) -> torch.Tensor:
+    """Tokens held by each of B KV caches, int32 uniform on [lo, hi]."""
+    return torch.randint(lo, hi + 1, (B,), generator=_gen(seed), dtype=torch.int64).to(torch.int32)
+
+
+def decode_inputs(B, Hq, Hkv, S_q, S_cap, D, dtype="bf16", seed=0, layout="bhsd"):
+    """q [B,Hq,S_q,D] (the newest tokens) and a KV cache of S_cap slots per
+    sequence, drawn in the order q, k, v as [B,Hkv,S_cap,D]; for layout
+    "bshd" the same values are returned as [B,S_cap,Hkv,D]."""
+    g = _gen(seed)
+    q = randn(g, (B, Hq, S_q, D), dtype)
+    k = randn(g, (B, Hkv, S_cap, D), dtype)
+    v = randn(g, (B, Hkv, S_cap, D), dtype)
+    if layout == "bshd":
+        k, v = k.transpose(1, 2).contiguous(), v.transpose(1, 2).contiguous()
+    return q, k, v
+
+
 @dataclass(frozen=True)
 class Workload:
     """A named synthetic workload: shapes, dtype, variants and seeds."""
 
     name: str
-    kind: str                    # "attn", "diffattn" or "evoformer"
+    kind: str                    # "attn", "diffattn", "evoformer" or "decode"
     dtype: str
     shape: dict
     variants: tuple
@@ -139,6 +157,15 @@ WORKLOADS = {
         "evoformer_bf16_nseq128_nres256_h8_c32", "evoformer", "bf16",
         dict(N_seq=128, N_res=256, H=8, C=32), ("row", "col"), seed=5,
         params=dict(masked_frac=0.05)),
+    # decode against a KV cache: one new token per sequence, GQA 32/8 with head
+    # dim 64 (the shape of the small LLM the pages serve), cache lengths mixed
+    # uniformly between 512 and 8192 tokens in place of a serving trace
+    "decode_bf16_b64_hq32_hkv8_cap8192_d64": Workload(
+        "decode_bf16_b64_hq32_hkv8_cap8192_d64", "decode", "bf16",
+        dict(B=64, Hq=32, Hkv=8, Sq=1, S_cap=8192, D=64),
+        ("causal", "softcap", "alibi", "sliding_window"), seed=7,
+        params=dict(softcap=50.0, alibi_max_bias=8.0, window=1024, window_causal=True,
+                    len_lo=512, len_hi=8192, len_seed=7007)),
 }
 
 
@@ -162,4 +189,9 @@ def make(wl: Workload, S: int | None = None):
         q, k, v, gate, bias, km = evoformer_inputs(s["N_seq"], s["N_res"], s["H"], s["C"],
                                                    wl.dtype, wl.seed, wl.params["masked_frac"])
         return dict(q=q, k=k, v=v, gate=gate, pair_bias=bias, key_mask=km)
+    if wl.kind == "decode":
+        q, k, v = decode_inputs(s["B"], s["Hq"], s["Hkv"], s["Sq"], s["S_cap"], s["D"], wl.dtype,
+                                wl.seed)
+        L = cache_lengths(s["B"], wl.params["len_lo"], wl.params["len_hi"], wl.params["len_seed"])
+        return dict(q=q, k_cache=k, v_cache=v, seqlens=L)
     raise ValueError(wl.kind)

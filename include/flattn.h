@@ -30,6 +30,7 @@
 #ifndef FLATTN_H
 #define FLATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -164,6 +165,76 @@ fl_status fl_evoformer_gated_attn_fwd(const void* q, const void* k, const void* 
                                       const uint8_t* key_mask, void* o, int N_seq, int N_res,
                                       int H, int C, fl_evo_axis axis, fl_dtype dtype,
                                       float scale, void* stream);
+
+/*
+ * Decode-phase attention against a KV cache, with the keys of each sequence
+ * split over several work-groups and their partial results merged (the
+ * serving path the pages leave untested: papers.lqhl.me wiki, "假设压力测试",
+ * serving-path paragraph; the merge is the online-softmax rescaling identity
+ * applied to whole key ranges: gist.science explainer, "Technical Summary:
+ * Methodology", semantic fusion).
+ *   q        [B, H_q, S_q, D] contiguous: the S_q newest tokens of each
+ *            sequence (S_q = 1 for plain decoding; more for speculative or
+ *            chunked steps)
+ *   k_cache, v_cache  the cache, S_cap token slots per sequence:
+ *            layout FL_KV_BHSD: [B, H_kv, S_cap, D]; FL_KV_BSHD: [B, S_cap, H_kv, D]
+ *   cache_seqlens  device int32 [B]: tokens held by each sequence's cache,
+ *            the new ones included (they were appended before the call).
+ *            Values are clamped to [0, max_seqlen] on the device.
+ *   o        [B, H_q, S_q, D] bf16 output; lse NULL or [B, H_q, S_q] float32
+ * Query i of sequence b sits at position L_b - S_q + i (L_b its clamped
+ * length) and sees the keys 0 .. L_b - 1 that its variant allows, with masks
+ * and ALiBi distances taken between positions (a causal mask is therefore
+ * bottom-right aligned).  Variants: vanilla, ALiBi, softcap, causal, sliding
+ * window, PrefixLM, and a mask composed with a score modification
+ * (fl_attn_params.mask); FL_DOCUMENT returns FL_ERR_UNSUPPORTED.  There is
+ * no bias.  GQA: the G = H_q / H_kv query heads of a K/V head are handled
+ * together, so each cached key is read once per K/V head.
+ *   max_seqlen  an upper bound of cache_seqlens, 0 <= max_seqlen <= S_cap:
+ *            the keys are cut into ranges up to it
+ *   num_splits  key ranges per (sequence, K/V head): 0 lets the library
+ *            choose from the shape; 1 computes each row in one pass with no
+ *            workspace; more are capped at the number of 64-key tiles
+ *   workspace  device memory, 16-byte aligned, of at least
+ *            fl_attn_decode_workspace_size(...) bytes for the same arguments
+ *            (may be NULL when that size is 0); it holds the partial results
+ *            between the two kernels this call enqueues
+ * FL_BF16 with D = 64 only.  Errors: FL_ERR_NULL (q, caches, seqlens, o, or
+ * a needed workspace missing), FL_ERR_SHAPE, FL_ERR_ALIGN, FL_ERR_PARAM (bad
+ * variant parameters, max_seqlen outside [0, S_cap], workspace too small),
+ * FL_ERR_UNSUPPORTED.
+ */
+typedef enum { FL_KV_BHSD = 0, FL_KV_BSHD = 1 } fl_kv_layout;
+
+fl_status fl_attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* cache_seqlens, void* o, float* lse, void* workspace,
+                             size_t workspace_bytes, int B, int H_q, int H_kv, int S_q, int S_cap,
+                             int max_seqlen, int D, fl_kv_layout layout, fl_dtype dtype,
+                             const fl_attn_params* params, int num_splits, void* stream);
+
+/* Workspace bytes fl_attn_decode_fwd needs for these arguments (0 when it
+ * runs one key range per row); -1 for invalid sizes. */
+int64_t fl_attn_decode_workspace_size(int B, int H_q, int H_kv, int S_q, int max_seqlen, int D,
+                                      int num_splits);
+
+/* Key ranges per (sequence, K/V head) that fl_attn_decode_fwd uses for
+ * these arguments; -1 for invalid sizes. */
+int fl_attn_decode_num_splits(int B, int H_q, int H_kv, int S_q, int max_seqlen, int num_splits);
+
+/*
+ * Merge of partial attention results over disjoint key sets (the same
+ * identity as above): for each of n_rows rows,
+ *   LSE = ln sum_p e^(LSE_p),  O = sum_p e^(LSE_p - LSE) O_p,
+ * parts with LSE_p = -inf weigh nothing, and a row with no non-empty part
+ * gets O = 0, LSE = -inf.
+ *   o_parts   device float32 [n_parts][n_rows][D], each part normalised
+ *   lse_parts device float32 [n_parts][n_rows], natural log
+ *   o         [n_rows][D] of out_dtype; lse NULL or float32 [n_rows]
+ * 1 <= n_parts; any D >= 1.  The same exchange merges results computed on
+ * different devices over shards of the keys.
+ */
+fl_status fl_attn_merge(const float* o_parts, const float* lse_parts, void* o, float* lse,
+                        int n_parts, int64_t n_rows, int D, fl_dtype out_dtype, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* fl_status_str(fl_status status);

@@ -18,8 +18,10 @@ def errors(got, want):
     got, want = np.asarray(got, np.float64), np.asarray(want, np.float64)
     assert got.shape == want.shape, (got.shape, want.shape)
     both_inf = np.isinf(got) & np.isinf(want) & (np.sign(got) == np.sign(want))
-    d = np.where(both_inf, 0.0, np.abs(got - want))
-    rel = np.linalg.norm(np.where(both_inf, 0, got - want)) / max(np.linalg.norm(np.where(both_inf, 0, want)), 1e-30)
+    with np.errstate(invalid="ignore"):  # inf - inf where both are the same infinity
+        diff = np.where(both_inf, 0.0, got - want)
+    d = np.abs(diff)
+    rel = np.linalg.norm(diff) / max(np.linalg.norm(np.where(both_inf, 0, want)), 1e-30)
     return float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0, float(rel)
 
 

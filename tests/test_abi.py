@@ -123,3 +123,66 @@ def test_evoformer_validation(lib):
     assert f(bias=FAKE, N_res=12) == api.FL_ERR_ALIGN
     assert f(o=MISALIGNED) == api.FL_ERR_ALIGN
     assert f(N_seq=0, q=None) == api.FL_OK
+
+
+def decode(lib, p, q=FAKE, kc=FAKE, vc=FAKE, seqlens=FAKE, o=FAKE, lse=None, ws=None, ws_bytes=0,
+           B=2, Hq=8, Hkv=2, Sq=1, S_cap=256, max_len=256, D=64, layout=0, dt=api.FL_BF16,
+           splits=1):
+    return lib.fl_attn_decode_fwd(q, kc, vc, seqlens, o, lse, ws, ws_bytes, B, Hq, Hkv, Sq, S_cap,
+                                  max_len, D, layout, dt,
+                                  None if p is None else ctypes.byref(p), splits, None)
+
+
+def test_decode_validation(lib):
+    assert decode(lib, None) == api.FL_ERR_NULL
+    assert decode(lib, params(), seqlens=None) == api.FL_ERR_NULL
+    assert decode(lib, params(), q=None) == api.FL_ERR_NULL
+    assert decode(lib, params(), D=128) == api.FL_ERR_UNSUPPORTED
+    assert decode(lib, params(), dt=api.FL_F32) == api.FL_ERR_UNSUPPORTED
+    assert decode(lib, params(variant=6, n_docs=1)) == api.FL_ERR_UNSUPPORTED
+    assert decode(lib, params(variant=1, mask=6, n_docs=1)) == api.FL_ERR_UNSUPPORTED
+    assert decode(lib, params(variant=3, mask=4)) == api.FL_ERR_PARAM
+    assert decode(lib, params(variant=4, window=0)) == api.FL_ERR_PARAM
+    assert decode(lib, params(variant=2, softcap=-1.0)) == api.FL_ERR_PARAM
+    assert decode(lib, params(), max_len=300) == api.FL_ERR_PARAM     # beyond the cache
+    assert decode(lib, params(), max_len=-1) == api.FL_ERR_SHAPE
+    assert decode(lib, params(), Hq=6, Hkv=4) == api.FL_ERR_SHAPE
+    assert decode(lib, params(), layout=2) == api.FL_ERR_PARAM
+    assert decode(lib, params(), splits=-1) == api.FL_ERR_PARAM
+    assert decode(lib, params(), o=MISALIGNED) == api.FL_ERR_ALIGN
+    assert decode(lib, params(), seqlens=P(0x10002)) == api.FL_ERR_ALIGN
+    # four key ranges need a workspace of the size the library reports
+    need = lib.fl_attn_decode_workspace_size(2, 8, 2, 1, 256, 64, 4)
+    assert need == 4 * 16 * 64 * 4 + 4 * 16 * 4
+    assert decode(lib, params(), splits=4) == api.FL_ERR_NULL
+    assert decode(lib, params(), splits=4, ws=FAKE, ws_bytes=need - 1) == api.FL_ERR_PARAM
+    assert decode(lib, params(), splits=4, ws=MISALIGNED, ws_bytes=need) == api.FL_ERR_ALIGN
+    assert decode(lib, params(), B=0, q=None, o=None) == api.FL_OK
+
+
+def test_decode_split_choice(lib):
+    ns = lib.fl_attn_decode_num_splits
+    ws = lib.fl_attn_decode_workspace_size
+    assert ns(2, 8, 2, 1, 256, 1) == 1 and ws(2, 8, 2, 1, 256, 64, 1) == 0
+    assert ns(2, 8, 2, 1, 256, 100) == 4          # capped at the 4 tiles of 64 keys
+    assert ns(1, 8, 8, 1, 300, 2) == 2            # 5 tiles: ranges of 3 and 2
+    # chosen: enough work-groups, but ranges of at least 8 tiles
+    assert ns(64, 32, 8, 1, 8192, 0) == 4         # 512 (sequence, head) pairs x 4
+    assert ns(1, 32, 8, 1, 8192, 0) == 16         # 128 tiles / 8
+    assert ns(1, 32, 8, 1, 256, 0) == 1
+    assert ns(4, 32, 8, 1, 0, 0) == 1 and ws(4, 32, 8, 1, 0, 64, 0) == 0
+    assert ns(2, 8, 3, 1, 256, 0) == -1 and ws(-1, 8, 2, 1, 256, 64, 0) == -1
+    # 16-byte rounding of the LSE block
+    assert ws(1, 1, 1, 3, 256, 64, 2) == 2 * 3 * 64 * 4 + 32
+
+
+def test_merge_validation(lib):
+    f = lambda **kw: lib.fl_attn_merge(kw.get("op", FAKE), kw.get("lp", FAKE), kw.get("o", FAKE),
+                                       kw.get("lse"), kw.get("n", 2), kw.get("rows", 10),
+                                       kw.get("D", 64), kw.get("dt", api.FL_BF16), None)
+    assert f(n=0) == api.FL_ERR_SHAPE
+    assert f(D=0) == api.FL_ERR_SHAPE
+    assert f(dt=5) == api.FL_ERR_UNSUPPORTED
+    assert f(op=None) == api.FL_ERR_NULL
+    assert f(lse=P(0x10002)) == api.FL_ERR_ALIGN
+    assert f(rows=0, op=None, lp=None, o=None) == api.FL_OK

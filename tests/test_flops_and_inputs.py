@@ -48,3 +48,32 @@ def test_inputs_seeded_and_rounded():
     assert torch.equal(a[0], f.to(torch.bfloat16))
     q, k, v, gate, bias, km = inputs.evoformer_inputs(16, 32, 2, 32, "bf16", seed=5)
     assert km.dtype == torch.uint8 and 0.8 < km.float().mean() < 1.0
+
+
+@pytest.mark.parametrize("mask", [None, "causal", "sliding_window", "prefix_lm"])
+@pytest.mark.parametrize("wc", [True, False])
+def test_decode_pairs_and_keys_bruteforce(mask, wc):
+    """Decode pair counts and the keys any row needs, against the brute-force
+    decode's own allowed matrix (a key's row of weights is non-zero exactly
+    where it is allowed, with V = identity)."""
+    for L, Sq in ((1, 1), (9, 3), (40, 1), (40, 7), (2, 5)):
+        q = np.zeros((1, 1, Sq, 4))
+        kc = np.zeros((1, 1, L, 4))
+        vc = np.eye(L)[None, None] if L else np.zeros((1, 1, 0, 0))
+        kw = dict(window=4, window_causal=wc, prefix=6)
+        p, _ = bf.decode_attention(q, kc, vc, [L], variant=mask or "vanilla", **kw)
+        allowed = p[0, 0] > 0
+        pairs, keys = flops.decode_keys(mask, L, Sq, **kw)
+        assert pairs == int(allowed.sum())
+        cols = np.nonzero(allowed.any(0))[0]
+        assert keys == (0 if cols.size == 0 else cols.max() - cols.min() + 1)
+
+
+def test_decode_inputs_and_lengths():
+    q, k, v = inputs.decode_inputs(2, 4, 2, 3, 10, 64, "bf16", seed=9)
+    q2, k2, v2 = inputs.decode_inputs(2, 4, 2, 3, 10, 64, "bf16", seed=9, layout="bshd")
+    assert k.shape == (2, 2, 10, 64) and k2.shape == (2, 10, 2, 64)
+    assert torch.equal(k2.transpose(1, 2), k) and torch.equal(q, q2)
+    L = inputs.cache_lengths(1000, 512, 8192, seed=7007)
+    assert L.dtype == torch.int32 and int(L.min()) >= 512 and int(L.max()) <= 8192
+    assert 4000 < float(L.float().mean()) < 4700
