@@ -6,7 +6,9 @@ document mask) on the MHA workload B=4, H=16, S=4096, D=64, bf16 (inputs
 resident in HBM before timing).  ``value`` is the useful TFLOP/s of the whole
 step; per-variant figures, the roofline of the dominant kernel (live HIP
 event timing on the launch stream) and the CPU oracle's throughput on a
-bounded sample of the same workload are printed on the same JSON line.
+bounded sample of the same workload are printed on the same JSON line, with
+the decode workload (64 sequences, 32/8 heads, KV caches of 512-8192 tokens)
+timed beside it in GB/s against the HBM roofline.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --report        # extra lines: every workload, every variant
@@ -21,6 +23,7 @@ import time
 
 METRIC = "attention fwd useful TFLOP/s + % bf16 MFMA peak (S=4k, D=64, per variant)"
 HEADLINE = "mha_bf16_b4_h16_s4096_d64"
+DECODE_WORKLOAD = "decode_bf16_b64_hq32_hkv8_cap8192_d64"
 
 
 def parse():
@@ -36,6 +39,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode measurement printed beside the step")
     ap.add_argument("--report", action="store_true",
                     help="also print one JSON line per workload and variant")
     ap.add_argument("--traffic", default=None,
@@ -168,6 +173,25 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(t, variants, kws, wl, args.cpu_seconds)
 
+    # decode against a KV cache (split keys + merge), HBM-bound: its own
+    # workload, timed after the step, reported beside it
+    decode = None
+    if not args.no_decode:
+        dwl = inputs.WORKLOADS[DECODE_WORKLOAD]
+        dt = inputs.make(dwl)
+        dg = {k_: v_.to(dev) for k_, v_ in dt.items()}
+        dper = {}
+        for vname in dwl.variants:
+            dms, df, dnb = decode_case(torch, api, flops, dwl, dt, dg, vname, dev)
+            gbs = dnb / (dms * 1e-3) / 1e9
+            dper[vname] = dict(ms=round(dms, 4), gbs=round(gbs, 1),
+                               frac_hbm=round(gbs / flops.PEAK_HBM_GBS, 4),
+                               tflops=round(df / (dms * 1e-3) / 1e12, 2),
+                               algorithmic_bytes=dnb, bound="hbm")
+        decode = dict(workload=dwl.name, per_variant=dper,
+                      timing="best of 3 batches of back-to-back calls, decode and merge kernels")
+        del dg
+
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 4),
@@ -177,7 +201,7 @@ def main():
                    "variants": variants, "step": "one forward call per variant",
                    "seed": wl.seed},
         "frac_bf16_peak": round(value / flops.PEAK_BF16_TFLOPS, 4),
-        "roofline": roofline, "cpu_baseline": cpu, "per_variant": per,
+        "roofline": roofline, "cpu_baseline": cpu, "per_variant": per, "decode": decode,
     }
     print(json.dumps(line), flush=True)
     if args.report:
@@ -252,33 +276,59 @@ def cpu_baseline(t, variants, kws, wl, seconds):
                       "%.1f s" % (n, len(variants), wl.name, total_s)}
 
 
-def report(torch, api, flops, inputs, dev):
-    """One JSON line per (workload, variant): time, TFLOP/s, roofline fraction."""
-
-    def timeit(fn, settle=0.3, batches=3, batch_s=0.05):
-        # a short settle at this case's load, then the fastest of a few
-        # timed batches of back-to-back calls
-        t_end = time.perf_counter() + settle
-        n = 0
-        while time.perf_counter() < t_end or n < 3:
-            fn()
-            torch.cuda.synchronize()
-            n += 1
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
+def timeit(torch, fn, settle=0.3, batches=3, batch_s=0.05):
+    """ms per call: a short settle at this case's load, then the fastest of a
+    few timed batches of back-to-back calls (events on the current stream,
+    which the calls launch on)."""
+    t_end = time.perf_counter() + settle
+    n = 0
+    while time.perf_counter() < t_end or n < 3:
         fn()
+        torch.cuda.synchronize()
+        n += 1
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    fn()
+    b.record()
+    torch.cuda.synchronize()
+    iters = max(5, int(batch_s * 1e3 / max(a.elapsed_time(b), 1e-3)))
+    best = float("inf")
+    for _ in range(batches):
+        a.record()
+        for _ in range(iters):
+            fn()
         b.record()
         torch.cuda.synchronize()
-        iters = max(5, int(batch_s * 1e3 / max(a.elapsed_time(b), 1e-3)))
-        best = float("inf")
-        for _ in range(batches):
-            a.record()
-            for _ in range(iters):
-                fn()
-            b.record()
-            torch.cuda.synchronize()
-            best = min(best, a.elapsed_time(b) / iters)
-        return best
+        best = min(best, a.elapsed_time(b) / iters)
+    return best
+
+
+def decode_case(torch, api, flops, wl, t, g, vname, dev):
+    """(ms, useful flops, algorithmic bytes) of one decode call of workload wl."""
+    s = wl.shape
+    kw = dict(variant=vname)
+    for key in ("softcap", "alibi_max_bias", "window", "window_causal"):
+        if key in wl.params:
+            kw[key] = wl.params[key]
+    L = t["seqlens"]
+    max_len = int(L.max())
+    ws_bytes = api.fl_attn_decode_workspace_size(
+        s["B"], s["Hq"], s["Hkv"], s["Sq"], max_len, s["D"], variant=vname,
+        window=kw.get("window", 256), window_causal=kw.get("window_causal", True))
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(g["q"])
+    ms = timeit(torch, lambda: api.fl_attn_decode_fwd(
+        g["q"], g["k_cache"], g["v_cache"], g["seqlens"], max_seqlen=max_len, workspace=ws,
+        out=out, **kw))
+    mask = vname if vname in ("causal", "sliding_window", "prefix_lm") else None
+    f, nb = flops.decode_work(mask, L.tolist(), s["Hq"], s["Hkv"], s["Sq"], s["D"],
+                              window=wl.params.get("window", 256),
+                              window_causal=wl.params.get("window_causal", True))
+    return ms, f, nb
+
+
+def report(torch, api, flops, inputs, dev):
+    """One JSON line per (workload, variant): time, TFLOP/s, roofline fraction."""
 
     for name, wl in inputs.WORKLOADS.items():
         t = inputs.make(wl)
@@ -293,7 +343,7 @@ def report(torch, api, flops, inputs, dev):
                 if vname == "document":
                     kw["doc_offsets"] = g["doc_offsets"]
                 out = torch.empty_like(g["q"])
-                ms = timeit(lambda: api.fl_attn_fwd(g["q"], g["k"], g["v"], out=out, **kw))
+                ms = timeit(torch, lambda: api.fl_attn_fwd(g["q"], g["k"], g["v"], out=out, **kw))
                 f = flops.attn_flops(vname, s["B"], s["Hq"], s["S"], s["S"], s["D"],
                                      window=wl.params.get("window", 256),
                                      window_causal=wl.params.get("window_causal", True),
@@ -305,15 +355,18 @@ def report(torch, api, flops, inputs, dev):
             elif wl.kind == "diffattn":
                 out = torch.empty(s["B"], s["H"], s["S"], s["Dv"], dtype=torch.bfloat16, device=dev)
                 causal = vname == "causal"
-                ms = timeit(lambda: api.fl_diffattn_fwd(g["q1"], g["q2"], g["k1"], g["k2"], g["v"],
+                ms = timeit(torch, lambda: api.fl_diffattn_fwd(g["q1"], g["q2"], g["k1"], g["k2"], g["v"],
                                                         lam=wl.params["lam"], causal=causal, out=out))
                 f = flops.diffattn_flops(s["B"], s["H"], s["S"], s["Dqk"], s["Dv"], causal)
                 nb = flops.diffattn_bytes(s["B"], s["H"], s["S"], s["Dqk"], s["Dv"])
                 peak = flops.PEAK_BF16_TFLOPS
+            elif wl.kind == "decode":
+                ms, f, nb = decode_case(torch, api, flops, wl, t, g, vname, dev)
+                peak = flops.PEAK_BF16_TFLOPS
             else:
                 out = torch.empty_like(g["q"])
                 pb = g["pair_bias"] if vname == "row" else None
-                ms = timeit(lambda: api.fl_evoformer_gated_attn_fwd(
+                ms = timeit(torch, lambda: api.fl_evoformer_gated_attn_fwd(
                     g["q"], g["k"], g["v"], g["gate"], pair_bias=pb, key_mask=g["key_mask"],
                     axis=vname, out=out))
                 f = flops.evoformer_flops(s["N_seq"], s["N_res"], s["H"], s["C"], vname)

@@ -73,9 +73,9 @@ def load_library(path: str | None = None):
     lib.fl_evoformer_gated_attn_fwd.argtypes = [V, V, V, V, V, V, V, I, I, I, I, I, I, F, V]
     lib.fl_attn_decode_fwd.argtypes = [V, V, V, V, V, V, V, SZ, I, I, I, I, I, I, I, I, I,
                                        ctypes.POINTER(AttnParams), I, V]
-    lib.fl_attn_decode_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    lib.fl_attn_decode_workspace_size.argtypes = [I, I, I, I, I, I, ctypes.POINTER(AttnParams), I]
     lib.fl_attn_decode_workspace_size.restype = I64
-    lib.fl_attn_decode_num_splits.argtypes = [I, I, I, I, I, I]
+    lib.fl_attn_decode_num_splits.argtypes = [I, I, I, I, I, ctypes.POINTER(AttnParams), I]
     lib.fl_attn_decode_num_splits.restype = I
     lib.fl_attn_merge.argtypes = [V, V, V, V, I, I64, I, I, V]
     for f in (lib.fl_attn_fwd, lib.fl_diffattn_fwd, lib.fl_evoformer_gated_attn_fwd,
@@ -168,17 +168,27 @@ def _params(variant, mask, scale, D, softcap, alibi_max_bias, window, window_cau
                       None if docs is None else docs.data_ptr(), msk)
 
 
-def fl_attn_decode_workspace_size(B, Hq, Hkv, Sq, max_seqlen, D=64, num_splits=0):
+def _window_params(variant, mask, window, window_causal):
+    return _params(variant, mask, None, 64, 50.0, 8.0, window, window_causal, 0)
+
+
+def fl_attn_decode_workspace_size(B, Hq, Hkv, Sq, max_seqlen, D=64, num_splits=0, *,
+                                  variant="vanilla", mask=None, window=256, window_causal=True):
     """Bytes of device workspace :func:`fl_attn_decode_fwd` needs (0: none)."""
-    n = load_library().fl_attn_decode_workspace_size(B, Hq, Hkv, Sq, max_seqlen, D, num_splits)
+    p = _window_params(variant, mask, window, window_causal)
+    n = load_library().fl_attn_decode_workspace_size(B, Hq, Hkv, Sq, max_seqlen, D,
+                                                     ctypes.byref(p), num_splits)
     if n < 0:
         raise ValueError("invalid decode sizes")
     return int(n)
 
 
-def fl_attn_decode_num_splits(B, Hq, Hkv, Sq, max_seqlen, num_splits=0):
+def fl_attn_decode_num_splits(B, Hq, Hkv, Sq, max_seqlen, num_splits=0, *, variant="vanilla",
+                              mask=None, window=256, window_causal=True):
     """Key ranges per (sequence, K/V head) the decode call uses."""
-    n = load_library().fl_attn_decode_num_splits(B, Hq, Hkv, Sq, max_seqlen, num_splits)
+    p = _window_params(variant, mask, window, window_causal)
+    n = load_library().fl_attn_decode_num_splits(B, Hq, Hkv, Sq, max_seqlen, ctypes.byref(p),
+                                                 num_splits)
     if n < 0:
         raise ValueError("invalid decode sizes")
     return int(n)
@@ -214,12 +224,12 @@ def fl_attn_decode_fwd(q, k_cache, v_cache, cache_seqlens, *, max_seqlen=None, l
     if lse is None and return_lse:
         lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=q.device)
     _dev(lse, "lse", torch.float32)
+    p = _params(variant, mask, scale, D, softcap, alibi_max_bias, window, window_causal, prefix)
     need = load_library().fl_attn_decode_workspace_size(B, Hq, Hkv, Sq, int(max_seqlen), D,
-                                                        int(num_splits))
+                                                        ctypes.byref(p), int(num_splits))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace", torch.uint8)
-    p = _params(variant, mask, scale, D, softcap, alibi_max_bias, window, window_causal, prefix)
     st = load_library().fl_attn_decode_fwd(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(out), _ptr(lse), _ptr(workspace),
         0 if workspace is None else workspace.numel(), B, Hq, Hkv, Sq, S_cap, int(max_seqlen), D,

@@ -51,7 +51,12 @@ struct MfmaCfg {
   // decode against a KV cache: packed GQA rows, per-sequence lengths, key
   // splits (see KernelArgs)
   static constexpr bool DEC = DEC_;
-  static constexpr int NW = 4;               // waves per work-group
+  // waves per work-group; decode rows are few (the G query heads of one K/V
+  // head), so its work-groups are narrower and more of them fit a unit
+#ifndef FL_DEC_WAVES
+#define FL_DEC_WAVES 4
+#endif
+  static constexpr int NW = DEC ? FL_DEC_WAVES : 4;
   static constexpr int BM = NW * 32 * QB;    // query rows per work-group
   static constexpr int BN = 64;              // keys per tile
   // K and V tiles sit in LDS row-major without padding; the 16-byte chunks
@@ -63,7 +68,13 @@ struct MfmaCfg {
   static constexpr int K_ELEMS = BN * DQK;
   static constexpr int V_ELEMS = BN * DV;
   static constexpr int STAGE = NS * K_ELEMS + V_ELEMS;
-  static constexpr int STAGES = 3;           // tiles t (in use), t+1 (landed), t+2 (in flight)
+  // LDS stages: the tile in use plus STAGES - 1 tiles landed or in flight.
+  // Decode streams each cached key once with little work per byte, so it
+  // keeps more bytes in flight per work-group.
+#ifndef FL_DEC_STAGES
+#define FL_DEC_STAGES 3
+#endif
+  static constexpr int STAGES = DEC ? FL_DEC_STAGES : 3;
   __device__ static constexpr int kswz(int row) { return KCPR == 4 ? (row >> 1) & 3 : row & 7; }
   __device__ static constexpr int vswz(int row) { return VCPR == 4 ? 2 * ((row >> 1) & 1) : 2 * (row & 3); }
   static constexpr int KCH = BN * DQK / 8 / (NW * 64);  // 16-byte K chunks per thread
@@ -76,6 +87,7 @@ struct MfmaCfg {
   static constexpr bool SCAPB = MOD == MOD_SOFTCAP_BOUNDED;
   static_assert(!SCAPB || (!BIAS && !KMASK), "bounded softcap takes no bias or key mask");
   static_assert(!DEC || (QB == 1 && NS == 1 && !BIAS && !KMASK && !GATE), "decode form");
+  static_assert(STAGES >= 3 && STAGES <= 6 && (STAGES == 3 || !KMASK), "pipeline depth");
   // one stream fits 2 waves per SIMD; two streams need the whole register file
 #ifndef FL_QB1_WAVES
 #define FL_QB1_WAVES 2
@@ -184,7 +196,7 @@ __device__ __forceinline__ void interleave_hint() {
 }
 
 template <class C>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_EU)))
+__global__ __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_EU)))
 void attn_mfma_kernel(KernelArgs a) {
   constexpr int BN = C::BN, DQK = C::DQK, DV = C::DV, NS = C::NS, QB = C::QB;
   __shared__ __attribute__((aligned(16))) bf16 lds[C::STAGES * C::STAGE];
@@ -242,9 +254,13 @@ void attn_mfma_kernel(KernelArgs a) {
   int kt_lo = lo_first / BN;
   int kt_hi = hi_last >= lo_first ? (hi_last + BN) / BN : kt_lo;
   if constexpr (C::DEC) {
-    // this work-group's share of the keys
-    kt_lo = max(kt_lo, split * a.split_tiles);
-    kt_hi = max(min(kt_hi, (split + 1) * a.split_tiles), kt_lo);
+    // this work-group's share of the keys: its rows' key tiles cut into
+    // n_split near-equal ranges, so every sequence's work spreads evenly over
+    // its work-groups whatever its length
+    const int per = (kt_hi - kt_lo + a.n_split - 1) / a.n_split;
+    const int lo = kt_lo + split * per;
+    kt_hi = min(lo + per, kt_hi);
+    kt_lo = min(lo, kt_hi);
   }
 
   // ---- this wave's rows and their key intervals ----------------------------
@@ -405,13 +421,13 @@ void attn_mfma_kernel(KernelArgs a) {
   int k_off[C::KCH], v_off[C::VCH];
 #pragma unroll
   for (int i = 0; i < C::KCH; ++i) {
-    const int q = (i * 4 + w) * 64 + lane;  // 16-byte slot in the K tile
+    const int q = (i * C::NW + w) * 64 + lane;  // 16-byte slot in the K tile
     const int row = q / C::KCPR, phys = q % C::KCPR;
     k_off[i] = row * (int)k_row_b + 16 * (phys ^ C::kswz(row));
   }
 #pragma unroll
   for (int i = 0; i < C::VCH; ++i) {
-    const int q = (i * 4 + w) * 64 + lane;
+    const int q = (i * C::NW + w) * 64 + lane;
     const int row = q / C::VCPR, phys = q % C::VCPR;
     v_off[i] = row * (int)v_row_b + 16 * (phys ^ C::vswz(row));
   }
@@ -431,11 +447,13 @@ void attn_mfma_kernel(KernelArgs a) {
     for (int s = 0; s < NS; ++s) {
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(kblk[s] + j0 * k_row_b, k_span - j0 * k_row_b);
 #pragma unroll
-      for (int i = 0; i < C::KCH; ++i) lds_load16(rs, ks + s * C::K_ELEMS + (i * 4 + w) * 512, k_off[i]);
+      for (int i = 0; i < C::KCH; ++i)
+        lds_load16(rs, ks + s * C::K_ELEMS + (i * C::NW + w) * 512, k_off[i]);
     }
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(vblk + j0 * v_row_b, v_span - j0 * v_row_b);
 #pragma unroll
-    for (int i = 0; i < C::VCH; ++i) lds_load16(rs, ks + NS * C::K_ELEMS + (i * 4 + w) * 512, v_off[i]);
+    for (int i = 0; i < C::VCH; ++i)
+      lds_load16(rs, ks + NS * C::K_ELEMS + (i * C::NW + w) * 512, v_off[i]);
   };
   // the key-mask column of a tile travels through a register
   auto store_kmask = [&](int stage) {
@@ -741,22 +759,43 @@ void attn_mfma_kernel(KernelArgs a) {
   };
 
   // ---- main loop ---------------------------------------------------------------
-  // The it-th tile visited is consumed from stage it % 3 while the next one
-  // lands and the one after is in flight.  The barrier at the end of an
-  // iteration both publishes the next tile (every wave waited for its own
-  // loads) and frees the current stage.
+  // The it-th tile visited is consumed from stage it % STAGES while the
+  // next AHEAD - 1 have landed or are in flight; the tile AHEAD places on
+  // goes into the stage freed at the end of the previous iteration.  The
+  // barrier at the end of an iteration both publishes the next tile (every
+  // wave waited for its own loads) and frees the current stage.
   constexpr int LOADS = NS * C::KCH + C::VCH;  // LDS-bound loads per thread per tile
-  static_assert(LOADS < 64, "vmcnt range");
+  constexpr int AHEAD = C::STAGES - 1;          // tiles issued ahead of the one consumed
+  static_assert((AHEAD - 1) * LOADS < 64, "vmcnt range");
   // Publish a landed tile: wait for this wave's loads of it (leaving the
-  // newest tile's LOADS in flight when asked) and its LDS stores, then the
+  // `newer` tiles issued after it in flight) and its LDS stores, then the
   // work-group barrier.  Written out because __syncthreads() also waits for
-  // the tile still in flight.  The memory clobber keeps the compiler from
+  // the tiles still in flight.  The memory clobber keeps the compiler from
   // moving memory accesses across it.
-  auto sync_tile = [&](bool leave_one_tile) {
-    if (leave_one_tile)
+  auto sync_tile = [&](int newer) {
+    if constexpr (AHEAD >= 5) {
+      if (newer >= 4) {
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(4 * LOADS) : "memory");
+        return;
+      }
+    }
+    if constexpr (AHEAD >= 4) {
+      if (newer >= 3) {
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(3 * LOADS) : "memory");
+        return;
+      }
+    }
+    if constexpr (AHEAD >= 3) {
+      if (newer >= 2) {
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LOADS) : "memory");
+        return;
+      }
+    }
+    if (newer >= 1) {
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LOADS) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      return;
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
   // Tile order: ascending keys, except under ALiBi, where the visit starts
   // at the work-group's diagonal tile and wraps round.  The scores of a row
@@ -772,19 +811,20 @@ void attn_mfma_kernel(KernelArgs a) {
   if (n_kt > 0) {
     load_tile(tile_of(0), 0);
     store_kmask(0);
-    const bool two = n_kt > 1;
-    if (two) load_tile(tile_of(1), 1);
-    sync_tile(two);
+#pragma unroll
+    for (int t = 1; t < AHEAD; ++t)
+      if (t < n_kt) load_tile(tile_of(t), t);
+    sync_tile(min(AHEAD, n_kt) - 1);
   }
   for (int it = 0; it < n_kt; ++it) {
     const int kt = tile_of(it);
-    const int stage = it % 3;
-    const bool next = it + 1 < n_kt, next2 = it + 2 < n_kt;
+    const int stage = it % C::STAGES;
+    const bool next = it + 1 < n_kt, next2 = it + AHEAD < n_kt;
     const int j0 = kt * BN, j1 = j0 + BN - 1;
     const bool empty = wave_idle || j0 > w_hi_max || j1 < w_lo_min;
     const bool full = j0 >= w_lo_max && j1 <= w_hi_min;
-    if (next) store_kmask(stage == 2 ? 0 : stage + 1);
-    if (next2) load_tile(tile_of(it + 2), stage == 0 ? 2 : stage - 1);
+    if (next) store_kmask(stage == C::STAGES - 1 ? 0 : stage + 1);
+    if (next2) load_tile(tile_of(it + AHEAD), stage == 0 ? C::STAGES - 1 : stage - 1);
     if (!empty) {
       using F = std::integral_constant<bool, false>;
       using T = std::integral_constant<bool, true>;
@@ -800,7 +840,7 @@ void attn_mfma_kernel(KernelArgs a) {
           compute_tile(stage, kt, T{}, F{});
       }
     }
-    if (next) sync_tile(next2);
+    if (next) sync_tile(min(AHEAD - 1, n_kt - 2 - it));
   }
 
   // ---- epilogue: normalise, combine, gate, store --------------------------------

@@ -40,11 +40,12 @@ bool span_ok(int64_t rows, int64_t row_stride, int64_t width) {
 }
 
 // Decode: key ranges per (sequence, K/V head).  Enough work-groups to give
-// every compute unit several (256 units), but no range shorter than eight
-// 64-key tiles, whose partial results would cost more to merge than they
-// save.  A request is capped at the number of tiles.
+// every compute unit several (256 units), but no range shorter than sixteen
+// 64-key tiles: a work-group pays a fixed start-up (the length, the Q rows,
+// the first tiles in flight) that short ranges do not amortise.  A request
+// is capped at the number of tiles.
 constexpr int kDecodeTargetWgs = 2048;
-constexpr int kDecodeMinTiles = 8;
+constexpr int kDecodeMinTiles = 16;
 constexpr int kDecodeMaxSplits = 256;
 
 bool decode_sizes_ok(int B, int H_q, int H_kv, int S_q, int max_seqlen) {
@@ -52,10 +53,26 @@ bool decode_sizes_ok(int B, int H_q, int H_kv, int S_q, int max_seqlen) {
          S_q <= kMaxSeq && max_seqlen <= kMaxSeq && (int64_t)(H_q / H_kv) * S_q <= kMaxSeq;
 }
 
-void decode_split(int B, int H_q, int H_kv, int S_q, int max_seqlen, int requested, int& n_split,
-                  int& split_tiles) {
-  const int n_tiles = max_seqlen > 0 ? (max_seqlen + 63) / 64 : 1;
-  const int64_t n_qt = grid_qtiles((H_q / H_kv) * S_q, mfma_rows_per_wg(1));
+// keys one row block of a decode call may need: a sliding window bounds
+// them whatever the cache length
+int64_t decode_span(int S_q, int max_seqlen, const fl_attn_params* p) {
+  int64_t span = max_seqlen;
+  if (p) {
+    const int mask = p->variant >= FL_CAUSAL ? p->variant : p->mask;
+    if (mask == FL_SLIDING_WINDOW && p->window >= 1) {
+      const int64_t w = p->window_causal ? (int64_t)p->window + S_q - 1
+                                         : 2 * (int64_t)p->window + S_q - 2;
+      span = w < span ? w : span;
+    }
+  }
+  return span;
+}
+
+int decode_split(int B, int H_q, int H_kv, int S_q, int max_seqlen, const fl_attn_params* p,
+                 int requested) {
+  const int64_t span = decode_span(S_q, max_seqlen, p);
+  const int n_tiles = span > 0 ? (int)((span + 63) / 64) : 1;
+  const int64_t n_qt = grid_qtiles((H_q / H_kv) * S_q, decode_rows_per_wg());
   int s;
   if (requested > 0) {
     s = requested < n_tiles ? requested : n_tiles;
@@ -66,8 +83,7 @@ void decode_split(int B, int H_q, int H_kv, int S_q, int max_seqlen, int request
     s = (int)(want < cap ? want : cap);
     s = s < 1 ? 1 : (s > kDecodeMaxSplits ? kDecodeMaxSplits : s);
   }
-  split_tiles = (n_tiles + s - 1) / s;
-  n_split = (n_tiles + split_tiles - 1) / split_tiles;
+  return s;
 }
 
 int64_t decode_workspace(int B, int H_q, int S_q, int D, int n_split) {
@@ -348,18 +364,17 @@ fl_status fl_evoformer_gated_attn_fwd(const void* q, const void* k, const void* 
   return launch_status(launch_evo_bf16(a, C, qb, pair_bias != nullptr, st));
 }
 
-int fl_attn_decode_num_splits(int B, int H_q, int H_kv, int S_q, int max_seqlen, int num_splits) {
+int fl_attn_decode_num_splits(int B, int H_q, int H_kv, int S_q, int max_seqlen,
+                              const fl_attn_params* p, int num_splits) {
   if (!decode_sizes_ok(B, H_q, H_kv, S_q, max_seqlen) || num_splits < 0) return -1;
-  int n_split, split_tiles;
-  decode_split(B, H_q, H_kv, S_q, max_seqlen, num_splits, n_split, split_tiles);
+  const int n_split = decode_split(B, H_q, H_kv, S_q, max_seqlen, p, num_splits);
   return n_split;
 }
 
 int64_t fl_attn_decode_workspace_size(int B, int H_q, int H_kv, int S_q, int max_seqlen, int D,
-                                      int num_splits) {
+                                      const fl_attn_params* p, int num_splits) {
   if (!decode_sizes_ok(B, H_q, H_kv, S_q, max_seqlen) || D < 1 || num_splits < 0) return -1;
-  int n_split, split_tiles;
-  decode_split(B, H_q, H_kv, S_q, max_seqlen, num_splits, n_split, split_tiles);
+  const int n_split = decode_split(B, H_q, H_kv, S_q, max_seqlen, p, num_splits);
   return decode_workspace(B, H_q, S_q, D, n_split);
 }
 
@@ -393,8 +408,7 @@ fl_status fl_attn_decode_fwd(const void* q, const void* k_cache, const void* v_c
     return FL_ERR_ALIGN;
 
   const int G = H_q / H_kv;
-  int n_split, split_tiles;
-  decode_split(B, H_q, H_kv, S_q, max_seqlen, num_splits, n_split, split_tiles);
+  const int n_split = decode_split(B, H_q, H_kv, S_q, max_seqlen, p, num_splits);
   const int64_t ws = decode_workspace(B, H_q, S_q, D, n_split);
   if (ws > 0 && !workspace) return FL_ERR_NULL;
   if ((int64_t)workspace_bytes < ws) return FL_ERR_PARAM;
@@ -463,9 +477,8 @@ fl_status fl_attn_decode_fwd(const void* q, const void* k_cache, const void* v_c
     default:
       break;
   }
-  a.n_qt = grid_qtiles(G * S_q, mfma_rows_per_wg(1));
+  a.n_qt = grid_qtiles(G * S_q, decode_rows_per_wg());
   a.n_split = n_split;
-  a.split_tiles = split_tiles;
   if ((int64_t)a.n_qt * B * H_kv * n_split > kMaxGrid) return FL_ERR_SHAPE;
   const int64_t rows = (int64_t)B * H_q * S_q;
   if (n_split > 1) {

@@ -74,13 +74,13 @@ struct KernelArgs {
   // query head hk*G + r / S_new (contiguous in [B, H_q, S_new, D]).  Batch
   // entry b's cache holds seqlens[b] tokens (clamped to [0, max_len]) and
   // the new tokens are its last S_new, so row r sits at position
-  // len - S_new + r % S_new.  The keys of each (b, hk) are cut into n_split
-  // ranges of split_tiles 64-key tiles; with n_split > 1 each range writes
+  // len - S_new + r % S_new.  The key tiles a work-group's rows need are
+  // cut into n_split near-equal ranges; with n_split > 1 each range writes
   // its normalised output and log-sum-exp to o_part / lse_part in float32
   // ([n_split][B*H_q*S_new][D] and [n_split][B*H_q*S_new]) for a merge.
   const int32_t* seqlens;
   int max_len, sq_new, grp;
-  int n_split, split_tiles;
+  int n_split;
   float* o_part;
   float* lse_part;
 };

@@ -21,6 +21,7 @@ hipError_t launch_evo_bf16(const KernelArgs& a, int c, int qb, bool bias, hipStr
 // bf16 decode against a KV cache, D = 64 (KernelArgs' decode fields set):
 // grid = B * H_kv * n_qt * n_split work-groups.
 hipError_t launch_decode_bf16(const KernelArgs& a, int mod, hipStream_t st);
+int decode_rows_per_wg();  // packed query rows per decode work-group
 
 // Merge of n_parts partial results per row (merge.hpp) into o (bf16 or
 // float32) and lse (may be NULL).

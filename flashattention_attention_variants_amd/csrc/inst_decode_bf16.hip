@@ -6,12 +6,14 @@ namespace fl {
 
 template <int MOD>
 static hipError_t go_dec(const KernelArgs& a, hipStream_t st) {
+  using C = MfmaCfg<64, 64, 1, 1, MOD, false, false, false, true>;
   const int64_t nwg = (int64_t)a.nb * a.nh * a.n_qt * a.n_split;
   (void)hipGetLastError();
-  hipLaunchKernelGGL((attn_mfma_kernel<MfmaCfg<64, 64, 1, 1, MOD, false, false, false, true>>),
-                     dim3((unsigned)nwg), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(attn_mfma_kernel<C>, dim3((unsigned)nwg), dim3(C::NW * 64), 0, st, a);
   return hipGetLastError();
 }
+
+int decode_rows_per_wg() { return MfmaCfg<64, 64, 1, 1, MOD_NONE, false, false, false, true>::BM; }
 
 hipError_t launch_decode_bf16(const KernelArgs& a, int mod, hipStream_t st) {
   switch (mod) {

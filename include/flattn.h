@@ -194,7 +194,9 @@ fl_status fl_evoformer_gated_attn_fwd(const void* q, const void* k, const void* 
  *            the keys are cut into ranges up to it
  *   num_splits  key ranges per (sequence, K/V head): 0 lets the library
  *            choose from the shape; 1 computes each row in one pass with no
- *            workspace; more are capped at the number of 64-key tiles
+ *            workspace; more are capped at the number of 64-key tiles.  Each
+ *            work-group's ranges cut the keys its rows need into near-equal
+ *            parts, so every sequence's work spreads over its work-groups
  *   workspace  device memory, 16-byte aligned, of at least
  *            fl_attn_decode_workspace_size(...) bytes for the same arguments
  *            (may be NULL when that size is 0); it holds the partial results
@@ -212,14 +214,17 @@ fl_status fl_attn_decode_fwd(const void* q, const void* k_cache, const void* v_c
                              int max_seqlen, int D, fl_kv_layout layout, fl_dtype dtype,
                              const fl_attn_params* params, int num_splits, void* stream);
 
-/* Workspace bytes fl_attn_decode_fwd needs for these arguments (0 when it
- * runs one key range per row); -1 for invalid sizes. */
+/* Workspace bytes fl_attn_decode_fwd needs for the same arguments (0 when
+ * it runs one key range per row); -1 for invalid sizes.  params may be NULL
+ * (no sliding window); the split choice depends only on the sizes and, for
+ * a sliding window, its width. */
 int64_t fl_attn_decode_workspace_size(int B, int H_q, int H_kv, int S_q, int max_seqlen, int D,
-                                      int num_splits);
+                                      const fl_attn_params* params, int num_splits);
 
-/* Key ranges per (sequence, K/V head) that fl_attn_decode_fwd uses for
- * these arguments; -1 for invalid sizes. */
-int fl_attn_decode_num_splits(int B, int H_q, int H_kv, int S_q, int max_seqlen, int num_splits);
+/* Key ranges per (sequence, K/V head) that fl_attn_decode_fwd uses for the
+ * same arguments; -1 for invalid sizes. */
+int fl_attn_decode_num_splits(int B, int H_q, int H_kv, int S_q, int max_seqlen,
+                              const fl_attn_params* params, int num_splits);
 
 /*
  * Merge of partial attention results over disjoint key sets (the same

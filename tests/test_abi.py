@@ -152,7 +152,7 @@ def test_decode_validation(lib):
     assert decode(lib, params(), o=MISALIGNED) == api.FL_ERR_ALIGN
     assert decode(lib, params(), seqlens=P(0x10002)) == api.FL_ERR_ALIGN
     # four key ranges need a workspace of the size the library reports
-    need = lib.fl_attn_decode_workspace_size(2, 8, 2, 1, 256, 64, 4)
+    need = lib.fl_attn_decode_workspace_size(2, 8, 2, 1, 256, 64, None, 4)
     assert need == 4 * 16 * 64 * 4 + 4 * 16 * 4
     assert decode(lib, params(), splits=4) == api.FL_ERR_NULL
     assert decode(lib, params(), splits=4, ws=FAKE, ws_bytes=need - 1) == api.FL_ERR_PARAM
@@ -161,15 +161,21 @@ def test_decode_validation(lib):
 
 
 def test_decode_split_choice(lib):
-    ns = lib.fl_attn_decode_num_splits
-    ws = lib.fl_attn_decode_workspace_size
+    ns = lambda *a, p=None: lib.fl_attn_decode_num_splits(*a[:5], p and ctypes.byref(p), a[5])
+    ws = lambda *a, p=None: lib.fl_attn_decode_workspace_size(*a[:6], p and ctypes.byref(p), a[6])
     assert ns(2, 8, 2, 1, 256, 1) == 1 and ws(2, 8, 2, 1, 256, 64, 1) == 0
     assert ns(2, 8, 2, 1, 256, 100) == 4          # capped at the 4 tiles of 64 keys
-    assert ns(1, 8, 8, 1, 300, 2) == 2            # 5 tiles: ranges of 3 and 2
-    # chosen: enough work-groups, but ranges of at least 8 tiles
+    assert ns(1, 8, 8, 1, 300, 2) == 2
+    # chosen: enough work-groups, but ranges of at least 16 tiles
     assert ns(64, 32, 8, 1, 8192, 0) == 4         # 512 (sequence, head) pairs x 4
-    assert ns(1, 32, 8, 1, 8192, 0) == 16         # 128 tiles / 8
-    assert ns(1, 32, 8, 1, 256, 0) == 1
+    assert ns(1, 32, 8, 1, 8192, 0) == 8          # 128 tiles / 16
+    assert ns(1, 32, 8, 1, 1024, 0) == 1
+    # a sliding window bounds the keys a row needs, whatever the cache length
+    win = params(variant=4, window=1024)
+    assert ns(1, 32, 8, 1, 65536, 0, p=win) == 1
+    assert ns(1, 32, 8, 1, 65536, 0, p=params(variant=4, window=4096)) == 4
+    assert ns(1, 32, 8, 1, 65536, 0, p=params(variant=1, mask=4, window=2048, window_causal=0)) == 4
+    assert ns(1, 32, 8, 1, 65536, 0, p=params(variant=3)) == 64
     assert ns(4, 32, 8, 1, 0, 0) == 1 and ws(4, 32, 8, 1, 0, 64, 0) == 0
     assert ns(2, 8, 3, 1, 256, 0) == -1 and ws(-1, 8, 2, 1, 256, 64, 0) == -1
     # 16-byte rounding of the LSE block
