@@ -57,11 +57,19 @@ def short_name(name: str) -> str:
     return name.replace("void ", "").replace("(fl::KernelArgs)", "")
 
 
-def stats_table(dirname: str) -> str:
+def is_decode_kernel(name: str) -> bool:
+    """The decode form of the attention kernel and the merge kernel."""
+    return "merge_kernel" in name or (name.rstrip().endswith("(fl::KernelArgs)")
+                                      and ", true>" in name.replace(" >", ">"))
+
+
+def stats_table(dirname: str, keep=None) -> str:
     rows = _csv(dirname, "kernel_stats.csv")
     out = ["| kernel | calls | avg (us) | min (us) | max (us) | share |",
            "|---|---:|---:|---:|---:|---:|"]
     for r in rows:
+        if keep is not None and not keep(r["Name"]):
+            continue
         out.append("| `%s` | %s | %.1f | %.1f | %.1f | %.1f%% |" % (
             short_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
             float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
@@ -127,7 +135,7 @@ def stats_markdown(dirname: str, bench_json: str, workload: str) -> str:
            "python3 $REPO/bench.py > gpurun_out/bench.json",
            "python -m flashattention_attention_variants_amd.profiling stats-md gpurun_out/kt "
            "--bench gpurun_out/bench.json --workload %s" % workload,
-           "```", "", stats_table(dirname), "",
+           "```", "", stats_table(dirname, lambda n: not is_decode_kernel(n)), "",
            "Kernel names: `MfmaCfg<D_qk, D_v, streams, QB, MOD, bias, key mask, gate>` with QB the "
            "32-query blocks per wave and MOD 0 = none (vanilla, causal, window, PrefixLM, document), "
            "1 = ALiBi, 2 = softcap with a running reference, 3 = bounded softcap.  One kernel "
@@ -140,6 +148,35 @@ def stats_markdown(dirname: str, bench_json: str, workload: str) -> str:
     r = b["roofline"]
     out += ["", "Step value %.1f TFLOP/s.  Dominant kernel: %s, %.4f ms per launch." % (
         b["value"], r["kernel"], r["ms_per_launch"]), ""]
+    return "\n".join(out)
+
+
+def decode_stats_markdown(dirname: str, bench_json: str) -> str:
+    """Kernel-trace summary of the decode kernels in the default bench
+    command, with the bench line's decode timing beside it."""
+    b = json.load(open(bench_json))
+    d = b["decode"]
+    out = ["# attn_mfma_kernel (decode form) and merge_kernel -- %s" % d["workload"], "",
+           "Kernel trace of the default bench command, which times each decode variant after the "
+           "step (a settle, then three batches of back-to-back calls; one call = the decode kernel "
+           "plus the merge kernel), one MI355X.", "",
+           "```",
+           "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/kt -o run "
+           "-- python3 $REPO/bench.py",
+           "python3 $REPO/bench.py > gpurun_out/bench.json",
+           "python -m flashattention_attention_variants_amd.profiling decode-stats-md gpurun_out/kt "
+           "--bench gpurun_out/bench.json",
+           "```", "", stats_table(dirname, is_decode_kernel), "",
+           "Kernel names: `MfmaCfg<64, 64, 1, 1, MOD, false, false, false, true>` is the decode form "
+           "with MOD 0 = none (causal, window), 1 = ALiBi, 3 = bounded softcap; `merge_kernel<bf16>` "
+           "recombines the key ranges.", "",
+           "Bench line of the same build (per call, decode + merge):", "",
+           "| variant | ms / call | GB/s (algorithmic) | % of 8 TB/s | algorithmic MB |",
+           "|---|---:|---:|---:|---:|"]
+    for k, v in d["per_variant"].items():
+        out.append("| %s | %.4f | %.1f | %.1f | %.1f |" % (
+            k, v["ms"], v["gbs"], 100 * v["frac_hbm"], v["algorithmic_bytes"] / 1e6))
+    out.append("")
     return "\n".join(out)
 
 
@@ -230,6 +267,9 @@ def main(argv=None):
     sm.add_argument("dir")
     sm.add_argument("--bench", required=True)
     sm.add_argument("--workload", required=True)
+    dm = sub.add_parser("decode-stats-md")
+    dm.add_argument("dir")
+    dm.add_argument("--bench", required=True)
     c = sub.add_parser("counters-md")
     c.add_argument("dirs", nargs="+")
     c.add_argument("--workload", required=True)
@@ -251,6 +291,12 @@ def main(argv=None):
         path = os.path.join(ROOT, "profiles", "attn_mfma_kernel_%s_counters.md" % a.workload)
         with open(path, "w") as fh:
             fh.write(counters_markdown(a.dirs, list(wl.variants), a.workload, units))
+        print("wrote", path)
+    elif a.cmd == "decode-stats-md":
+        b = json.load(open(a.bench))
+        path = os.path.join(ROOT, "profiles", "attn_mfma_kernel_%s_stats.md" % b["decode"]["workload"])
+        with open(path, "w") as fh:
+            fh.write(decode_stats_markdown(a.dir, a.bench))
         print("wrote", path)
     elif a.cmd == "stats-md":
         path = os.path.join(ROOT, "profiles", "attn_mfma_kernel_%s_stats.md" % a.workload)

@@ -189,6 +189,83 @@ def merge(o_parts, lse_parts):
     return o.reshape(lp.shape[1:] + (Dv,)), lse.reshape(lp.shape[1:])
 
 
+def _allowed(kind, Sq, Sk, window, window_causal, prefix, offsets):
+    """Boolean [Sq, Sk] matrix of the keys each query may see (the same mask
+    definitions as oracle.c, as whole matrices)."""
+    i = np.arange(Sq)[:, None]
+    j = np.arange(Sk)[None, :]
+    if kind in (VANILLA, ALIBI, SOFTCAP):
+        return np.ones((Sq, Sk), bool)
+    if kind == CAUSAL:
+        return j <= i
+    if kind == SLIDING_WINDOW:
+        return (j <= i) & (j > i - window) if window_causal else np.abs(i - j) < window
+    if kind == PREFIX_LM:
+        return (j < prefix) | (j <= i)
+    if kind == DOCUMENT:
+        off = np.asarray(offsets)
+        doc = lambda x: np.searchsorted(off, x, side="right") - 1
+        return doc(np.arange(Sq))[:, None] == doc(np.arange(Sk))[None, :]
+    raise ValueError(kind)
+
+
+def attn_bwd(q, k, v, do, *, variant="vanilla", scale=None, softcap=50.0, alibi_max_bias=8.0,
+             window=256, window_causal=True, prefix=512, doc_offsets=None, mask=None,
+             heads=None):
+    """Gradients (dq, dk, dv) of sum(do * O) for O = attn(q, k, v, ...) (no bias).
+
+    The chain rule written out per (batch, query head) on whole float64
+    matrices (gist.science explainer, "Technical Summary: Methodology": the
+    forward is the plain softmax attention, so its gradient is the plain one):
+      S = scale q k^T, s = mod(S) masked, P = softmax_rows(s)
+      dV += P^T dO;  dP = dO V^T;  ds = P * (dP - rowsum(P * dP))
+      dS = ds * mod'(S);  dQ = scale dS K;  dK += scale dS^T Q
+    with mod' = 1 for vanilla and ALiBi (an additive term) and 1 - tanh^2(S /
+    cap) for softcap.  Rows with no allowed key get P = 0.  Query heads of a
+    group add into their K/V head's dK, dV.  ``heads`` restricts the work to
+    a list of (b, h_kv) pairs (their dk, dv are complete; dq is computed for
+    the query heads of those groups only, zero elsewhere).
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Sk, Dv = v.shape
+    G = Hq // Hkv
+    var = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    msk = 0 if mask is None else (VARIANTS[mask] if isinstance(mask, str) else int(mask))
+    kind = var if var >= CAUSAL else msk
+    sc = float(scale if scale is not None else 1.0 / np.sqrt(D))
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    todo = heads if heads is not None else [(b, hk) for b in range(B) for hk in range(Hkv)]
+    for b, hk in todo:
+        allowed = _allowed(kind, Sq, Sk, window, window_causal, prefix,
+                           None if doc_offsets is None else doc_offsets[b])
+        live = allowed.any(1)
+        for h in range(hk * G, (hk + 1) * G):
+            S = sc * (q[b, h] @ k[b, hk].T)
+            if var == ALIBI:
+                slope = 2.0 ** (-alibi_max_bias * (h + 1) / Hq)
+                S = S - slope * np.abs(np.arange(Sq)[:, None] - np.arange(Sk)[None, :])
+            dmod = 1.0
+            if var == SOFTCAP:
+                t = np.tanh(S / softcap)
+                S = softcap * t
+                dmod = 1.0 - t * t
+            s = np.where(allowed, S, -np.inf)
+            P = np.zeros_like(s)
+            m = np.max(s[live], axis=1, keepdims=True)
+            e = np.exp(s[live] - m)
+            P[live] = e / e.sum(1, keepdims=True)
+            dv[b, hk] += P.T @ do[b, h]
+            dP = do[b, h] @ v[b, hk].T
+            ds = P * (dP - (P * dP).sum(1, keepdims=True))
+            dS = ds * dmod
+            dq[b, h] = sc * (dS @ k[b, hk])
+            dk[b, hk] += sc * (dS.T @ q[b, h])
+    return dq, dk, dv
+
+
 def diffattn(q1, q2, k1, k2, v, *, scale=None, lam=0.8, causal=False, rows=None,
              threads=None):
     """Differential attention; returns (o, lse1, lse2) shaped like :func:`attn`."""

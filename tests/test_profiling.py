@@ -58,3 +58,12 @@ def test_stats_table(tmp_path):
 def test_digest_tracks_sources():
     a = profiling.kernel_digest()
     assert a == profiling.kernel_digest() and len(a) == 16
+
+
+def test_decode_kernel_names():
+    dec = "void fl::attn_mfma_kernel<fl::MfmaCfg<64, 64, 1, 1, 3, false, false, false, true> >(fl::KernelArgs)"
+    pre = "void fl::attn_mfma_kernel<fl::MfmaCfg<64, 64, 1, 2, 0, false, false, false, false> >(fl::KernelArgs)"
+    evo = "void fl::attn_mfma_kernel<fl::MfmaCfg<32, 32, 1, 2, 0, true, true, true, false> >(fl::KernelArgs)"
+    assert profiling.is_decode_kernel(dec)
+    assert profiling.is_decode_kernel("_ZN2fl12merge_kernelIDF16bEEvPKfS2_iliPT_Pf")
+    assert not profiling.is_decode_kernel(pre) and not profiling.is_decode_kernel(evo)
