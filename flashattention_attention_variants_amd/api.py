@@ -26,7 +26,7 @@ EVO_AXES = {"row": 0, "col": 1}
 KV_LAYOUTS = {"bhsd": 0, "bshd": 1}
 SYMBOLS = ("fl_attn_fwd", "fl_diffattn_fwd", "fl_evoformer_gated_attn_fwd", "fl_attn_decode_fwd",
            "fl_attn_decode_workspace_size", "fl_attn_decode_num_splits", "fl_attn_merge",
-           "fl_status_str", "fl_abi_version")
+           "fl_attn_bwd", "fl_status_str", "fl_abi_version")
 
 
 class FlError(RuntimeError):
@@ -78,8 +78,10 @@ def load_library(path: str | None = None):
     lib.fl_attn_decode_num_splits.argtypes = [I, I, I, I, I, ctypes.POINTER(AttnParams), I]
     lib.fl_attn_decode_num_splits.restype = I
     lib.fl_attn_merge.argtypes = [V, V, V, V, I, I64, I, I, V]
+    lib.fl_attn_bwd.argtypes = [V, V, V, V, V, V, V, V, V, V, I, I, I, I, I, I, I,
+                                ctypes.POINTER(AttnParams), V]
     for f in (lib.fl_attn_fwd, lib.fl_diffattn_fwd, lib.fl_evoformer_gated_attn_fwd,
-              lib.fl_attn_decode_fwd, lib.fl_attn_merge):
+              lib.fl_attn_decode_fwd, lib.fl_attn_merge, lib.fl_attn_bwd):
         f.restype = ctypes.c_int
     lib.fl_status_str.argtypes = [I]
     lib.fl_status_str.restype = ctypes.c_char_p
@@ -258,6 +260,35 @@ def fl_attn_merge(o_parts, lse_parts, *, out_dtype=torch.bfloat16, out=None, lse
                                       D, _dtype_code(out), _stream(stream))
     _check("fl_attn_merge", st)
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def fl_attn_bwd(q, k, v, o, lse, d_o, *, variant="vanilla", scale=None, softcap=50.0,
+                alibi_max_bias=8.0, window=256, window_causal=True, prefix=512, doc_offsets=None,
+                mask=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of the forward call with the same arguments,
+    given its output ``o``, its ``lse`` and the output gradient ``d_o``."""
+    q = _dev(q, "q")
+    dt = q.dtype
+    k, v, o, d_o = (_dev(t, n, dt) for t, n in ((k, "k"), (v, "v"), (o, "o"), (d_o, "d_o")))
+    lse = _dev(lse, "lse", torch.float32)
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Sk, _ = k.shape
+    dq = torch.empty_like(q) if dq is None else _dev(dq, "dq", dt)
+    dk = torch.empty_like(k) if dk is None else _dev(dk, "dk", dt)
+    dv = torch.empty_like(v) if dv is None else _dev(dv, "dv", dt)
+    if workspace is None:
+        workspace = torch.empty(max(B * Hq * Sq, 1), dtype=torch.float32, device=q.device)
+    _dev(workspace, "workspace", torch.float32)
+    docs = None
+    if VARIANTS["document"] in (VARIANTS.get(variant, variant), VARIANTS.get(mask, mask)):
+        docs = _dev(doc_offsets, "doc_offsets", torch.int32)
+    p = _params(variant, mask, scale, D, softcap, alibi_max_bias, window, window_causal, prefix,
+                docs)
+    st = load_library().fl_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
+                                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), B, Hq, Hkv, Sq,
+                                    Sk, D, _dtype_code(q), ctypes.byref(p), _stream(stream))
+    _check("fl_attn_bwd", st)
+    return dq, dk, dv
 
 
 def fl_diffattn_fwd(q1, q2, k1, k2, v, *, lam=0.8, scale=None, causal=False, out=None,

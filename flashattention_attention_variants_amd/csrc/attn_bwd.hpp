@@ -1,0 +1,390 @@
+// attn_bwd.hpp -- backward of the bf16 fused attention (gfx950 matrix cores).
+//
+// With S = scale Q K^T, s = mod(S) masked, P = softmax(s) and the saved
+// LSE, the gradients of a loss with output gradient dO are
+//
+//   D_i = sum_d dO_id O_id                     (= rowsum(P * dP))
+//   dP  = dO V^T,   dS = P * (dP - D) * mod'(S)
+//   dQ  = scale dS K,   dK = scale dS^T Q,   dV = P^T dO
+//
+// with mod' = 1 for plain scores and ALiBi (an additive term) and
+// 1 - tanh^2(S / cap) for softcap; P is recomputed from the scores and the
+// LSE, never stored (the single-pass forward keeps no score matrix; the
+// pages leave training to future work: gist.science explainer,
+// "Significance and Claims").
+//
+// Two launches share one kernel template.  Each wave owns 32 "rows" for
+// the whole kernel, held in registers in matrix-core operand order, and the
+// work-group streams 64-entry tiles of two tensors T1, T2 through LDS:
+//
+//   role   rows         T1, T2        products per 32x32 unit
+//   DQ     queries      K, V          X = S^T, Y = dP^T; dQ^T += K^T dS^T
+//   DKDV   keys         Q, dO         X = S,   Y = dP;   dK^T += Q^T dS,
+//                                                        dV^T += dO^T P
+//
+// X = T1 R1^T and Y = T2 R2^T put the row entity in the lane (one column
+// per lane) and the streamed entity in the accumulator registers, exactly
+// as the forward's S^T = K Q^T; the accumulations read T1 or T2 transposed
+// with ds_read_b64_tr_b16, and the packed bf16 dS (or P) registers are
+// directly their B operands, because the key order inside each 16-entry
+// step is the forward's permutation (16st + 4g + 0..3, 16st + 8 + 4g + 0..3).
+// DQ runs first and also writes D for the DKDV launch, which visits, for
+// each key tile, the tiles of every query head of the group that may see it.
+#pragma once
+
+#include "attn_mfma.hpp"
+
+namespace fl {
+
+enum BwdRole { BWD_DQ = 0, BWD_DKDV = 1 };
+
+template <int ROLE_, int MOD_>
+struct BwdCfg {
+  static constexpr int ROLE = ROLE_;
+  static constexpr int MOD = MOD_;
+  static constexpr int D = 64;
+  static constexpr int NW = 4;
+  static constexpr int BM = NW * 32;  // rows per work-group
+  static constexpr int BN = 64;       // streamed entries per tile
+  static constexpr int T_ELEMS = BN * D;
+  static constexpr int STAGE = 2 * T_ELEMS;
+  static constexpr int CH = BN * D / 8 / (NW * 64);  // 16-byte chunks per thread per tensor
+  // 16-byte chunks of a row are XOR-swizzled by row & 7 in LDS
+  __device__ static constexpr int swz(int row) { return row & 7; }
+  static_assert(MOD == MOD_NONE || MOD == MOD_ALIBI || MOD == MOD_SOFTCAP, "score modification");
+};
+
+template <class C>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
+  constexpr int D = C::D, BN = C::BN;
+  constexpr bool DQ = C::ROLE == BWD_DQ;
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) float stat[2][2][BN];  // [stage][lse2, delta][entry]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int c = lane & 31, g = lane >> 5;
+
+  // ---- work-group -> (b, head, row tile) ------------------------------------------
+  const int n_rows = DQ ? a.sq : a.sk;             // row entities
+  const int n_rt = (n_rows + C::BM - 1) / C::BM;
+  const int nh_rows = DQ ? a.nh : a.nh / a.group;  // heads the rows belong to
+  const int bh = blockIdx.x / n_rt, rt = blockIdx.x % n_rt;
+  const int b = bh / nh_rows, hr = bh % nh_rows;   // query head (DQ) or K/V head (DKDV)
+  const int hk = DQ ? hr / a.group : hr;
+  const int r0 = rt * C::BM;
+  const int wr0 = r0 + 32 * w;
+  const int row = min(wr0 + c, n_rows - 1);        // this lane's row (clamped)
+  const bool wave_idle = wr0 >= n_rows;
+
+  const int64_t q_row_b = a.q_si * 2, k_row_b = a.k_si * 2;
+
+  // ---- the wave's rows in registers: B operands, lane (c, g) holds
+  // R[row c][16t + 8g .. +7] -------------------------------------------------------
+  bf16x8 r1[D / 16], r2[D / 16];
+  {
+    const bf16* p1 = DQ ? (const bf16*)a.q[0] + b * a.q_sb + hr * a.q_sh
+                        : (const bf16*)a.k[0] + b * a.k_sb + hk * a.k_sh;
+    const bf16* p2 = DQ ? (const bf16*)g2.dout + b * a.q_sb + hr * a.q_sh
+                        : (const bf16*)a.v + b * a.v_sb + hk * a.v_sh;
+    const int64_t rb = DQ ? q_row_b : k_row_b;
+    const int64_t off = (int64_t)row * rb;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      r1[t] = *(const bf16x8*)((const char*)p1 + off + 32 * t + 16 * g);
+      r2[t] = *(const bf16x8*)((const char*)p2 + off + 32 * t + 16 * g);
+    }
+  }
+
+  // ---- per-row statistics and intervals ------------------------------------------
+  float lse2_row = 0.0f, delta_row = 0.0f;  // DQ: this lane's query
+  int lane_lo, lane_hi;                     // DQ: keys of the query; DKDV: queries of the key
+  if constexpr (DQ) {
+    // D = dO . O over the row; the lane holds half of the head dimension
+    const bf16* po = (const bf16*)g2.o + b * a.q_sb + hr * a.q_sh + (int64_t)row * a.q_si;
+    float part = 0.0f;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      const bf16x8 ov = *(const bf16x8*)(po + 16 * t + 8 * g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf((float)r2[t][e], (float)ov[e], part);
+    }
+    delta_row = part + __shfl_xor(part, 32);
+    const int64_t li = b * a.lse_sb + hr * a.lse_sh + row;
+    if (g == 0 && wr0 + c < a.sq) g2.delta[li] = delta_row;
+    const float l = a.lse[0][li];
+    lse2_row = l == kNegInf ? __builtin_inff() : l * kLog2e;  // no key: every p is 0
+    key_interval(a, b, row, lane_lo, lane_hi);
+  } else {
+    query_interval(a, b, row, lane_lo, lane_hi);
+  }
+
+  // streamed range of the work-group and of this wave (union over rows)
+  int lo_first, hi_first, lo_last, hi_last, w_lo_min, w_hi_min, w_lo_max, w_hi_max;
+  auto ivl = [&](int x, int& lo, int& hi) {
+    if constexpr (DQ) key_interval(a, b, x, lo, hi);
+    else query_interval(a, b, x, lo, hi);
+  };
+  ivl(r0, lo_first, hi_first);
+  ivl(min(r0 + C::BM, n_rows) - 1, lo_last, hi_last);
+  ivl(min(wr0, n_rows - 1), w_lo_min, w_hi_min);
+  ivl(max(min(wr0 + 31, n_rows - 1), min(wr0, n_rows - 1)), w_lo_max, w_hi_max);
+  const int t_lo = lo_first / BN;
+  const int t_hi = hi_last >= lo_first ? (hi_last + BN) / BN : t_lo;
+  const int n_t = t_hi - t_lo;
+  // DKDV visits the query tiles of every query head of the group
+  const int n_heads = DQ ? 1 : a.group;
+  const int n_it = n_t * n_heads;
+
+  float alibi_l2 = 0.0f;
+  if constexpr (C::MOD == MOD_ALIBI) {
+    if constexpr (DQ) alibi_l2 = alibi_slope_log2(a, hr);
+  }
+
+  // ---- tile loads: global -> LDS ----------------------------------------------------
+  int t_off[C::CH];
+  const int64_t s_row_b = DQ ? k_row_b : q_row_b;  // streamed tensors' row stride
+#pragma unroll
+  for (int i = 0; i < C::CH; ++i) {
+    const int q = (i * C::NW + w) * 64 + lane;
+    const int rr = q / 8, phys = q % 8;
+    t_off[i] = rr * (int)s_row_b + 16 * (phys ^ C::swz(rr));
+  }
+  const int n_s = DQ ? a.sk : a.sq;  // streamed entities
+  const int64_t s_span = n_s > 0 ? (int64_t)(n_s - 1) * s_row_b + D * 2 : 0;
+  float st_lse = 0.0f, st_del = 0.0f;  // DKDV: one entry's statistics, staged through registers
+  auto tile_coords = [&](int it, int& head, int& tile) {
+    head = DQ ? hr : hk * a.group + it / max(n_t, 1);
+    tile = t_lo + (DQ ? it : it % max(n_t, 1));
+  };
+  auto load_tile = [&](int it, int stage) {
+    int head, tile;
+    tile_coords(it, head, tile);
+    const int64_t e0 = (int64_t)tile * BN;
+    const char* b1;
+    const char* b2;
+    if constexpr (DQ) {
+      b1 = (const char*)((const bf16*)a.k[0] + b * a.k_sb + hk * a.k_sh);
+      b2 = (const char*)((const bf16*)a.v + b * a.v_sb + hk * a.v_sh);
+    } else {
+      b1 = (const char*)((const bf16*)a.q[0] + b * a.q_sb + head * a.q_sh);
+      b2 = (const char*)((const bf16*)g2.dout + b * a.q_sb + head * a.q_sh);
+    }
+    bf16* ts = lds + stage * C::STAGE;
+    const __amdgpu_buffer_rsrc_t rs1 = make_rsrc(b1 + e0 * s_row_b, s_span - e0 * s_row_b);
+    const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(b2 + e0 * s_row_b, s_span - e0 * s_row_b);
+#pragma unroll
+    for (int i = 0; i < C::CH; ++i) lds_load16(rs1, ts + (i * C::NW + w) * 512, t_off[i]);
+#pragma unroll
+    for (int i = 0; i < C::CH; ++i) lds_load16(rs2, ts + C::T_ELEMS + (i * C::NW + w) * 512, t_off[i]);
+    if constexpr (!DQ) {
+      if (tid < BN) {
+        const int qi = (int)e0 + tid;
+        const int64_t li = b * a.lse_sb + head * a.lse_sh + qi;
+        const float l = qi < a.sq ? a.lse[0][li] : kNegInf;
+        st_lse = l == kNegInf ? __builtin_inff() : l * kLog2e;
+        st_del = qi < a.sq ? g2.delta[li] : 0.0f;
+      }
+    }
+  };
+  auto store_stats = [&](int stage) {
+    if constexpr (!DQ) {
+      if (tid < BN) {
+        stat[stage][0][tid] = st_lse;
+        stat[stage][1][tid] = st_del;
+      }
+    }
+  };
+  auto sync_all = [&]() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  // LDS offsets of this lane's reads.  Row reads (A operands of X and Y):
+  // row 32kb + c, logical chunk 2t + g.
+  int rd[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) rd[t] = c * D + 8 * ((2 * t + g) ^ C::swz(c));
+  // Transposed reads (A operands of the accumulations): lane i of a 16-lane
+  // block points at row i/4 of a 4-entry group and 4 columns 4*(i%4) of the
+  // block's 16; rows 8m + tr_row share tr_row's swizzle.
+  const int tr_row = 4 * g + ((c & 15) >> 2);
+  int tr[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int d = 32 * db + 16 * (c >> 4) + 4 * (c & 3);
+    tr[db] = tr_row * D + 8 * ((d >> 3) ^ C::swz(tr_row)) + (d & 7);
+  }
+
+  f32x16 acc1[D / 32], acc2[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    acc1[db] = f32x16{};
+    acc2[db] = f32x16{};
+  }
+
+  // A operands of an accumulation from tensor base `tb` (LDS byte address)
+  // for entry half kb: [db][h2]
+  auto read_tr = [&](uint32_t tb, int kb, bf16x8 (&op)[D / 32][2]) {
+    u32x2 raw[D / 32 * 4];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const uint32_t ad = tb + 2 * tr[db];
+      u32x2* r = raw + 4 * db;
+      if (kb == 0)
+        ds_read_tr4<0, 16 * D, 32 * D, 48 * D>(ad, r[0], r[1], r[2], r[3]);
+      else
+        ds_read_tr4<64 * D, 80 * D, 96 * D, 112 * D>(ad, r[0], r[1], r[2], r[3]);
+    }
+    lds_fence(raw);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const u32x2 lo = raw[4 * db + 2 * h2], hi = raw[4 * db + 2 * h2 + 1];
+        op[db][h2] = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
+      }
+  };
+
+  auto compute_tile = [&](int it, int stage, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    int head, tile;
+    tile_coords(it, head, tile);
+    const int e0 = tile * BN;
+    const bf16* t1 = lds + stage * C::STAGE;
+    const bf16* t2 = t1 + C::T_ELEMS;
+    float sl = alibi_l2;
+    if constexpr (C::MOD == MOD_ALIBI && !DQ) sl = alibi_slope_log2(a, head);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 x = f32x16{}, y = f32x16{};
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        const bf16x8 a1 = *(const bf16x8*)(t1 + rd[t] + 32 * kb * D);
+        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, r1[t], x, 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        const bf16x8 a2 = *(const bf16x8*)(t2 + rd[t] + 32 * kb * D);
+        y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, r2[t], y, 0, 0, 0);
+      }
+      // streamed entity of register 0 in this lane; register r adds acc_row(r)
+      const int eb = e0 + 32 * kb + 4 * g;
+      float lse4[16], del4[16];
+      if constexpr (!DQ) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const f32x4 lv = *(const f32x4*)&stat[stage][0][32 * kb + 4 * g + 8 * m];
+          const f32x4 dv = *(const f32x4*)&stat[stage][1][32 * kb + 4 * g + 8 * m];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lse4[4 * m + e] = lv[e];
+            del4[4 * m + e] = dv[e];
+          }
+        }
+      }
+      f32x16 ds, pp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ent = eb + acc_row(r);
+        const int qi = DQ ? row : ent, kj = DQ ? ent : row;
+        float s = x[r] * a.scale_log2;
+        float dmod = 1.0f;
+        if constexpr (C::MOD == MOD_ALIBI) s -= sl * __builtin_fabsf((float)(qi - kj));
+        if constexpr (C::MOD == MOD_SOFTCAP) {
+          s = softcap_log2(a, x[r]);
+          const float th = s * (1.0f / a.softcap_log2);
+          dmod = 1.0f - th * th;
+        }
+        const float l2 = DQ ? lse2_row : lse4[r];
+        const float dl = DQ ? delta_row : del4[r];
+        float p = fast_exp2(s - l2);
+        if constexpr (MASKED) p = (ent >= lane_lo && ent <= lane_hi) ? p : 0.0f;
+        pp[r] = p;
+        ds[r] = p * (y[r] - dl) * dmod;
+      }
+      // B operands: 16-entry steps 2kb and 2kb + 1 in the permuted order
+      bf16x8 pds[2], ppk[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        f32x8 v1, v2;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          v1[e] = ds[8 * h2 + e];
+          v2[e] = pp[8 * h2 + e];
+        }
+        pds[h2] = __builtin_convertvector(v1, bf16x8);
+        ppk[h2] = __builtin_convertvector(v2, bf16x8);
+      }
+      bf16x8 op1[D / 32][2];
+      read_tr(lds_addr(t1), kb, op1);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+          acc1[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op1[db][h2], pds[h2], acc1[db], 0, 0, 0);
+      if constexpr (!DQ) {
+        bf16x8 op2[D / 32][2];
+        read_tr(lds_addr(t2), kb, op2);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2)
+            acc2[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op2[db][h2], ppk[h2], acc2[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- main loop: two LDS stages, the next tile loads while this one computes
+  if (n_it > 0) {
+    load_tile(0, 0);
+    store_stats(0);
+    sync_all();
+  }
+  for (int it = 0; it < n_it; ++it) {
+    const int stage = it & 1;
+    const bool next = it + 1 < n_it;
+    if (next) load_tile(it + 1, stage ^ 1);
+    int head, tile;
+    tile_coords(it, head, tile);
+    const int e0 = tile * BN, e1 = e0 + BN - 1;
+    const bool empty = wave_idle || e0 > w_hi_max || e1 < w_lo_min;
+    const bool full = e0 >= w_lo_max && e1 <= w_hi_min;
+    if (!empty) {
+      if (full)
+        compute_tile(it, stage, std::integral_constant<bool, false>{});
+      else
+        compute_tile(it, stage, std::integral_constant<bool, true>{});
+    }
+    if (next) {
+      store_stats(stage ^ 1);
+      sync_all();
+    }
+  }
+
+  // ---- epilogue: lane = row, registers = head dimension --------------------------
+  if (wr0 + c >= n_rows) return;
+  const float sc = a.scale_log2 * kLn2;  // scale
+  bf16* o1;
+  bf16* o2 = nullptr;
+  if constexpr (DQ) {
+    o1 = (bf16*)g2.dq + b * a.q_sb + hr * a.q_sh + (int64_t)row * a.q_si;
+  } else {
+    o1 = (bf16*)g2.dk + b * a.k_sb + hk * a.k_sh + (int64_t)row * a.k_si;
+    o2 = (bf16*)g2.dv + b * a.v_sb + hk * a.v_sh + (int64_t)row * a.v_si;
+  }
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * db + 8 * r4 + 4 * g;
+      const bf16x4 v1 = {(bf16)(acc1[db][4 * r4] * sc), (bf16)(acc1[db][4 * r4 + 1] * sc),
+                         (bf16)(acc1[db][4 * r4 + 2] * sc), (bf16)(acc1[db][4 * r4 + 3] * sc)};
+      *(bf16x4*)(o1 + d) = v1;
+      if constexpr (!DQ) {
+        const bf16x4 v2 = {(bf16)acc2[db][4 * r4], (bf16)acc2[db][4 * r4 + 1],
+                           (bf16)acc2[db][4 * r4 + 2], (bf16)acc2[db][4 * r4 + 3]};
+        *(bf16x4*)(o2 + d) = v2;
+      }
+    }
+}
+
+}  // namespace fl

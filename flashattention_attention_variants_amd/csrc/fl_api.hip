@@ -93,6 +93,66 @@ int64_t decode_workspace(int B, int H_q, int S_q, int D, int n_split) {
   return o_bytes + ((int64_t)n_split * rows * 4 + 15) / 16 * 16;
 }
 
+// Validation of fl_attn_params shared by the forward and the backward.
+fl_status check_params(const fl_attn_params* p, int S_q, int S_k) {
+  if (p->variant < FL_VANILLA || p->variant > FL_DOCUMENT) return FL_ERR_PARAM;
+  if (!isfinite(p->scale)) return FL_ERR_PARAM;
+  // the mask in force: the variant's own, or one composed with a score
+  // modification (vanilla, ALiBi, softcap)
+  const bool variant_is_mask = p->variant >= FL_CAUSAL;
+  if (p->mask != FL_VANILLA && (variant_is_mask || p->mask < FL_CAUSAL || p->mask > FL_DOCUMENT))
+    return FL_ERR_PARAM;
+  const int mask = variant_is_mask ? p->variant : p->mask;
+  if (mask != FL_VANILLA && S_q != S_k) return FL_ERR_SHAPE;
+  if (p->variant == FL_SOFTCAP && !(p->softcap > 0.0f && isfinite(p->softcap))) return FL_ERR_PARAM;
+  if (p->variant == FL_ALIBI && !(p->alibi_max_bias >= 0.0f && isfinite(p->alibi_max_bias)))
+    return FL_ERR_PARAM;
+  if (mask == FL_SLIDING_WINDOW && p->window < 1) return FL_ERR_PARAM;
+  if (mask == FL_PREFIX_LM && p->prefix < 0) return FL_ERR_PARAM;
+  if (mask == FL_DOCUMENT) {
+    if (p->n_docs < 1) return FL_ERR_PARAM;
+    if (!p->doc_offsets) return FL_ERR_NULL;
+  }
+  return FL_OK;
+}
+
+// Score modification (returned) and key intervals of a variant.
+int variant_args(const fl_attn_params* p, int S_k, KernelArgs& a) {
+  int mod = MOD_NONE;
+  const int mask = p->variant >= FL_CAUSAL ? p->variant : p->mask;
+  if (p->variant == FL_ALIBI) {
+    mod = MOD_ALIBI;
+    a.alibi_max_bias = p->alibi_max_bias;
+  } else if (p->variant == FL_SOFTCAP) {
+    mod = MOD_SOFTCAP;
+    a.softcap_arg = 2.0f * p->scale * kLog2e / p->softcap;
+    a.softcap_log2 = p->softcap * kLog2e;
+  }
+  switch (mask) {
+    case FL_CAUSAL:
+      a.iv_kind = IV_CAUSAL;
+      a.heavy_first = 1;
+      break;
+    case FL_SLIDING_WINDOW:
+      a.iv_kind = p->window_causal ? IV_WINDOW_CAUSAL : IV_WINDOW_TWO_SIDED;
+      a.window = p->window > S_k + 1 ? S_k + 1 : p->window;  // wider windows change nothing
+      break;
+    case FL_PREFIX_LM:
+      a.iv_kind = IV_PREFIX;
+      a.prefix = p->prefix > S_k ? S_k : p->prefix;
+      a.heavy_first = 1;
+      break;
+    case FL_DOCUMENT:
+      a.iv_kind = IV_DOCUMENT;
+      a.n_docs = p->n_docs;
+      a.doc_offsets = p->doc_offsets;
+      break;
+    default:
+      break;
+  }
+  return mod;
+}
+
 }  // namespace
 
 extern "C" {
@@ -120,24 +180,8 @@ fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* b
   if (H_q % H_kv) return FL_ERR_SHAPE;
   if (S_q > kMaxSeq || S_k > kMaxSeq) return FL_ERR_SHAPE;
   if (dtype != FL_BF16 && dtype != FL_F32) return FL_ERR_UNSUPPORTED;
-  if (p->variant < FL_VANILLA || p->variant > FL_DOCUMENT) return FL_ERR_PARAM;
-  if (!isfinite(p->scale)) return FL_ERR_PARAM;
-  // the mask in force: the variant's own, or one composed with a score
-  // modification (vanilla, ALiBi, softcap)
-  const bool variant_is_mask = p->variant >= FL_CAUSAL;
-  if (p->mask != FL_VANILLA && (variant_is_mask || p->mask < FL_CAUSAL || p->mask > FL_DOCUMENT))
-    return FL_ERR_PARAM;
-  const int mask = variant_is_mask ? p->variant : p->mask;
-  if (mask != FL_VANILLA && S_q != S_k) return FL_ERR_SHAPE;
-  if (p->variant == FL_SOFTCAP && !(p->softcap > 0.0f && isfinite(p->softcap))) return FL_ERR_PARAM;
-  if (p->variant == FL_ALIBI && !(p->alibi_max_bias >= 0.0f && isfinite(p->alibi_max_bias)))
-    return FL_ERR_PARAM;
-  if (mask == FL_SLIDING_WINDOW && p->window < 1) return FL_ERR_PARAM;
-  if (mask == FL_PREFIX_LM && p->prefix < 0) return FL_ERR_PARAM;
-  if (mask == FL_DOCUMENT) {
-    if (p->n_docs < 1) return FL_ERR_PARAM;
-    if (!p->doc_offsets) return FL_ERR_NULL;
-  }
+  const fl_status pv = check_params(p, S_q, S_k);
+  if (pv != FL_OK) return pv;
   if (dtype == FL_BF16 && D != 64) return FL_ERR_UNSUPPORTED;
   if (dtype == FL_F32 && D != 32 && D != 64 && D != 128) return FL_ERR_UNSUPPORTED;
   if ((int64_t)B * H_q * S_q == 0) return FL_OK;  // no output element
@@ -170,37 +214,7 @@ fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* b
   a.sq = S_q;
   a.sk = S_k;
   a.scale_log2 = p->scale * kLog2e;
-  int mod = MOD_NONE;
-  if (p->variant == FL_ALIBI) {
-    mod = MOD_ALIBI;
-    a.alibi_max_bias = p->alibi_max_bias;
-  } else if (p->variant == FL_SOFTCAP) {
-    mod = MOD_SOFTCAP;
-    a.softcap_arg = 2.0f * p->scale * kLog2e / p->softcap;
-    a.softcap_log2 = p->softcap * kLog2e;
-  }
-  switch (mask) {
-    case FL_CAUSAL:
-      a.iv_kind = IV_CAUSAL;
-      a.heavy_first = 1;
-      break;
-    case FL_SLIDING_WINDOW:
-      a.iv_kind = p->window_causal ? IV_WINDOW_CAUSAL : IV_WINDOW_TWO_SIDED;
-      a.window = p->window > S_k + 1 ? S_k + 1 : p->window;  // wider windows change nothing
-      break;
-    case FL_PREFIX_LM:
-      a.iv_kind = IV_PREFIX;
-      a.prefix = p->prefix > S_k ? S_k : p->prefix;
-      a.heavy_first = 1;
-      break;
-    case FL_DOCUMENT:
-      a.iv_kind = IV_DOCUMENT;
-      a.n_docs = p->n_docs;
-      a.doc_offsets = p->doc_offsets;
-      break;
-    default:
-      break;
-  }
+  int mod = variant_args(p, S_k, a);
   a.head_major = a.iv_kind == IV_FULL;
   hipStream_t st = (hipStream_t)stream;
   if (dtype == FL_F32) {
@@ -504,6 +518,62 @@ fl_status fl_attn_merge(const float* o_parts, const float* lse_parts, void* o, f
     return FL_ERR_ALIGN;
   return launch_status(launch_merge(o_parts, lse_parts, n_parts, n_rows, D, o,
                                     out_dtype == FL_BF16, lse, (hipStream_t)stream));
+}
+
+fl_status fl_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                      const float* lse, void* dq, void* dk, void* dv, float* workspace, int B,
+                      int H_q, int H_kv, int S_q, int S_k, int D, fl_dtype dtype,
+                      const fl_attn_params* p, void* stream) {
+  if (!p) return FL_ERR_NULL;
+  if (B < 0 || H_q < 1 || H_kv < 1 || S_q < 0 || S_k < 0 || D < 1) return FL_ERR_SHAPE;
+  if (H_q % H_kv) return FL_ERR_SHAPE;
+  if (S_q > kMaxSeq || S_k > kMaxSeq) return FL_ERR_SHAPE;
+  if (dtype != FL_BF16 || D != 64) return FL_ERR_UNSUPPORTED;
+  const fl_status pv = check_params(p, S_q, S_k);
+  if (pv != FL_OK) return pv;
+  const bool no_q = (int64_t)B * H_q * S_q == 0, no_k = (int64_t)B * H_kv * S_k == 0;
+  if (no_q && no_k) return FL_OK;
+  if ((!no_k && (!k || !v || !dk || !dv)) || (!no_q && (!q || !o || !d_o || !lse || !dq)) ||
+      (!no_q && !no_k && !workspace))
+    return FL_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(d_o, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, 4))
+    return FL_ERR_ALIGN;
+  if (!span_ok(S_k, D, D) || !span_ok(S_q, D, D)) return FL_ERR_SHAPE;
+  hipStream_t st = (hipStream_t)stream;
+
+  KernelArgs a;
+  init_args(a);
+  a.q[0] = q;
+  a.k[0] = k;
+  a.v = v;
+  a.lse[0] = const_cast<float*>(lse);
+  bhsd(H_q, S_q, D, a.q_sb, a.q_sh, a.q_si);
+  bhsd(H_kv, S_k, D, a.k_sb, a.k_sh, a.k_si);
+  bhsd(H_kv, S_k, D, a.v_sb, a.v_sh, a.v_si);
+  bhsd(H_q, S_q, D, a.o_sb, a.o_sh, a.o_si);
+  a.lse_sh = S_q;
+  a.lse_sb = (int64_t)H_q * S_q;
+  a.nb = B;
+  a.nh = H_q;
+  a.alibi_nh = H_q;
+  a.group = H_q / H_kv;
+  a.sq = S_q;
+  a.sk = S_k;
+  a.scale_log2 = p->scale * kLog2e;
+  const int mod = variant_args(p, S_k, a);
+  const int64_t rows_q = (int64_t)B * H_q * ((S_q + 127) / 128);
+  const int64_t rows_k = (int64_t)B * H_kv * ((S_k + 127) / 128);
+  if (rows_q > kMaxGrid || rows_k > kMaxGrid) return FL_ERR_SHAPE;
+  BwdArgs g;
+  g.o = o;
+  g.dout = d_o;
+  g.dq = dq;
+  g.dk = dk;
+  g.dv = dv;
+  g.delta = workspace;
+  return launch_status(launch_bwd_bf16(a, g, mod, st));
 }
 
 }  // extern "C"

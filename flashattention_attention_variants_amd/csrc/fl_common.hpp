@@ -85,6 +85,17 @@ struct KernelArgs {
   float* lse_part;
 };
 
+// Tensors of the backward beyond the forward's arguments; all [B, H, S, D]
+// with the strides of q (o, dout, dq) or of k (dk, dv).
+struct BwdArgs {
+  const void* o;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // [B, H_q, S_q]: written by the dQ launch, read by the dK, dV launch
+};
+
 // Key interval [lo, hi] of query i, clamped to [0, S_k-1] (empty: lo > hi).
 __device__ __forceinline__ void key_interval(const KernelArgs& a, int b, int i, int& lo,
                                              int& hi) {
@@ -124,6 +135,48 @@ __device__ __forceinline__ void key_interval(const KernelArgs& a, int b, int i, 
   }
   lo = lo < 0 ? 0 : lo;
   hi = hi > a.sk - 1 ? a.sk - 1 : hi;
+}
+
+// Queries that may see key j, [lo, hi] clamped to [0, S_q-1] (empty: lo > hi):
+// every interval kind has both ends of [lo(i), hi(i)] non-decreasing in i,
+// so {i : lo(i) <= j <= hi(i)} is one run of queries.
+__device__ __forceinline__ void query_interval(const KernelArgs& a, int b, int j, int& lo,
+                                               int& hi) {
+  switch (a.iv_kind) {
+    case IV_CAUSAL:
+      lo = j;
+      hi = a.sq - 1;
+      break;
+    case IV_WINDOW_CAUSAL:
+      lo = j;
+      hi = j + a.window - 1;
+      break;
+    case IV_WINDOW_TWO_SIDED:
+      lo = j - a.window + 1;
+      hi = j + a.window - 1;
+      break;
+    case IV_PREFIX:
+      lo = j < a.prefix ? 0 : j;
+      hi = a.sq - 1;
+      break;
+    case IV_DOCUMENT: {
+      const int32_t* off = a.doc_offsets + (int64_t)b * (a.n_docs + 1);
+      int dlo = 0, dhi = a.n_docs - 1;
+      while (dlo < dhi) {
+        const int mid = (dlo + dhi + 1) >> 1;
+        if (off[mid] <= j) dlo = mid; else dhi = mid - 1;
+      }
+      lo = off[dlo];
+      hi = off[dlo + 1] - 1;
+      break;
+    }
+    default:
+      lo = 0;
+      hi = a.sq - 1;
+      break;
+  }
+  lo = lo < 0 ? 0 : lo;
+  hi = hi > a.sq - 1 ? a.sq - 1 : hi;
 }
 
 // Work-group id -> (b*H + h, query tile).  Work-groups are dealt to the 8

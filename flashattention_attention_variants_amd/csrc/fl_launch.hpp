@@ -28,6 +28,10 @@ int decode_rows_per_wg();  // packed query rows per decode work-group
 hipError_t launch_merge(const float* o_part, const float* lse_part, int n_parts, int64_t n_rows,
                         int D, void* o, bool out_bf16, float* lse, hipStream_t st);
 
+// bf16 attention backward, D = 64 (attn_bwd.hpp): the dQ launch, then the
+// dK, dV launch.
+hipError_t launch_bwd_bf16(const KernelArgs& a, const BwdArgs& g, int mod, hipStream_t st);
+
 // float32 path: (dqk, dv, ns, mod) as built in inst_f32.hip.
 hipError_t launch_f32(const KernelArgs& a, int dqk, int dv, int ns, int mod, hipStream_t st);
 

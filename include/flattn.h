@@ -241,6 +241,32 @@ int fl_attn_decode_num_splits(int B, int H_q, int H_kv, int S_q, int max_seqlen,
 fl_status fl_attn_merge(const float* o_parts, const float* lse_parts, void* o, float* lse,
                         int n_parts, int64_t n_rows, int D, fl_dtype out_dtype, void* stream);
 
+/*
+ * Backward of fl_attn_fwd: the gradients of a loss L with dO = dL/dO,
+ *   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO,
+ *   dS = P * (dO V^T - D) * mod',  D_i = sum_d dO_id O_id,
+ * where P is recomputed from the scores and the saved LSE (never stored)
+ * and mod' is the derivative of the score modification (1 for vanilla and
+ * ALiBi, 1 - tanh^2(s / softcap) for softcap).  The pages name training as
+ * future work (gist.science explainer, "Significance and Claims";
+ * papers.lqhl.me wiki, "局限与 Future Work"); this is the plain gradient of
+ * the forward above.
+ *   q, k, v, params   as given to fl_attn_fwd (no bias)
+ *   o, lse            its outputs: o [B, H_q, S_q, D], lse [B, H_q, S_q] float32
+ *   d_o               [B, H_q, S_q, D], the gradient of the loss w.r.t. o
+ *   dq                [B, H_q, S_q, D] output
+ *   dk, dv            [B, H_kv, S_k, D] outputs (query heads of a group add
+ *                     into their K/V head)
+ *   workspace         device float32 [B, H_q, S_q] (16 KiB per 4096 rows):
+ *                     holds D between the two kernels the call enqueues
+ * FL_BF16 with D = 64 only; every variant and composed mask of
+ * fl_attn_fwd; positional masks need S_q == S_k.  Errors as fl_attn_fwd.
+ */
+fl_status fl_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                      const float* lse, void* dq, void* dk, void* dv, float* workspace, int B,
+                      int H_q, int H_kv, int S_q, int S_k, int D, fl_dtype dtype,
+                      const fl_attn_params* params, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* fl_status_str(fl_status status);
 

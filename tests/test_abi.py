@@ -192,3 +192,21 @@ def test_merge_validation(lib):
     assert f(op=None) == api.FL_ERR_NULL
     assert f(lse=P(0x10002)) == api.FL_ERR_ALIGN
     assert f(rows=0, op=None, lp=None, o=None) == api.FL_OK
+
+
+def test_bwd_validation(lib):
+    f = lambda p=None, **kw: lib.fl_attn_bwd(
+        *[kw.get(n, FAKE) for n in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "ws")],
+        kw.get("B", 1), kw.get("Hq", 2), kw.get("Hkv", 2), kw.get("Sq", 8), kw.get("Sk", 8),
+        kw.get("D", 64), kw.get("dt", api.FL_BF16), None if p is None else ctypes.byref(p), None)
+    assert f() == api.FL_ERR_NULL
+    assert f(params(), ws=None) == api.FL_ERR_NULL
+    assert f(params(), do=None) == api.FL_ERR_NULL
+    assert f(params(), D=128) == api.FL_ERR_UNSUPPORTED
+    assert f(params(), dt=api.FL_F32) == api.FL_ERR_UNSUPPORTED
+    assert f(params(), Hq=3) == api.FL_ERR_SHAPE
+    assert f(params(variant=3), Sk=16) == api.FL_ERR_SHAPE
+    assert f(params(variant=2, softcap=0.0)) == api.FL_ERR_PARAM
+    assert f(params(variant=1, mask=2)) == api.FL_ERR_PARAM
+    assert f(params(), dk=MISALIGNED) == api.FL_ERR_ALIGN
+    assert f(params(), B=0, q=None, k=None, v=None) == api.FL_OK
