@@ -7,8 +7,9 @@ resident in HBM before timing).  ``value`` is the useful TFLOP/s of the whole
 step; per-variant figures, the roofline of the dominant kernel (live HIP
 event timing on the launch stream) and the CPU oracle's throughput on a
 bounded sample of the same workload are printed on the same JSON line, with
-the decode workload (64 sequences, 32/8 heads, KV caches of 512-8192 tokens)
-timed beside it in GB/s against the HBM roofline.
+the backward of each variant (TFLOP/s of its five products) and the decode
+workload (64 sequences, 32/8 heads, KV caches of 512-8192 tokens, GB/s
+against the HBM roofline) timed beside it.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --report        # extra lines: every workload, every variant
@@ -39,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward measurement printed beside the step")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode measurement printed beside the step")
     ap.add_argument("--report", action="store_true",
@@ -173,6 +176,25 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(t, variants, kws, wl, args.cpu_seconds)
 
+    # backward of each variant on the same workload (dQ launch + dK, dV
+    # launch), timed after the step
+    backward = None
+    if not args.no_backward:
+        d_o = inputs.randn(inputs._gen(wl.seed + 100), tuple(q.shape), wl.dtype).to(dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(B * Hq * S, dtype=torch.float32, device=dev)
+        bper = {}
+        for vname in variants:
+            o_, lse_ = api.fl_attn_fwd(q, k, v, return_lse=True, **kws[vname])
+            bms = timeit(torch, lambda: api.fl_attn_bwd(q, k, v, o_, lse_, d_o, dq=dq, dk=dk, dv=dv,
+                                                        workspace=ws, **kws[vname]))
+            bf = fl[vname] * 5 // 2
+            btf = bf / (bms * 1e-3) / 1e12
+            bper[vname] = dict(ms=round(bms, 4), tflops=round(btf, 1),
+                               frac_bf16_peak=round(btf / flops.PEAK_BF16_TFLOPS, 4))
+        backward = dict(per_variant=bper, useful_flop="2.5 x the forward's (five products)",
+                        timing="best of 3 batches of back-to-back calls, both launches")
+
     # decode against a KV cache (split keys + merge), HBM-bound: its own
     # workload, timed after the step, reported beside it
     decode = None
@@ -201,7 +223,8 @@ def main():
                    "variants": variants, "step": "one forward call per variant",
                    "seed": wl.seed},
         "frac_bf16_peak": round(value / flops.PEAK_BF16_TFLOPS, 4),
-        "roofline": roofline, "cpu_baseline": cpu, "per_variant": per, "decode": decode,
+        "roofline": roofline, "cpu_baseline": cpu, "per_variant": per, "backward": backward,
+        "decode": decode,
     }
     print(json.dumps(line), flush=True)
     if args.report:

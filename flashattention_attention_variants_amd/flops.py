@@ -63,6 +63,13 @@ def attn_bytes(B, Hq, Hkv, S_q, S_k, D, Dv=None, elem=2, lse=False, bias=False) 
     return b
 
 
+def attn_bwd_flops(variant, B, Hq, S_q, S_k, D, **kw) -> int:
+    """Useful FLOPs of the backward: the five products on allowed pairs (S
+    recomputed, dP, dV, dK, dQ), i.e. 2.5 times the forward's two; the dQ
+    launch's second recomputation of S and dP is not counted."""
+    return attn_flops(variant, B, Hq, S_q, S_k, D, **kw) * 5 // 2
+
+
 def diffattn_flops(B, H, S, Dqk, Dv, causal) -> int:
     n = (S * (S + 1) // 2 if causal else S * S) * B * H
     return 2 * 2 * n * (Dqk + Dv)

@@ -57,6 +57,10 @@ def short_name(name: str) -> str:
     return name.replace("void ", "").replace("(fl::KernelArgs)", "")
 
 
+def is_bwd_kernel(name: str) -> bool:
+    return "attn_bwd_kernel" in name
+
+
 def is_decode_kernel(name: str) -> bool:
     """The decode form of the attention kernel and the merge kernel."""
     return "merge_kernel" in name or (name.rstrip().endswith("(fl::KernelArgs)")
@@ -135,7 +139,7 @@ def stats_markdown(dirname: str, bench_json: str, workload: str) -> str:
            "python3 $REPO/bench.py > gpurun_out/bench.json",
            "python -m flashattention_attention_variants_amd.profiling stats-md gpurun_out/kt "
            "--bench gpurun_out/bench.json --workload %s" % workload,
-           "```", "", stats_table(dirname, lambda n: not is_decode_kernel(n)), "",
+           "```", "", stats_table(dirname, lambda n: not is_decode_kernel(n) and not is_bwd_kernel(n)), "",
            "Kernel names: `MfmaCfg<D_qk, D_v, streams, QB, MOD, bias, key mask, gate>` with QB the "
            "32-query blocks per wave and MOD 0 = none (vanilla, causal, window, PrefixLM, document), "
            "1 = ALiBi, 2 = softcap with a running reference, 3 = bounded softcap.  One kernel "
@@ -176,6 +180,33 @@ def decode_stats_markdown(dirname: str, bench_json: str) -> str:
     for k, v in d["per_variant"].items():
         out.append("| %s | %.4f | %.1f | %.1f | %.1f |" % (
             k, v["ms"], v["gbs"], 100 * v["frac_hbm"], v["algorithmic_bytes"] / 1e6))
+    out.append("")
+    return "\n".join(out)
+
+
+def bwd_stats_markdown(dirname: str, bench_json: str, workload: str) -> str:
+    """Kernel-trace summary of the backward launches in the default bench
+    command, with the bench line's backward timing beside it."""
+    b = json.load(open(bench_json))
+    out = ["# attn_bwd_kernel -- %s, all variants" % workload, "",
+           "Kernel trace of the default bench command, which times the backward of each variant "
+           "after the step (a settle, then three batches of back-to-back calls; one call = the dQ "
+           "launch plus the dK, dV launch), one MI355X.", "",
+           "```",
+           "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/kt -o run "
+           "-- python3 $REPO/bench.py",
+           "python3 $REPO/bench.py > gpurun_out/bench.json",
+           "python -m flashattention_attention_variants_amd.profiling bwd-stats-md gpurun_out/kt "
+           "--bench gpurun_out/bench.json --workload %s" % workload,
+           "```", "", stats_table(dirname, is_bwd_kernel), "",
+           "Kernel names: `BwdCfg<role, MOD>` with role 0 = dQ (rows are queries, K and V "
+           "streamed), 1 = dK, dV (rows are keys, Q and dO of every query head of the group "
+           "streamed); MOD 0 = none, 1 = ALiBi, 2 = softcap.  One instance serves every mask.", "",
+           "Bench line of the same build (per call, both launches; useful FLOPs = 2.5 x the "
+           "forward's):", "",
+           "| variant | ms / call | useful TFLOP/s | % of bf16 peak |", "|---|---:|---:|---:|"]
+    for k, v in b["backward"]["per_variant"].items():
+        out.append("| %s | %.4f | %.1f | %.1f |" % (k, v["ms"], v["tflops"], 100 * v["frac_bf16_peak"]))
     out.append("")
     return "\n".join(out)
 
@@ -267,6 +298,10 @@ def main(argv=None):
     sm.add_argument("dir")
     sm.add_argument("--bench", required=True)
     sm.add_argument("--workload", required=True)
+    bm = sub.add_parser("bwd-stats-md")
+    bm.add_argument("dir")
+    bm.add_argument("--bench", required=True)
+    bm.add_argument("--workload", required=True)
     dm = sub.add_parser("decode-stats-md")
     dm.add_argument("dir")
     dm.add_argument("--bench", required=True)
@@ -291,6 +326,11 @@ def main(argv=None):
         path = os.path.join(ROOT, "profiles", "attn_mfma_kernel_%s_counters.md" % a.workload)
         with open(path, "w") as fh:
             fh.write(counters_markdown(a.dirs, list(wl.variants), a.workload, units))
+        print("wrote", path)
+    elif a.cmd == "bwd-stats-md":
+        path = os.path.join(ROOT, "profiles", "attn_bwd_kernel_%s_stats.md" % a.workload)
+        with open(path, "w") as fh:
+            fh.write(bwd_stats_markdown(a.dir, a.bench, a.workload))
         print("wrote", path)
     elif a.cmd == "decode-stats-md":
         b = json.load(open(a.bench))
