@@ -70,7 +70,20 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
   const int n_rows = DQ ? a.sq : a.sk;             // row entities
   const int n_rt = (n_rows + C::BM - 1) / C::BM;
   const int nh_rows = DQ ? a.nh : a.nh / a.group;  // heads the rows belong to
-  const int bh = blockIdx.x / n_rt, rt = blockIdx.x % n_rt;
+  // the forward's XCD-aware order over (head, row tile): the work-groups of
+  // one K/V head share an XCD's L2; under causal-class masks the heaviest
+  // tiles go first (the last query tiles for dQ, the first key tiles for
+  // dK, dV)
+  int bh, rt;
+  {
+    KernelArgs t = a;
+    t.nh = nh_rows;
+    t.group = DQ ? a.group : 1;
+    t.n_qt = n_rt;
+    t.head_major = 0;
+    t.heavy_first = DQ ? a.heavy_first : 0;
+    decode_tile(t, blockIdx.x, bh, rt);
+  }
   const int b = bh / nh_rows, hr = bh % nh_rows;   // query head (DQ) or K/V head (DKDV)
   const int hk = DQ ? hr / a.group : hr;
   const int r0 = rt * C::BM;
