@@ -51,6 +51,11 @@ struct MfmaCfg {
   // decode against a KV cache: packed GQA rows, per-sequence lengths, key
   // splits (see KernelArgs)
   static constexpr bool DEC = DEC_;
+  // gated (Evoformer) launches: a work-group walks rows_per_wg consecutive
+  // batch entries (MSA rows) of one head and query tile, its K/V tile
+  // pipeline running straight across the entries, so the short per-entry
+  // key ranges do not each pay a work-group's start-up
+  static constexpr bool PERSIST = GATE_;
   // waves per work-group; decode rows are few (the G query heads of one K/V
   // head), so its work-groups are narrower and more of them fit a unit
 #ifndef FL_DEC_WAVES
@@ -74,20 +79,26 @@ struct MfmaCfg {
 #ifndef FL_DEC_STAGES
 #define FL_DEC_STAGES 3
 #endif
-  static constexpr int STAGES = DEC ? FL_DEC_STAGES : 3;
+#ifndef FL_EVO_STAGES
+#define FL_EVO_STAGES 3
+#endif
+  static constexpr int STAGES = DEC ? FL_DEC_STAGES : (GATE ? FL_EVO_STAGES : 3);
   __device__ static constexpr int kswz(int row) { return KCPR == 4 ? (row >> 1) & 3 : row & 7; }
   __device__ static constexpr int vswz(int row) { return VCPR == 4 ? 2 * ((row >> 1) & 1) : 2 * (row & 3); }
   static constexpr int KCH = BN * DQK / 8 / (NW * 64);  // 16-byte K chunks per thread
   static constexpr int VCH = BN * DV / 8 / (NW * 64);   // 16-byte V chunks per thread
   // Folded scores: the scale, the running reference and (for ALiBi) the
   // distance penalty all enter the S^T product itself.
-  static constexpr bool FOLD = (MOD == MOD_NONE || MOD == MOD_ALIBI) && !BIAS && !KMASK;
+  // Folded scores: the scale, the running reference, the ALiBi distance
+  // penalty or the key mask all enter the S^T product itself.
+  static constexpr bool FOLD = (MOD == MOD_NONE || MOD == MOD_ALIBI) && !BIAS;
   static constexpr bool ALIBI_FOLD = FOLD && MOD == MOD_ALIBI;
+  static_assert(!(ALIBI_FOLD && KMASK), "ALiBi and the key mask share a folded k-slot");
   // bounded softcap: fixed reference 0
   static constexpr bool SCAPB = MOD == MOD_SOFTCAP_BOUNDED;
   static_assert(!SCAPB || (!BIAS && !KMASK), "bounded softcap takes no bias or key mask");
   static_assert(!DEC || (QB == 1 && NS == 1 && !BIAS && !KMASK && !GATE), "decode form");
-  static_assert(STAGES >= 3 && STAGES <= 6 && (STAGES == 3 || !KMASK), "pipeline depth");
+  static_assert(STAGES >= 3 && STAGES <= 6, "pipeline depth");
   // one stream fits 2 waves per SIMD; two streams need the whole register file
 #ifndef FL_QB1_WAVES
 #define FL_QB1_WAVES 2
@@ -207,15 +218,33 @@ void attn_mfma_kernel(KernelArgs a) {
   const int c = lane & 31, g = lane >> 5;
 
   int bh, qt, split = 0;
+  int b_first = 0, n_rep = 1;  // batch entries this work-group walks
   if constexpr (C::DEC) {
     split = blockIdx.x % a.n_split;
     const int rest = blockIdx.x / a.n_split;
     qt = rest % a.n_qt;
     bh = rest / a.n_qt;
+  } else if constexpr (C::PERSIST) {
+    // Heads of one position are adjacent in memory (a head's row is 64
+    // bytes), so the work-groups of all heads of a batch entry share an
+    // XCD, whose L2 then serves each 128-byte line to both of its heads.
+    const int n_grp = (a.nb + a.rows_per_wg - 1) / a.rows_per_wg;
+    int item = blockIdx.x;  // (row group, query tile, head), head fastest
+    if ((n_grp & 7) == 0) {
+      const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+      const int per = a.nh * a.n_qt;  // items of one row group
+      item = ((slot / per) * 8 + xcd) * per + slot % per;
+    }
+    const int hh = item % a.nh, rest = item / a.nh;
+    qt = rest % a.n_qt;
+    b_first = (rest / a.n_qt) * a.rows_per_wg;
+    n_rep = min(a.rows_per_wg, a.nb - b_first);
+    bh = b_first * a.nh + hh;
   } else {
     decode_tile(a, blockIdx.x, bh, qt);
   }
-  const int b = bh / a.nh, h = bh % a.nh, hk = h / a.group;
+  int b = bh / a.nh;  // the batch entry whose rows are in flight
+  const int h = bh % a.nh, hk = h / a.group;
   const int q0 = qt * C::BM;
   const int qlast = min(q0 + C::BM, a.sq) - 1;
 
@@ -296,25 +325,28 @@ void attn_mfma_kernel(KernelArgs a) {
   // Folded scores: Q is pre-multiplied by scale*log2(e) (one bf16 rounding),
   // so S^T comes out in base-2 units.
   bf16x8 qreg[NS][QB][DQK / 16];
+  auto load_q = [&](int bb) {
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    // rows past S_q read as zeros through the bounds-checked resource
-    const bf16* qh = (const bf16*)a.q[s] + b * a.q_sb + h * a.q_sh;
-    const int64_t q_row_b = a.q_si * 2;
-    const int64_t q_span = (int64_t)(a.sq - 1) * q_row_b + DQK * 2 - (int64_t)wq0 * q_row_b;
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qh + (int64_t)wq0 * a.q_si, q_span);
+    for (int s = 0; s < NS; ++s) {
+      // rows past S_q read as zeros through the bounds-checked resource
+      const bf16* qh = (const bf16*)a.q[s] + bb * a.q_sb + h * a.q_sh;
+      const int64_t q_row_b = a.q_si * 2;
+      const int64_t q_span = (int64_t)(a.sq - 1) * q_row_b + DQK * 2 - (int64_t)wq0 * q_row_b;
+      const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qh + (int64_t)wq0 * a.q_si, q_span);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-      for (int t = 0; t < DQK / 16; ++t) {
-        qreg[s][qb][t] = load16(qrs, (32 * qb + c) * (int)q_row_b + 32 * t + 16 * g);
-        if constexpr (C::FOLD) {
-          f32x8 f = __builtin_convertvector(qreg[s][qb][t], f32x8);
-          qreg[s][qb][t] = __builtin_convertvector(f * a.scale_log2, bf16x8);
+        for (int t = 0; t < DQK / 16; ++t) {
+          qreg[s][qb][t] = load16(qrs, (32 * qb + c) * (int)q_row_b + 32 * t + 16 * g);
+          if constexpr (C::FOLD) {
+            f32x8 f = __builtin_convertvector(qreg[s][qb][t], f32x8);
+            qreg[s][qb][t] = __builtin_convertvector(f * a.scale_log2, bf16x8);
+          }
         }
       }
     }
-  }
+  };
+  load_q(b);
 
   // ---- per-row softmax state -------------------------------------------------
   f32x16 oacc[NS][QB][DV / 32];
@@ -358,15 +390,23 @@ void attn_mfma_kernel(KernelArgs a) {
       bf16 x0, x1, x2;
       split3(-alibi_l2 * (float)(lane_pos[qb] - j0), x0, x1, x2);
       qext[s][qb] = bf16x8{mt, x0, x1, x2, sl0, sl1, sl2, zero};
+    } else if constexpr (C::KMASK) {
+      qext[s][qb] = bf16x8{mt, one, zero, zero, zero, zero, zero, zero};
     } else {
       qext[s][qb] = bf16x8{mt, zero, zero, zero, zero, zero, zero, zero};
     }
   };
-  // key-side operand of key half kb
+  // key-side operand of key half kb.  With a key mask, k-slot 1 carries the
+  // key's additive mask term (0, or -inf for an excluded key) against a
+  // query-side 1, so excluded keys come out of the product at -inf.
+  int cur_stage = 0;  // LDS stage of the tile being consumed
   auto kext = [&](int kb) {
     if constexpr (C::ALIBI_FOLD) {
       const bf16 ck = (bf16)(float)(32 * kb + c);
       return g == 0 ? bf16x8{one, one, one, one, ck, ck, ck, zero} : bf16x8{};
+    } else if constexpr (C::KMASK) {
+      const bf16 km = (bf16)kmadd[cur_stage * BN + 32 * kb + c];
+      return g == 0 ? bf16x8{one, km, zero, zero, zero, zero, zero, zero} : bf16x8{};
     } else {
       return g == 0 ? bf16x8{one, zero, zero, zero, zero, zero, zero, zero} : bf16x8{};
     }
@@ -377,20 +417,23 @@ void attn_mfma_kernel(KernelArgs a) {
     w ^= (u32x4){0x80000000u, 0x80008000u, 0x80008000u, 0x00008000u};
     return __builtin_bit_cast(bf16x8, w);
   };
+  auto reset_state = [&]() {
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      // folded: m = 0 is a valid reference from the start; it moves only
-      // when terms overflow or a row's terms underflow
-      m_run[s][qb] = (C::FOLD || C::SCAPB) ? 0.0f : kNegInf;
-      m_set[s][qb] = false;
-      l_run[s][qb] = 0.0f;
-      qext[s][qb] = bf16x8{};
-      if constexpr (C::FOLD) set_qext(s, qb, 0.0f, 0);
+      for (int qb = 0; qb < QB; ++qb) {
+        // folded: m = 0 is a valid reference from the start; it moves only
+        // when terms overflow or a row's terms underflow
+        m_run[s][qb] = (C::FOLD || C::SCAPB) ? 0.0f : kNegInf;
+        m_set[s][qb] = false;
+        l_run[s][qb] = 0.0f;
+        qext[s][qb] = bf16x8{};
+        if constexpr (C::FOLD) set_qext(s, qb, 0.0f, 0);
 #pragma unroll
-      for (int db = 0; db < DV / 32; ++db) oacc[s][qb][db] = f32x16{};
-    }
+        for (int db = 0; db < DV / 32; ++db) oacc[s][qb][db] = f32x16{};
+      }
+  };
+  reset_state();
 
   // Scores live in base 2.  Modified scores are converted to base-2 units
   // after the product and use a lazy rescale: the running max used in the
@@ -407,11 +450,10 @@ void attn_mfma_kernel(KernelArgs a) {
   // read as zeros.  One load instruction of a wave fills 1 KiB of LDS in lane
   // order, so the swizzled layout is realised by choosing, per lane, which
   // global 16-byte chunk to fetch.
-  const char* kblk[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s)
-    kblk[s] = (const char*)((const bf16*)a.k[s] + b * a.k_sb + hk * a.k_sh);
-  const char* vblk = (const char*)((const bf16*)a.v + b * a.v_sb + hk * a.v_sh);
+  auto kblk = [&](int s, int bb) {
+    return (const char*)((const bf16*)a.k[s] + bb * a.k_sb + hk * a.k_sh);
+  };
+  auto vblk = [&](int bb) { return (const char*)((const bf16*)a.v + bb * a.v_sb + hk * a.v_sh); };
   const int64_t k_row_b = a.k_si * 2, v_row_b = a.v_si * 2;
   // (decode: only the first len rows exist; cache slots past them may hold
   // anything, NaN included, and must not reach even a zero-weighted product)
@@ -433,24 +475,25 @@ void attn_mfma_kernel(KernelArgs a) {
   }
   float kmpre = 0.0f;
 
-  // issue the loads of tile kt into LDS stage `stage`
-  auto load_tile = [&](int kt, int stage) {
+  // issue the loads of tile kt of batch entry bb into LDS stage `stage`
+  auto load_tile = [&](int bb, int kt, int stage) {
     const int64_t j0 = (int64_t)kt * BN;
     if (C::KMASK && tid < BN) {
       const int j = (int)j0 + tid;
-      kmpre = (j < a.sk && (!a.kmask || a.kmask[b * a.km_sb + (int64_t)j * a.km_sj] != 0))
+      kmpre = (j < a.sk && (!a.kmask || a.kmask[bb * a.km_sb + (int64_t)j * a.km_sj] != 0))
                   ? 0.0f
                   : kNegInf;
     }
     bf16* ks = lds + stage * C::STAGE;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(kblk[s] + j0 * k_row_b, k_span - j0 * k_row_b);
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(kblk(s, bb) + j0 * k_row_b, k_span - j0 * k_row_b);
 #pragma unroll
       for (int i = 0; i < C::KCH; ++i)
         lds_load16(rs, ks + s * C::K_ELEMS + (i * C::NW + w) * 512, k_off[i]);
     }
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(vblk + j0 * v_row_b, v_span - j0 * v_row_b);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(vblk(bb) + j0 * v_row_b, v_span - j0 * v_row_b);
 #pragma unroll
     for (int i = 0; i < C::VCH; ++i)
       lds_load16(rs, ks + NS * C::K_ELEMS + (i * C::NW + w) * 512, v_off[i]);
@@ -529,6 +572,7 @@ void attn_mfma_kernel(KernelArgs a) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     constexpr bool FOLDED = decltype(folded_tag)::value;
     constexpr int U = NS * 2 * QB;
+    cur_stage = stage;
     const bf16* ks = lds + stage * C::STAGE;
     const int j0 = kt * BN;
 
@@ -808,39 +852,121 @@ void attn_mfma_kernel(KernelArgs a) {
     const int x = it + kt_start;
     return kt_lo + (x >= n_kt ? x - n_kt : x);
   };
-  if (n_kt > 0) {
-    load_tile(tile_of(0), 0);
-    store_kmask(0);
+  // normalise, combine, gate and store the rows of batch entry b
+  auto finish_row = [&]() {
+    float inv[NS][QB];
+  #pragma unroll
+    for (int s = 0; s < NS; ++s)
+  #pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float l = l_run[s][qb] + __shfl_xor(l_run[s][qb], 32);
+        inv[s][qb] = l > 0.0f ? 1.0f / l : 0.0f;
+        const int qi = wq0 + 32 * qb + c;
+        if (a.lse[s] && g == 0 && qi < a.sq) {
+          const float m = m_run[s][qb];
+          const float lse = l > 0.0f ? (m + __builtin_log2f(l)) * kLn2 : kNegInf;
+          a.lse[s][b * a.lse_sb + h * a.lse_sh + qi] = lse;
+        }
+      }
+
+  #pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qi = wq0 + 32 * qb + c;
+      if (qi >= a.sq) continue;
+      bf16* op = (bf16*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_si;
+      const bf16* gp = C::GATE ? (const bf16*)a.gate + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_si
+                               : nullptr;
+  #pragma unroll
+      for (int db = 0; db < DV / 32; ++db)
+  #pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d = 32 * db + 8 * r4 + 4 * g;
+          float ov[4];
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ov[e] = oacc[0][qb][db][4 * r4 + e] * inv[0][qb];
+            if constexpr (NS == 2) ov[e] -= a.lambda * oacc[1][qb][db][4 * r4 + e] * inv[1][qb];
+          }
+          if constexpr (C::GATE) {
+            const bf16x4 gv = *(const bf16x4*)(gp + d);
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) ov[e] *= sigmoid((float)gv[e]);
+          }
+          const bf16x4 out = {(bf16)ov[0], (bf16)ov[1], (bf16)ov[2], (bf16)ov[3]};
+          *(bf16x4*)(op + d) = out;
+        }
+    }
+  };
+  // the visit: n_kt tiles of each of the n_rep batch entries, in sequence
+  const int n_total = n_rep * n_kt;
+  auto issue = [&](int it, int stage) {
+    if constexpr (C::PERSIST)
+      load_tile(b_first + it / n_kt, tile_of(it % n_kt), stage);
+    else
+      load_tile(b, tile_of(it), stage);
+  };
+  if (n_total > 0) {
+    // the key-mask column of a tile goes to LDS one step after its load
+    // was issued; the prologue stores all but the newest
+    issue(0, 0);
 #pragma unroll
     for (int t = 1; t < AHEAD; ++t)
-      if (t < n_kt) load_tile(tile_of(t), t);
-    sync_tile(min(AHEAD, n_kt) - 1);
+      if (t < n_total) {
+        store_kmask(t - 1);
+        issue(t, t);
+      }
+    // with fewer tiles than the pipeline holds, no iteration stores the last
+    if (n_total < AHEAD) store_kmask(n_total - 1);
+    sync_tile(min(AHEAD, n_total) - 1);
   }
-  for (int it = 0; it < n_kt; ++it) {
-    const int kt = tile_of(it);
+  for (int it = 0; it < n_total; ++it) {
+    const int kt = C::PERSIST ? tile_of(it % n_kt) : tile_of(it);
     const int stage = it % C::STAGES;
-    const bool next = it + 1 < n_kt, next2 = it + AHEAD < n_kt;
+    const bool next = it + 1 < n_total, next2 = it + AHEAD < n_total;
     const int j0 = kt * BN, j1 = j0 + BN - 1;
     const bool empty = wave_idle || j0 > w_hi_max || j1 < w_lo_min;
     const bool full = j0 >= w_lo_max && j1 <= w_hi_min;
-    if (next) store_kmask(stage == C::STAGES - 1 ? 0 : stage + 1);
-    if (next2) load_tile(tile_of(it + AHEAD), stage == 0 ? C::STAGES - 1 : stage - 1);
+    // the newest tile issued so far is it + AHEAD - 1 (if it exists)
+    if (it + AHEAD - 1 < n_total) store_kmask((it + AHEAD - 1) % C::STAGES);
+    if (next2) issue(it + AHEAD, stage == 0 ? C::STAGES - 1 : stage - 1);
     if (!empty) {
       using F = std::integral_constant<bool, false>;
       using T = std::integral_constant<bool, true>;
-      if (!C::FOLD || C::ALIBI_FOLD || need_fold) {
+      if (!C::FOLD || C::ALIBI_FOLD || C::KMASK || need_fold) {
         if (full)
           compute_tile(stage, kt, F{}, T{});
         else
           compute_tile(stage, kt, T{}, T{});
-      } else if constexpr (C::FOLD && !C::ALIBI_FOLD) {
+      } else if constexpr (C::FOLD && !C::ALIBI_FOLD && !C::KMASK) {
         if (full)
           compute_tile(stage, kt, F{}, F{});
         else
           compute_tile(stage, kt, T{}, F{});
       }
     }
-    if (next) sync_tile(min(AHEAD - 1, n_kt - 2 - it));
+    if constexpr (C::PERSIST) {
+      if (it % n_kt == n_kt - 1 && next) {
+        // the entry's last tile: its rows are done; the next entry's first
+        // tiles are already in flight.  (The output stores and the next Q
+        // loads only add to the count the tile wait below allows: loads
+        // return in issue order, so it still cannot pass before the awaited
+        // tile has landed.)
+        finish_row();
+        ++b;
+        reset_state();
+        load_q(b);
+      }
+    }
+    if (next) sync_tile(min(AHEAD - 1, n_total - 2 - it));
+  }
+  if constexpr (C::PERSIST) {
+    // entries left without a tile (no key at all) still write their rows
+    if (n_kt == 0) {
+      for (int r = 1; r < n_rep; ++r) {
+        finish_row();
+        ++b;
+      }
+    }
   }
 
   // ---- epilogue: normalise, combine, gate, store --------------------------------
@@ -869,48 +995,7 @@ void attn_mfma_kernel(KernelArgs a) {
       return;
     }
   }
-  float inv[NS][QB];
-#pragma unroll
-  for (int s = 0; s < NS; ++s)
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float l = l_run[s][qb] + __shfl_xor(l_run[s][qb], 32);
-      inv[s][qb] = l > 0.0f ? 1.0f / l : 0.0f;
-      const int qi = wq0 + 32 * qb + c;
-      if (a.lse[s] && g == 0 && qi < a.sq) {
-        const float m = m_run[s][qb];
-        const float lse = l > 0.0f ? (m + __builtin_log2f(l)) * kLn2 : kNegInf;
-        a.lse[s][b * a.lse_sb + h * a.lse_sh + qi] = lse;
-      }
-    }
-
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qi = wq0 + 32 * qb + c;
-    if (qi >= a.sq) continue;
-    bf16* op = (bf16*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_si;
-    const bf16* gp = C::GATE ? (const bf16*)a.gate + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_si
-                             : nullptr;
-#pragma unroll
-    for (int db = 0; db < DV / 32; ++db)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d = 32 * db + 8 * r4 + 4 * g;
-        float ov[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ov[e] = oacc[0][qb][db][4 * r4 + e] * inv[0][qb];
-          if constexpr (NS == 2) ov[e] -= a.lambda * oacc[1][qb][db][4 * r4 + e] * inv[1][qb];
-        }
-        if constexpr (C::GATE) {
-          const bf16x4 gv = *(const bf16x4*)(gp + d);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ov[e] *= sigmoid((float)gv[e]);
-        }
-        const bf16x4 out = {(bf16)ov[0], (bf16)ov[1], (bf16)ov[2], (bf16)ov[3]};
-        *(bf16x4*)(op + d) = out;
-      }
-  }
+  finish_row();
 }
 
 }  // namespace fl

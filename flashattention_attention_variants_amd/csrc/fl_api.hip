@@ -375,6 +375,15 @@ fl_status fl_evoformer_gated_attn_fwd(const void* q, const void* k, const void* 
   const int qb = L > 128 ? 2 : 1;
   a.n_qt = grid_qtiles(L, mfma_rows_per_wg(qb));
   if ((int64_t)a.n_qt * a.nb * H > kMaxGrid) return FL_ERR_SHAPE;
+  // A work-group may walk several batch entries (MSA rows or columns) of one
+  // head with its tile pipeline running across them.  Measured at the
+  // AlphaFold2 sizes: two entries per work-group help the two-block tiles
+  // of long key ranges (256 residues), one is best for one-block tiles.
+#ifdef FL_EVO_ROWS
+  a.rows_per_wg = FL_EVO_ROWS;
+#else
+  a.rows_per_wg = qb == 2 ? 2 : 1;
+#endif
   return launch_status(launch_evo_bf16(a, C, qb, pair_bias != nullptr, st));
 }
 

@@ -69,6 +69,7 @@ struct KernelArgs {
   int heavy_first;             // schedule the most expensive query tiles first
   int head_major;              // deal a head's query tiles to its XCD consecutively
   int alibi_nh;                // query heads in the ALiBi slope formula
+  int rows_per_wg;             // gated launches: batch entries per work-group
   // Decode against a KV cache.  The rows of K/V head hk are the G*S_new
   // query rows of its G query heads, packed: row r is new token r % S_new of
   // query head hk*G + r / S_new (contiguous in [B, H_q, S_new, D]).  Batch

@@ -7,7 +7,9 @@ namespace fl {
 
 template <class C>
 static hipError_t go(const KernelArgs& a, hipStream_t st) {
-  const int nwg = a.nb * a.nh * a.n_qt;
+  // each work-group walks rows_per_wg batch entries of one head and query tile
+  const int groups = (a.nb + a.rows_per_wg - 1) / a.rows_per_wg;
+  const int nwg = groups * a.nh * a.n_qt;
   (void)hipGetLastError();
   hipLaunchKernelGGL(attn_mfma_kernel<C>, dim3(nwg), dim3(256), 0, st, a);
   return hipGetLastError();
