@@ -38,6 +38,7 @@ namespace fl {
 
 enum BwdRole { BWD_DQ = 0, BWD_DKDV = 1 };
 
+
 template <int ROLE_, int MOD_>
 struct BwdCfg {
   static constexpr int ROLE = ROLE_;
@@ -71,16 +72,16 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
   const int n_rt = (n_rows + C::BM - 1) / C::BM;
   const int nh_rows = DQ ? a.nh : a.nh / a.group;  // heads the rows belong to
   // the forward's XCD-aware order over (head, row tile): the work-groups of
-  // one K/V head share an XCD's L2; under causal-class masks the heaviest
-  // tiles go first (the last query tiles for dQ, the first key tiles for
-  // dK, dV)
+  // one K/V head share an XCD's L2; dense rows go out head by head, and
+  // under causal-class masks the heaviest tiles go first (the last query
+  // tiles for dQ, the first key tiles for dK, dV)
   int bh, rt;
   {
     KernelArgs t = a;
     t.nh = nh_rows;
     t.group = DQ ? a.group : 1;
     t.n_qt = n_rt;
-    t.head_major = 0;
+    t.head_major = a.iv_kind == IV_FULL;
     t.heavy_first = DQ ? a.heavy_first : 0;
     decode_tile(t, blockIdx.x, bh, rt);
   }
@@ -266,9 +267,10 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
     const bf16* t2 = t1 + C::T_ELEMS;
     float sl = alibi_l2;
     if constexpr (C::MOD == MOD_ALIBI && !DQ) sl = alibi_slope_log2(a, head);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 x = f32x16{}, y = f32x16{};
+    // X = T1 R1^T and Y = T2 R2^T of entry half kb
+    auto products = [&](int kb, f32x16& x, f32x16& y) {
+      x = f32x16{};
+      y = f32x16{};
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
         const bf16x8 a1 = *(const bf16x8*)(t1 + rd[t] + 32 * kb * D);
@@ -279,6 +281,13 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
         const bf16x8 a2 = *(const bf16x8*)(t2 + rd[t] + 32 * kb * D);
         y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, r2[t], y, 0, 0, 0);
       }
+    };
+    // (issuing the second half's products before the first half's vector
+    // work measured no faster)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 x, y;
+      products(kb, x, y);
       // streamed entity of register 0 in this lane; register r adds acc_row(r)
       const int eb = e0 + 32 * kb + 4 * g;
       float lse4[16], del4[16];
