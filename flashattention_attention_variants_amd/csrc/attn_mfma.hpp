@@ -180,7 +180,7 @@ __device__ __forceinline__ void lds_fence(u32x2 (&r)[16]) {
 #define FL_SCHED_INTERLEAVE 1
 #endif
 #ifndef FL_SCHED_VALU_PER_MFMA
-#define FL_SCHED_VALU_PER_MFMA 4
+#define FL_SCHED_VALU_PER_MFMA 5
 #endif
 
 // Scheduling shape of one pipeline unit's basic block (the previous unit's
@@ -204,6 +204,22 @@ __device__ __forceinline__ void interleave_hint() {
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
   }
 #endif
+}
+
+#ifndef FL_SCAPB_VALU
+#define FL_SCAPB_VALU 14
+#endif
+// One bounded-softcap unit, a single basic block: the K operand reads, then
+// each matrix instruction (the successor's S^T products, the predecessor's
+// P.V products) followed by a share of this unit's vector work.
+__device__ __forceinline__ void unit_hint_scapb() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, FL_SCAPB_VALU, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <class C>
@@ -521,11 +537,12 @@ void attn_mfma_kernel(KernelArgs a) {
 
   // ---- one key tile: S^T, softmax update, O^T += V^T P^T ---------------------
   // Work units u = (stream s, 32-key half kb, query block qb) run as a
-  // two-stage pipeline: the S^T product of unit u+1 is issued before the
-  // softmax of unit u, so the matrix cores work while the vector ALUs
-  // exponentiate, and P.V of unit u follows its softmax at once so P dies
-  // early.  The running reference of a row never needs a tile-wide maximum,
-  // so the two key halves of a tile are independent units.
+  // three-stage pipeline: while the vector ALUs take the softmax of unit u,
+  // the matrix cores run the S^T product of unit u+1 and the P.V product of
+  // unit u-1, neither of which depends on it.  (P.V of u-1 is accumulated
+  // before u's softmax may rescale the same rows' accumulator.)  The running
+  // reference of a row never needs a tile-wide maximum, so the two key halves
+  // of a tile are independent units.
   bf16x8 kop[DQK / 16];  // K operands of the current (stream, key half)
   auto read_k = [&](const bf16* ks, int s, int kb) {
 #pragma unroll
@@ -640,6 +657,15 @@ void attn_mfma_kernel(KernelArgs a) {
         for (int qb = 0; qb < QB; ++qb) set_qext(s, qb, m_run[s][qb], j0);
     }
     f32x16 sacc[2];  // [pipeline slot]
+    bf16x8 pkp[2];  // P of the previous unit, whose P.V product is still to come
+    auto pv = [&](int s, int qb, const bf16x8 (&p)[2]) {
+#pragma unroll
+      for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+          oacc[s][qb][db] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][h2], p[h2], oacc[s][qb][db], 0, 0, 0);
+    };
     read_k(ks, 0, 0);
     qk(j0, 0, 0, 0, sacc[0], folded_tag);
     // unit u: key half kb = u / (NS*QB), stream s = (u / QB) % NS, block qb = u % QB
@@ -650,6 +676,12 @@ void attn_mfma_kernel(KernelArgs a) {
         const int kb1 = (u + 1) / (NS * QB), s1 = ((u + 1) / QB) % NS, qb1 = (u + 1) % QB;
         if (qb1 == 0) read_k(ks, s1, kb1);
         qk(j0, s1, kb1, qb1, sacc[(u + 1) & 1], folded_tag);
+      }
+      // the previous unit's P.V product, independent of this unit's softmax
+      if (u >= 1) {
+        if ((u - 1) % (NS * QB) == 0) take_v();
+        pv(((u - 1) / QB) % NS, (u - 1) % QB, pkp);
+        if (u - 1 == NS * QB - 1) read_v(1);
       }
       f32x16& sc = sacc[u & 1];
       const int qi = wq0 + 32 * qb + c;
@@ -791,15 +823,12 @@ void attn_mfma_kernel(KernelArgs a) {
       // O^T += V^T P^T over this unit's 32 keys; the V^T operands of a key
       // half are taken at its first unit and the second half's reads are
       // issued after the first half's last product.
-      if (s == 0 && qb == 0) take_v();
-#pragma unroll
-      for (int db = 0; db < DV / 32; ++db)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-          oacc[s][qb][db] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][h2], pk[h2], oacc[s][qb][db], 0, 0, 0);
-      if (kb == 0 && s == NS - 1 && qb == QB - 1) read_v(1);
+      pkp[0] = pk[0];
+      pkp[1] = pk[1];
+      if constexpr (C::SCAPB) unit_hint_scapb();
     }
+    if ((U - 1) % (NS * QB) == 0) take_v();
+    pv(((U - 1) / QB) % NS, (U - 1) % QB, pkp);
   };
 
   // ---- main loop ---------------------------------------------------------------

@@ -237,8 +237,8 @@ fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* b
   const int qb = FL_FORCE_QB;
 #else
   int qb;
-  if (mod == MOD_ALIBI && !bias)
-    qb = 1;  // the folded ALiBi terms do not fit two blocks per wave in registers
+  if (mod == MOD_ALIBI)
+    qb = 1;  // the ALiBi terms do not fit two blocks per wave in registers
   else if (a.iv_kind == IV_FULL)
     qb = wg2 >= 512 ? 2 : 1;
   else if (a.iv_kind == IV_WINDOW_CAUSAL || a.iv_kind == IV_WINDOW_TWO_SIDED)

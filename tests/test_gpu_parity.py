@@ -316,8 +316,11 @@ def evo_small(dtype, N_seq=6, N_res=72, H=4, C=32, seed=80):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("with_bias", [True, False])
-def test_evoformer_row(dtype, with_bias):
-    q, k, v, gate, bias, km = evo_small(dtype)
+@pytest.mark.parametrize("N_res", [72, 200])
+def test_evoformer_row(dtype, with_bias, N_res):
+    # 72 residues: one partial query tile and a partial key tile; 200: two
+    # query tiles (the second partial) and four key tiles of the staged bias
+    q, k, v, gate, bias, km = evo_small(dtype, N_res=N_res)
     pb = bias if with_bias else None
     o = api.fl_evoformer_gated_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), gate.to(DEV),
                                         pair_bias=None if pb is None else pb.to(DEV),
