@@ -712,9 +712,13 @@ void attn_mfma_kernel(KernelArgs a) {
         // scores are recomputed and re-exponentiated.  In a tile without the
         // folded step, every unit after a reference moved is recomputed the
         // same way.  Wave-uniform, rarely taken.
-        const bool has_key = row_hi[qb] >= j0 + 32 * kb && row_lo[qb] <= j0 + 32 * kb + 31 &&
-                             row_lo[qb] <= row_hi[qb];
-        const bool redo = (has_key && l_run[s][qb] + lsum == 0.0f) || !(lsum <= 0x1p64f);
+        // (Every row has all keys of a full tile.  Bitwise operators keep the
+        // test in vector compares, without divergent control flow.)
+        bool has_key = true;
+        if constexpr (MASKED)
+          has_key = (row_hi[qb] >= j0 + 32 * kb) & (row_lo[qb] <= j0 + 32 * kb + 31) &
+                    (row_lo[qb] <= row_hi[qb]);
+        const bool redo = (has_key & (l_run[s][qb] + lsum == 0.0f)) | !(lsum <= 0x1p64f);
         interleave_hint();
         if (__builtin_amdgcn_ballot_w64(redo) || (!FOLDED && need_fold)) {
           f32x16 rs = f32x16{};
