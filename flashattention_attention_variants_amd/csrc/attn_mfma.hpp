@@ -501,18 +501,21 @@ void attn_mfma_kernel(KernelArgs a) {
                   : kNegInf;
     }
     bf16* ks = lds + stage * C::STAGE;
+    // one resource over the whole (b, K/V head) block; the tile's offset
+    // rides in the per-lane offset, which the launcher keeps below 2^31 for
+    // every row up to 63 past S_k
+    const int kt_off = (int)j0 * (int)k_row_b, vt_off = (int)j0 * (int)v_row_b;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const __amdgpu_buffer_rsrc_t rs =
-          make_rsrc(kblk(s, bb) + j0 * k_row_b, k_span - j0 * k_row_b);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(kblk(s, bb), k_span);
 #pragma unroll
       for (int i = 0; i < C::KCH; ++i)
-        lds_load16(rs, ks + s * C::K_ELEMS + (i * C::NW + w) * 512, k_off[i]);
+        lds_load16(rs, ks + s * C::K_ELEMS + (i * C::NW + w) * 512, k_off[i] + kt_off);
     }
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(vblk(bb) + j0 * v_row_b, v_span - j0 * v_row_b);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(vblk(bb), v_span);
 #pragma unroll
     for (int i = 0; i < C::VCH; ++i)
-      lds_load16(rs, ks + NS * C::K_ELEMS + (i * C::NW + w) * 512, v_off[i]);
+      lds_load16(rs, ks + NS * C::K_ELEMS + (i * C::NW + w) * 512, v_off[i] + vt_off);
   };
   // the key-mask column of a tile travels through a register
   auto store_kmask = [&](int stage) {

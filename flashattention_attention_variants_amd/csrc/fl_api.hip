@@ -35,8 +35,11 @@ int grid_qtiles(int S_q, int rows_per_wg) { return (S_q + rows_per_wg - 1) / row
 
 // The matrix-core kernels address one (batch, K/V head) block of K and of V
 // through 32-bit byte offsets.
+// Byte offsets within one (batch, head) block of bf16 rows stay below 2^31
+// (32-bit buffer offsets), for the rows given and for the 64 rows past them
+// that a partial key tile addresses (and reads as zeros).
 bool span_ok(int64_t rows, int64_t row_stride, int64_t width) {
-  return rows <= 0 || ((rows - 1) * row_stride + width) * 2 < ((int64_t)1 << 31);
+  return rows <= 0 || ((rows + 63) * row_stride + width) * 2 < ((int64_t)1 << 31);
 }
 
 // Decode: key ranges per (sequence, K/V head).  Enough work-groups to give
