@@ -339,7 +339,8 @@ void attn_mfma_kernel(KernelArgs a) {
   // ---- Q operands in registers ---------------------------------------------
   // B operand of S^T = K Q^T: lane (c, g) holds Q[row c][16t + 8g .. +7].
   // Folded scores: Q is pre-multiplied by scale*log2(e) (one bf16 rounding),
-  // so S^T comes out in base-2 units.
+  // so S^T comes out in base-2 units; bounded softcap: by the tanh argument
+  // 2*scale*log2(e)/cap, so S^T is t below.
   bf16x8 qreg[NS][QB][DQK / 16];
   auto load_q = [&](int bb) {
 #pragma unroll
@@ -354,9 +355,12 @@ void attn_mfma_kernel(KernelArgs a) {
 #pragma unroll
         for (int t = 0; t < DQK / 16; ++t) {
           qreg[s][qb][t] = load16(qrs, (32 * qb + c) * (int)q_row_b + 32 * t + 16 * g);
-          if constexpr (C::FOLD) {
+          if constexpr (C::FOLD || C::SCAPB) {
+            // folded: scale*log2(e); bounded softcap: the tanh argument
+            // 2*scale*log2(e)/cap, so that S^T is 2^t's exponent at once
+            const float qs = C::FOLD ? a.scale_log2 : a.softcap_arg;
             f32x8 f = __builtin_convertvector(qreg[s][qb][t], f32x8);
-            qreg[s][qb][t] = __builtin_convertvector(f * a.scale_log2, bf16x8);
+            qreg[s][qb][t] = __builtin_convertvector(f * qs, bf16x8);
           }
         }
       }
@@ -692,7 +696,7 @@ void attn_mfma_kernel(KernelArgs a) {
       bf16x8 pk[2];
 
       if constexpr (C::SCAPB) {
-        // With t = 2 y log2(e) for y = scale q.k / cap, the softcapped
+        // With t = 2 y log2(e) for y = scale q.k / cap (S^T holds t), the softcapped
         // base-2 score is cap log2(e) tanh(y) = c - 2c / (2^t + 1), where
         // c = cap log2(e) <= 100: the terms 2^score stay within fp32's normal
         // range with the fixed reference 0.
@@ -700,7 +704,7 @@ void attn_mfma_kernel(KernelArgs a) {
         f32x16 x;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          x[r] = fmaf(fast_rcp(fast_exp2(sc[r] * a.softcap_arg) + 1.0f), -2.0f * c2, c2);
+          x[r] = fmaf(fast_rcp(fast_exp2(sc[r]) + 1.0f), -2.0f * c2, c2);
         if constexpr (MASKED) mask(x, kb, qb);
         l_run[s][qb] += exp_pack(x, pk, 0.0f);
       } else if constexpr (C::FOLD) {
