@@ -186,12 +186,16 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
       b2 = (const char*)((const bf16*)g2.dout + b * a.q_sb + head * a.q_sh);
     }
     bf16* ts = lds + stage * C::STAGE;
-    const __amdgpu_buffer_rsrc_t rs1 = make_rsrc(b1 + e0 * s_row_b, s_span - e0 * s_row_b);
-    const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(b2 + e0 * s_row_b, s_span - e0 * s_row_b);
+    // one resource over the whole block; the tile's offset rides in the
+    // per-lane offset (below 2^31 up to 63 rows past the block's end)
+    const __amdgpu_buffer_rsrc_t rs1 = make_rsrc(b1, s_span);
+    const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(b2, s_span);
+    const int e_off = (int)e0 * (int)s_row_b;
 #pragma unroll
-    for (int i = 0; i < C::CH; ++i) lds_load16(rs1, ts + (i * C::NW + w) * 512, t_off[i]);
+    for (int i = 0; i < C::CH; ++i) lds_load16(rs1, ts + (i * C::NW + w) * 512, t_off[i] + e_off);
 #pragma unroll
-    for (int i = 0; i < C::CH; ++i) lds_load16(rs2, ts + C::T_ELEMS + (i * C::NW + w) * 512, t_off[i]);
+    for (int i = 0; i < C::CH; ++i)
+      lds_load16(rs2, ts + C::T_ELEMS + (i * C::NW + w) * 512, t_off[i] + e_off);
     if constexpr (!DQ) {
       if (tid < BN) {
         const int qi = (int)e0 + tid;
