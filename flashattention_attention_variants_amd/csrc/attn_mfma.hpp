@@ -1,6 +1,7 @@
 // attn_mfma.hpp -- the bf16 fused attention forward on gfx950 matrix cores.
 //
-// One work-group = 4 waves = a tile of BM = 4*32*QB query rows of one (b, h).
+// One work-group = 4 waves = a tile of BM = 4*32*QB query rows of one (b, h)
+// (two softmax streams: 8 waves, four per stream over the same rows).
 // Each wave owns 32*QB rows for the whole kernel: its Q rows sit in
 // registers, already in matrix-core operand order; K and V stream through
 // LDS in tiles of 64 keys, double-buffered, with the next tile's global loads
@@ -61,8 +62,15 @@ struct MfmaCfg {
 #ifndef FL_DEC_WAVES
 #define FL_DEC_WAVES 4
 #endif
-  static constexpr int NW = DEC ? FL_DEC_WAVES : 4;
-  static constexpr int BM = NW * 32 * QB;    // query rows per work-group
+  // Two streams (DiffAttn) split over the waves: eight waves, the first four
+  // take stream 0 of the work-group's rows and the last four stream 1; each
+  // wave then holds one stream's state, which leaves room for two waves per
+  // SIMD, and the streams meet through LDS at the end.
+  static constexpr bool SPLIT = NS_ == 2;
+  static constexpr int NSU = SPLIT ? 1 : NS_;  // streams per wave
+  static constexpr int NW = DEC ? FL_DEC_WAVES : (SPLIT ? 8 : 4);
+  static constexpr int RW = SPLIT ? NW / NS_ : NW;  // waves per stream (row blocks)
+  static constexpr int BM = RW * 32 * QB;    // query rows per work-group
   static constexpr int BN = 64;              // keys per tile
   // K and V tiles sit in LDS row-major without padding; the 16-byte chunks
   // of a row are XOR-swizzled by the row index so that the operand reads
@@ -103,7 +111,7 @@ struct MfmaCfg {
 #ifndef FL_QB1_WAVES
 #define FL_QB1_WAVES 2
 #endif
-  static constexpr int WAVES_PER_EU = NS == 1 ? (QB == 1 ? FL_QB1_WAVES : 2) : 1;
+  static constexpr int WAVES_PER_EU = NSU == 1 ? (QB == 1 ? FL_QB1_WAVES : 2) : 1;
   static_assert(DQK % 16 == 0 && DV % 32 == 0, "head dims");
   static_assert(KCH >= 1 && VCH >= 1, "tile too small for the work-group");
 };
@@ -226,12 +234,16 @@ template <class C>
 __global__ __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_EU)))
 void attn_mfma_kernel(KernelArgs a) {
   constexpr int BN = C::BN, DQK = C::DQK, DV = C::DV, NS = C::NS, QB = C::QB;
+  constexpr int NSU = C::NSU;  // streams held by one wave
   __shared__ __attribute__((aligned(16))) bf16 lds[C::STAGES * C::STAGE];
   __shared__ __attribute__((aligned(16))) float kmadd[C::KMASK ? C::STAGES * BN : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int c = lane & 31, g = lane >> 5;
+  // split streams: this wave's stream and row block
+  const int ws = C::SPLIT ? w / C::RW : 0, wr = C::SPLIT ? w % C::RW : w;
+  auto stream_of = [&](int s) { return C::SPLIT ? ws : s; };
 
   int bh, qt, split = 0;
   int b_first = 0, n_rep = 1;  // batch entries this work-group walks
@@ -309,7 +321,7 @@ void attn_mfma_kernel(KernelArgs a) {
   }
 
   // ---- this wave's rows and their key intervals ----------------------------
-  const int wq0 = q0 + w * 32 * QB;
+  const int wq0 = q0 + wr * 32 * QB;
   const int wq1 = min(wq0 + 32 * QB, a.sq) - 1;  // last valid row of the wave
   int wp_min, wp_max, w_lo_min, w_hi_min, w_lo_max, w_hi_max;
   pos_range(min(wq0, a.sq - 1), max(wq1, min(wq0, a.sq - 1)), wp_min, wp_max);
@@ -341,12 +353,12 @@ void attn_mfma_kernel(KernelArgs a) {
   // Folded scores: Q is pre-multiplied by scale*log2(e) (one bf16 rounding),
   // so S^T comes out in base-2 units; bounded softcap: by the tanh argument
   // 2*scale*log2(e)/cap, so S^T is t below.
-  bf16x8 qreg[NS][QB][DQK / 16];
+  bf16x8 qreg[NSU][QB][DQK / 16];
   auto load_q = [&](int bb) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
+    for (int s = 0; s < NSU; ++s) {
       // rows past S_q read as zeros through the bounds-checked resource
-      const bf16* qh = (const bf16*)a.q[s] + bb * a.q_sb + h * a.q_sh;
+      const bf16* qh = (const bf16*)a.q[stream_of(s)] + bb * a.q_sb + h * a.q_sh;
       const int64_t q_row_b = a.q_si * 2;
       const int64_t q_span = (int64_t)(a.sq - 1) * q_row_b + DQK * 2 - (int64_t)wq0 * q_row_b;
       const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qh + (int64_t)wq0 * a.q_si, q_span);
@@ -369,9 +381,9 @@ void attn_mfma_kernel(KernelArgs a) {
   load_q(b);
 
   // ---- per-row softmax state -------------------------------------------------
-  f32x16 oacc[NS][QB][DV / 32];
-  float m_run[NS][QB], l_run[NS][QB];
-  bool m_set[NS][QB];
+  f32x16 oacc[NSU][QB][DV / 32];
+  float m_run[NSU][QB], l_run[NSU][QB];
+  bool m_set[NSU][QB];
   // Folded scores: one more k-step of the S^T product adds the terms of the
   // score that are not q.k.  Only lane half 0 (k-slots 0..7) carries them;
   // half 1 of the key-side operand is zero.  For the tile at key j0, key
@@ -387,7 +399,7 @@ void attn_mfma_kernel(KernelArgs a) {
   // exponential.  The row term is rebuilt once per tile; sigma = -1 flips
   // the sign bits of slots 1..6.  Blocks that straddle the diagonal take
   // sigma = +1 and a vector correction for j > i.  Plain scores use slot 0.
-  bf16x8 qext[NS][QB];
+  bf16x8 qext[NSU][QB];
   // Wave-uniform: some row of the wave has a reference m != 0, so S^T needs
   // the folded step (always under ALiBi, whose penalty rides on it).
   bool need_fold = C::ALIBI_FOLD;
@@ -439,7 +451,7 @@ void attn_mfma_kernel(KernelArgs a) {
   };
   auto reset_state = [&]() {
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+    for (int s = 0; s < NSU; ++s)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         // folded: m = 0 is a valid reference from the start; it moves only
@@ -554,7 +566,7 @@ void attn_mfma_kernel(KernelArgs a) {
   auto read_k = [&](const bf16* ks, int s, int kb) {
 #pragma unroll
     for (int t = 0; t < DQK / 16; ++t)
-      kop[t] = *(const bf16x8*)(ks + s * C::K_ELEMS + k_rd[t] + 32 * kb * DQK);
+      kop[t] = *(const bf16x8*)(ks + stream_of(s) * C::K_ELEMS + k_rd[t] + 32 * kb * DQK);
   };
   // position of a (key half, query block) unit against the diagonal
   // (wave-uniform): keys wholly above the rows' diagonal, or straddling it
@@ -595,7 +607,7 @@ void attn_mfma_kernel(KernelArgs a) {
   auto compute_tile = [&](int stage, int kt, auto masked_tag, auto folded_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     constexpr bool FOLDED = decltype(folded_tag)::value;
-    constexpr int U = NS * 2 * QB;
+    constexpr int U = NSU * 2 * QB;
     cur_stage = stage;
     const bf16* ks = lds + stage * C::STAGE;
     const int j0 = kt * BN;
@@ -659,7 +671,7 @@ void attn_mfma_kernel(KernelArgs a) {
 
     if constexpr (C::ALIBI_FOLD) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
+      for (int s = 0; s < NSU; ++s)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) set_qext(s, qb, m_run[s][qb], j0);
     }
@@ -675,20 +687,20 @@ void attn_mfma_kernel(KernelArgs a) {
     };
     read_k(ks, 0, 0);
     qk(j0, 0, 0, 0, sacc[0], folded_tag);
-    // unit u: key half kb = u / (NS*QB), stream s = (u / QB) % NS, block qb = u % QB
+    // unit u: key half kb = u / (NSU*QB), stream s = (u / QB) % NSU, block qb = u % QB
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int kb = u / (NS * QB), s = (u / QB) % NS, qb = u % QB;
+      const int kb = u / (NSU * QB), s = (u / QB) % NSU, qb = u % QB;
       if (u + 1 < U) {
-        const int kb1 = (u + 1) / (NS * QB), s1 = ((u + 1) / QB) % NS, qb1 = (u + 1) % QB;
+        const int kb1 = (u + 1) / (NSU * QB), s1 = ((u + 1) / QB) % NSU, qb1 = (u + 1) % QB;
         if (qb1 == 0) read_k(ks, s1, kb1);
         qk(j0, s1, kb1, qb1, sacc[(u + 1) & 1], folded_tag);
       }
       // the previous unit's P.V product, independent of this unit's softmax
       if (u >= 1) {
-        if ((u - 1) % (NS * QB) == 0) take_v();
-        pv(((u - 1) / QB) % NS, (u - 1) % QB, pkp);
-        if (u - 1 == NS * QB - 1) read_v(1);
+        if ((u - 1) % (NSU * QB) == 0) take_v();
+        pv(((u - 1) / QB) % NSU, (u - 1) % QB, pkp);
+        if (u - 1 == NSU * QB - 1) read_v(1);
       }
       f32x16& sc = sacc[u & 1];
       const int qi = wq0 + 32 * qb + c;
@@ -731,7 +743,7 @@ void attn_mfma_kernel(KernelArgs a) {
           f32x16 rs = f32x16{};
 #pragma unroll
           for (int t = 0; t < DQK / 16; ++t) {
-            const bf16x8 ka = *(const bf16x8*)(ks + s * C::K_ELEMS + k_rd[t] + 32 * kb * DQK);
+            const bf16x8 ka = *(const bf16x8*)(ks + stream_of(s) * C::K_ELEMS + k_rd[t] + 32 * kb * DQK);
             rs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s][qb][t], rs, 0, 0, 0);
           }
           fold(j0, s, kb, qb, rs);
@@ -761,7 +773,7 @@ void attn_mfma_kernel(KernelArgs a) {
           set_qext(s, qb, m_run[s][qb], j0);
           if (__builtin_amdgcn_ballot_w64(m_run[s][qb] != 0.0f)) need_fold = true;
           // the next unit's scores, already issued, may belong to the same rows
-          if (u + 1 < U && (u + 1) % QB == qb && ((u + 1) / QB) % NS == s) {
+          if (u + 1 < U && (u + 1) % QB == qb && ((u + 1) / QB) % NSU == s) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[(u + 1) & 1][r] -= shift;
           }
@@ -838,8 +850,8 @@ void attn_mfma_kernel(KernelArgs a) {
       pkp[1] = pk[1];
       if constexpr (C::SCAPB) unit_hint_scapb();
     }
-    if ((U - 1) % (NS * QB) == 0) take_v();
-    pv(((U - 1) / QB) % NS, (U - 1) % QB, pkp);
+    if ((U - 1) % (NSU * QB) == 0) take_v();
+    pv(((U - 1) / QB) % NSU, (U - 1) % QB, pkp);
   };
 
   // ---- main loop ---------------------------------------------------------------
@@ -894,20 +906,48 @@ void attn_mfma_kernel(KernelArgs a) {
   };
   // normalise, combine, gate and store the rows of batch entry b
   auto finish_row = [&]() {
-    float inv[NS][QB];
+    float inv[NSU][QB];
   #pragma unroll
-    for (int s = 0; s < NS; ++s)
+    for (int s = 0; s < NSU; ++s)
   #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const float l = l_run[s][qb] + __shfl_xor(l_run[s][qb], 32);
         inv[s][qb] = l > 0.0f ? 1.0f / l : 0.0f;
         const int qi = wq0 + 32 * qb + c;
-        if (a.lse[s] && g == 0 && qi < a.sq) {
+        float* lse_out = a.lse[stream_of(s)];
+        if (lse_out && g == 0 && qi < a.sq) {
           const float m = m_run[s][qb];
           const float lse = l > 0.0f ? (m + __builtin_log2f(l)) * kLn2 : kNegInf;
-          a.lse[s][b * a.lse_sb + h * a.lse_sh + qi] = lse;
+          lse_out[b * a.lse_sb + h * a.lse_sh + qi] = lse;
         }
       }
+
+    // Split streams: the stream-1 waves hand their normalised rows through
+    // LDS (row-major, rows padded by 4 floats) to the stream-0 wave of the
+    // same rows, which stores O1/l1 - lambda O2/l2.  Both barriers are met by
+    // every wave; the first frees the K/V stages.
+    constexpr int XS = DV + 4;
+    float* xo = (float*)lds;
+    if constexpr (C::SPLIT) {
+      static_assert(C::BM * XS * 4 <= C::STAGES * C::STAGE * 2, "combine buffer");
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (ws == 1) {
+  #pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          float* xr = xo + (wr * 32 * QB + 32 * qb + c) * XS;
+  #pragma unroll
+          for (int db = 0; db < DV / 32; ++db)
+  #pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const f32x4 v = {oacc[0][qb][db][4 * r4] * inv[0][qb], oacc[0][qb][db][4 * r4 + 1] * inv[0][qb],
+                               oacc[0][qb][db][4 * r4 + 2] * inv[0][qb], oacc[0][qb][db][4 * r4 + 3] * inv[0][qb]};
+              *(f32x4*)(xr + 32 * db + 8 * r4 + 4 * g) = v;
+            }
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (ws == 1) return;
+    }
 
   #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -916,6 +956,7 @@ void attn_mfma_kernel(KernelArgs a) {
       bf16* op = (bf16*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_si;
       const bf16* gp = C::GATE ? (const bf16*)a.gate + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_si
                                : nullptr;
+      const float* xr = xo + (wr * 32 * QB + 32 * qb + c) * XS;
   #pragma unroll
       for (int db = 0; db < DV / 32; ++db)
   #pragma unroll
@@ -923,9 +964,11 @@ void attn_mfma_kernel(KernelArgs a) {
           const int d = 32 * db + 8 * r4 + 4 * g;
           float ov[4];
   #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            ov[e] = oacc[0][qb][db][4 * r4 + e] * inv[0][qb];
-            if constexpr (NS == 2) ov[e] -= a.lambda * oacc[1][qb][db][4 * r4 + e] * inv[1][qb];
+          for (int e = 0; e < 4; ++e) ov[e] = oacc[0][qb][db][4 * r4 + e] * inv[0][qb];
+          if constexpr (C::SPLIT) {
+            const f32x4 o2 = *(const f32x4*)(xr + d);
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) ov[e] -= a.lambda * o2[e];
           }
           if constexpr (C::GATE) {
             const bf16x4 gv = *(const bf16x4*)(gp + d);
