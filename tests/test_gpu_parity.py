@@ -296,11 +296,32 @@ def test_diffattn_small(dtype, causal, Dv):
                                    scale=0.125)
     check(np64(o), ro, dtype, "diffattn")
     check(np64(l1), rl1, "f32" if dtype == "f32" else "bf16", "lse1")
+    check(np64(l2), rl2, "f32" if dtype == "f32" else "bf16", "lse2")
     # lambda = 0 is vanilla attention of the first stream
     o0 = api.fl_diffattn_fwd(*g, lam=0.0, causal=causal)
     torch.cuda.synchronize()
     rv, _ = oracle.attn(np64(q1), np64(k1), np64(v), variant="causal" if causal else "vanilla")
     check(np64(o0), rv, dtype, "diffattn lambda 0")
+
+
+@pytest.mark.parametrize("Dv", [64, 128])
+def test_diffattn_cross_lengths_and_cancellation(Dv):
+    # 70 queries against 200 keys (a partial query tile whose missing rows
+    # still join the streams' hand-over, ragged key tiles), and identical
+    # streams with lambda 1, whose outputs cancel (to within the rounding of
+    # one normalised stream: the combine may fuse its multiply and subtract)
+    q1, q2, _, _, _ = inputs.diffattn_inputs(2, 3, 70, 64, Dv, "bf16", seed=71)
+    _, _, k1, k2, v = inputs.diffattn_inputs(2, 3, 200, 64, Dv, "bf16", seed=72)
+    g = [t.to(DEV) for t in (q1, q2, k1, k2, v)]
+    o, l1, l2 = api.fl_diffattn_fwd(*g, lam=0.8, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl1, rl2 = oracle.diffattn(*(np64(t) for t in (q1, q2, k1, k2, v)), lam=0.8, scale=0.125)
+    check(np64(o), ro, "bf16", "diffattn cross lengths")
+    check(np64(l1), rl1, "bf16", "lse1")
+    check(np64(l2), rl2, "bf16", "lse2")
+    o1 = api.fl_diffattn_fwd(g[0], g[0], g[2], g[2], g[4], lam=1.0)
+    torch.cuda.synchronize()
+    assert np.abs(np64(o1)).max() <= 1e-6
 
 
 # ---------------------------------------------------------------------------
