@@ -95,6 +95,13 @@ struct MfmaCfg {
   __device__ static constexpr int vswz(int row) { return VCPR == 4 ? 2 * ((row >> 1) & 1) : 2 * (row & 3); }
   static constexpr int KCH = BN * DQK / 8 / (NW * 64);  // 16-byte K chunks per thread
   static constexpr int VCH = BN * DV / 8 / (NW * 64);   // 16-byte V chunks per thread
+  // gated launches that walk several entries per work-group (two query
+  // blocks per wave): the gate rows of an entry (BM x DV) go to LDS when
+  // the entry starts, double-buffered by entry parity.  (With one entry per
+  // work-group the gate is read in the epilogue directly: measured faster.)
+  static constexpr bool GATE_LDS = GATE && QB == 2;
+  static constexpr int G_ELEMS = GATE_LDS ? BM * DV : 0;
+  static constexpr int GCH = G_ELEMS / 8 / (NW * 64);  // 16-byte gate chunks per thread
   // Folded scores: the scale, the running reference and (for ALiBi) the
   // distance penalty all enter the S^T product itself.
   // Folded scores: the scale, the running reference, the ALiBi distance
@@ -237,6 +244,7 @@ void attn_mfma_kernel(KernelArgs a) {
   constexpr int NSU = C::NSU;  // streams held by one wave
   __shared__ __attribute__((aligned(16))) bf16 lds[C::STAGES * C::STAGE];
   __shared__ __attribute__((aligned(16))) float kmadd[C::KMASK ? C::STAGES * BN : 4];
+  __shared__ __attribute__((aligned(16))) bf16 gbuf[C::GATE_LDS ? 2 * C::G_ELEMS : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -379,6 +387,27 @@ void attn_mfma_kernel(KernelArgs a) {
     }
   };
   load_q(b);
+
+  // Gate rows of entry bb (rows q0.., DV values each) into gate buffer
+  // `buf`, straight from global memory; rows past S_q read as zeros.  They
+  // land while the entry's tiles compute: the tile waits retire them (loads
+  // return in issue order), and the epilogue of an entry with fewer than two
+  // tiles waits for them itself.
+  auto issue_gate = [&](int bb, int buf) {
+    if constexpr (C::GATE_LDS) {
+      const int64_t g_row_b = a.o_si * 2;
+      const bf16* gb = (const bf16*)a.gate + bb * a.o_sb + h * a.o_sh + (int64_t)q0 * a.o_si;
+      const __amdgpu_buffer_rsrc_t grs =
+          make_rsrc(gb, (int64_t)(a.sq - 1 - q0) * g_row_b + DV * 2);
+#pragma unroll
+      for (int i = 0; i < C::GCH; ++i) {
+        const int q = (i * C::NW + w) * 64 + lane;  // 16-byte slot: row q / (DV/8)
+        lds_load16(grs, gbuf + buf * C::G_ELEMS + (i * C::NW + w) * 512,
+                   (q / (DV / 8)) * (int)g_row_b + 16 * (q % (DV / 8)));
+      }
+    }
+  };
+  issue_gate(b, 0);
 
   // ---- per-row softmax state -------------------------------------------------
   f32x16 oacc[NSU][QB][DV / 32];
@@ -905,7 +934,12 @@ void attn_mfma_kernel(KernelArgs a) {
     return kt_lo + (x >= n_kt ? x - n_kt : x);
   };
   // normalise, combine, gate and store the rows of batch entry b
-  auto finish_row = [&]() {
+  auto finish_row = [&](bool gate_wait) {
+    if constexpr (C::GATE_LDS) {
+      if (gate_wait) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    } else {
+      (void)gate_wait;
+    }
     float inv[NSU][QB];
   #pragma unroll
     for (int s = 0; s < NSU; ++s)
@@ -954,8 +988,10 @@ void attn_mfma_kernel(KernelArgs a) {
       const int qi = wq0 + 32 * qb + c;
       if (qi >= a.sq) continue;
       bf16* op = (bf16*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_si;
-      const bf16* gp = C::GATE ? (const bf16*)a.gate + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_si
-                               : nullptr;
+      const bf16* gp = !C::GATE ? nullptr
+                       : C::GATE_LDS
+                           ? gbuf + ((b - b_first) & 1) * C::G_ELEMS + (wq0 - q0 + 32 * qb + c) * DV
+                           : (const bf16*)a.gate + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_si;
       const float* xr = xo + (wr * 32 * QB + 32 * qb + c) * XS;
   #pragma unroll
       for (int db = 0; db < DV / 32; ++db)
@@ -1027,27 +1063,47 @@ void attn_mfma_kernel(KernelArgs a) {
           compute_tile(stage, kt, T{}, F{});
       }
     }
+    bool boundary = false;
     if constexpr (C::PERSIST) {
       if (it % n_kt == n_kt - 1 && next) {
         // the entry's last tile: its rows are done; the next entry's first
-        // tiles are already in flight.  (The output stores and the next Q
-        // loads only add to the count the tile wait below allows: loads
-        // return in issue order, so it still cannot pass before the awaited
-        // tile has landed.)
-        finish_row();
+        // tiles are already in flight.  Its Q and gate loads go out after
+        // them, and the tile wait below leaves them outstanding too (loads
+        // return in issue order).
+        finish_row(n_kt < 2);
         ++b;
         reset_state();
         load_q(b);
+        issue_gate(b, (b - b_first) & 1);
+        boundary = true;
       }
     }
-    if (next) sync_tile(min(AHEAD - 1, n_total - 2 - it));
+    if (next) {
+      if constexpr (C::PERSIST) {
+        static_assert(AHEAD == 2, "entry hand-over waits");
+        constexpr int EXTRA = NSU * QB * (DQK / 16) + C::GCH;  // Q and gate loads of an entry
+        static_assert(LOADS + EXTRA < 64, "vmcnt range");
+        const int newer = min(AHEAD - 1, n_total - 2 - it);
+        if (boundary) {
+          if (newer >= 1)
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LOADS + EXTRA) : "memory");
+          else
+            asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(EXTRA) : "memory");
+        } else {
+          sync_tile(newer);
+        }
+      } else {
+        sync_tile(min(AHEAD - 1, n_total - 2 - it));
+      }
+    }
   }
   if constexpr (C::PERSIST) {
     // entries left without a tile (no key at all) still write their rows
     if (n_kt == 0) {
       for (int r = 1; r < n_rep; ++r) {
-        finish_row();
+        finish_row(true);
         ++b;
+        issue_gate(b, (b - b_first) & 1);
       }
     }
   }
@@ -1078,7 +1134,7 @@ void attn_mfma_kernel(KernelArgs a) {
       return;
     }
   }
-  finish_row();
+  finish_row(!C::PERSIST || n_kt < 2);
 }
 
 }  // namespace fl
