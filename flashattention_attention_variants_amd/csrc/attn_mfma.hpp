@@ -813,15 +813,25 @@ void attn_mfma_kernel(KernelArgs a) {
         // score modification, bias, key mask, positional mask
         float bias_v[16];
         if constexpr (C::BIAS) {
+          // Two 16-byte loads per lane (keys 16r + 8g .. +7 of the unit's 32)
+          // and a swap of half of each with the lane 32 apart give every lane
+          // its keys 4g + 8 r4 + 0..3 (the accumulator layout).
           const int qi_c = min(qi, a.sq - 1);
           const bf16* bp = (const bf16*)a.bias + h * a.bias_sh + (int64_t)qi_c * a.bias_si;
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int j = jb + 8 * r4;
-            bf16x4 bv = {};
-            if (!MASKED || j < a.sk) bv = *(const bf16x4*)(bp + j);
+          for (int r = 0; r < 2; ++r) {
+            const int j = j0 + 32 * kb + 16 * r + 8 * g;  // S_k % 8 == 0: whole chunk or none
+            u32x4 raw = {};
+            if (!MASKED || j < a.sk) raw = *(const u32x4*)(bp + j);
+            const auto s0 = __builtin_amdgcn_permlane32_swap(raw[0], raw[2], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(raw[1], raw[3], false, false);
+            const bf16x4 lo = __builtin_bit_cast(bf16x4, u32x2{s0[0], s1[0]});  // r4 = 2r
+            const bf16x4 hi = __builtin_bit_cast(bf16x4, u32x2{s0[1], s1[1]});  // r4 = 2r + 1
 #pragma unroll
-            for (int e = 0; e < 4; ++e) bias_v[4 * r4 + e] = (float)bv[e] * kLog2e;
+            for (int e = 0; e < 4; ++e) {
+              bias_v[8 * r + e] = (float)lo[e] * kLog2e;
+              bias_v[8 * r + 4 + e] = (float)hi[e] * kLog2e;
+            }
           }
         }
         float km_v[16];
