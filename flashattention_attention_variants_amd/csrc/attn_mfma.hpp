@@ -1003,26 +1003,45 @@ void attn_mfma_kernel(KernelArgs a) {
                            ? gbuf + ((b - b_first) & 1) * C::G_ELEMS + (wq0 - q0 + 32 * qb + c) * DV
                            : (const bf16*)a.gate + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_si;
       const float* xr = xo + (wr * 32 * QB + 32 * qb + c) * XS;
+  // A lane holds dims 8 r4 + 4g + 0..3 of its row; pairs (r4 = 2r, 2r + 1)
+  // trade halves with the lane 32 apart (the same row) so that each lane
+  // moves 16 contiguous bytes (dims 16r + 8g .. +7) per global access.
   #pragma unroll
       for (int db = 0; db < DV / 32; ++db)
   #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int d = 32 * db + 8 * r4 + 4 * g;
-          float ov[4];
-  #pragma unroll
-          for (int e = 0; e < 4; ++e) ov[e] = oacc[0][qb][db][4 * r4 + e] * inv[0][qb];
-          if constexpr (C::SPLIT) {
-            const f32x4 o2 = *(const f32x4*)(xr + d);
-  #pragma unroll
-            for (int e = 0; e < 4; ++e) ov[e] -= a.lambda * o2[e];
+        for (int r = 0; r < 2; ++r) {
+          bf16x4 gvv[2];
+          if constexpr (C::GATE && !C::GATE_LDS) {
+            const u32x4 raw = *(const u32x4*)(gp + 32 * db + 16 * r + 8 * g);
+            const auto s0 = __builtin_amdgcn_permlane32_swap(raw[0], raw[2], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(raw[1], raw[3], false, false);
+            gvv[0] = __builtin_bit_cast(bf16x4, u32x2{s0[0], s1[0]});
+            gvv[1] = __builtin_bit_cast(bf16x4, u32x2{s0[1], s1[1]});
           }
-          if constexpr (C::GATE) {
-            const bf16x4 gv = *(const bf16x4*)(gp + d);
+          u32x2 packed[2];
   #pragma unroll
-            for (int e = 0; e < 4; ++e) ov[e] *= sigmoid((float)gv[e]);
+          for (int hh = 0; hh < 2; ++hh) {
+            const int r4 = 2 * r + hh;
+            const int d = 32 * db + 8 * r4 + 4 * g;
+            float ov[4];
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) ov[e] = oacc[0][qb][db][4 * r4 + e] * inv[0][qb];
+            if constexpr (C::SPLIT) {
+              const f32x4 o2 = *(const f32x4*)(xr + d);
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) ov[e] -= a.lambda * o2[e];
+            }
+            if constexpr (C::GATE) {
+              const bf16x4 gv = C::GATE_LDS ? *(const bf16x4*)(gp + d) : gvv[hh];
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) ov[e] *= sigmoid((float)gv[e]);
+            }
+            const bf16x4 out = {(bf16)ov[0], (bf16)ov[1], (bf16)ov[2], (bf16)ov[3]};
+            packed[hh] = __builtin_bit_cast(u32x2, out);
           }
-          const bf16x4 out = {(bf16)ov[0], (bf16)ov[1], (bf16)ov[2], (bf16)ov[3]};
-          *(bf16x4*)(op + d) = out;
+          const auto t0 = __builtin_amdgcn_permlane32_swap(packed[0][0], packed[1][0], false, false);
+          const auto t1 = __builtin_amdgcn_permlane32_swap(packed[0][1], packed[1][1], false, false);
+          *(u32x4*)(op + 32 * db + 16 * r + 8 * g) = u32x4{t0[0], t1[0], t0[1], t1[1]};
         }
     }
   };
