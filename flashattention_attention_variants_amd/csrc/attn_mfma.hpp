@@ -411,6 +411,20 @@ void attn_mfma_kernel(KernelArgs a) {
 
   // ---- per-row softmax state -------------------------------------------------
   f32x16 oacc[NSU][QB][DV / 32];
+  // Bounded softcap: the row sums go through the matrix cores (the path is
+  // vector-bound and never needs a unit's sum on its own).  A 16x16x32
+  // product with a 0/1 selector as A adds each query's 32 rounded terms of a
+  // unit: lane l supplies selector row l % 16 over k-group l / 16, and the
+  // B operand (P^T of the unit) puts query n's terms in k-groups 0 and 2 and
+  // query n + 16's in k-groups 1 and 3 of column n; rows 0 and 1 of the
+  // 16x16 accumulator (registers 0 and 1 of lanes 0..15) collect them.
+  f32x4 lacc[NSU][QB];
+  bf16x8 lsel = {};
+  if constexpr (C::SCAPB) {
+    const int m = lane & 15, kgrp = lane >> 4;
+    const bf16 v = (bf16)((m == 0 && (kgrp & 1) == 0) || (m == 1 && (kgrp & 1) == 1) ? 1.0f : 0.0f);
+    lsel = bf16x8{v, v, v, v, v, v, v, v};
+  }
   float m_run[NSU][QB], l_run[NSU][QB];
   bool m_set[NSU][QB];
   // Folded scores: one more k-step of the S^T product adds the terms of the
@@ -488,6 +502,7 @@ void attn_mfma_kernel(KernelArgs a) {
         m_run[s][qb] = (C::FOLD || C::SCAPB) ? 0.0f : kNegInf;
         m_set[s][qb] = false;
         l_run[s][qb] = 0.0f;
+        lacc[s][qb] = f32x4{};
         qext[s][qb] = bf16x8{};
         if constexpr (C::FOLD) set_qext(s, qb, 0.0f, 0);
 #pragma unroll
@@ -688,6 +703,7 @@ void attn_mfma_kernel(KernelArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = fast_exp2(x[8 * h2 + e] - shift);
         pk[h2] = __builtin_convertvector(p, bf16x8);
+        if constexpr (C::SCAPB) continue;  // summed by the matrix cores
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           bf16x2 pr = {pk[h2][e], pk[h2][e + 1]};
@@ -747,7 +763,9 @@ void attn_mfma_kernel(KernelArgs a) {
         for (int r = 0; r < 16; ++r)
           x[r] = fmaf(fast_rcp(fast_exp2(sc[r]) + 1.0f), -2.0f * c2, c2);
         if constexpr (MASKED) mask(x, kb, qb);
-        l_run[s][qb] += exp_pack(x, pk, 0.0f);
+        exp_pack(x, pk, 0.0f);
+        lacc[s][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pk[0], lacc[s][qb], 0, 0, 0);
+        lacc[s][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pk[1], lacc[s][qb], 0, 0, 0);
       } else if constexpr (C::FOLD) {
         // S^T already holds (score - m) in base 2.
         alibi_fix(j0, sc, kb, qb);
@@ -944,6 +962,16 @@ void attn_mfma_kernel(KernelArgs a) {
     return kt_lo + (x >= n_kt ? x - n_kt : x);
   };
   // normalise, combine, gate and store the rows of batch entry b
+  // the full row sum of this lane's row (both lane halves)
+  auto row_sum = [&](int s, int qb) {
+    if constexpr (C::SCAPB) {
+      const float l0 = __shfl(lacc[s][qb][0], c & 15);
+      const float l1 = __shfl(lacc[s][qb][1], c & 15);
+      return c < 16 ? l0 : l1;
+    } else {
+      return l_run[s][qb] + __shfl_xor(l_run[s][qb], 32);
+    }
+  };
   auto finish_row = [&](bool gate_wait) {
     if constexpr (C::GATE_LDS) {
       if (gate_wait) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
@@ -955,7 +983,7 @@ void attn_mfma_kernel(KernelArgs a) {
     for (int s = 0; s < NSU; ++s)
   #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const float l = l_run[s][qb] + __shfl_xor(l_run[s][qb], 32);
+        const float l = row_sum(s, qb);
         inv[s][qb] = l > 0.0f ? 1.0f / l : 0.0f;
         const int qi = wq0 + 32 * qb + c;
         float* lse_out = a.lse[stream_of(s)];
@@ -1142,7 +1170,7 @@ void attn_mfma_kernel(KernelArgs a) {
     if (a.n_split > 1) {
       // one key range of a split decode: normalised float32 output and
       // natural-log LSE of this range (0 and -inf when it held no key)
-      const float l = l_run[0][0] + __shfl_xor(l_run[0][0], 32);
+      const float l = row_sum(0, 0);
       const float iv = l > 0.0f ? 1.0f / l : 0.0f;
       const int qi = wq0 + c;
       if (qi < a.sq) {
