@@ -140,6 +140,10 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, void* lds,
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
                                            byte_off, 0, 0, 0);
+#else
+  (void)rs;
+  (void)lds;
+  (void)byte_off;
 #endif
 }
 
