@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--probe-traffic", action="store_true",
                     help="make only the dispatches the counter runs read: a copy of known "
                          "size, then one call per variant")
+    ap.add_argument("--probe-evoformer", action="store_true",
+                    help="as --probe-traffic, for the Evoformer workload (row with pair bias, "
+                         "then column)")
     return ap.parse_args()
 
 
@@ -70,6 +73,9 @@ def main():
         sys.exit(1)
     api.load_library()
     dev = "cuda"
+    if args.probe_evoformer:
+        probe_evoformer(torch, api, inputs, dev)
+        return
     wl = inputs.WORKLOADS[args.workload]
     assert wl.kind == "attn"
     s = wl.shape
@@ -402,6 +408,37 @@ def report(torch, api, flops, inputs, dev):
                               "bound": bound, "roofline_tflops": round(roof, 1),
                               "frac_roofline": round(tf / roof, 4),
                               "frac_peak": round(tf / peak, 4)}), flush=True)
+
+
+EVO_WORKLOAD = "evoformer_bf16_nseq128_nres256_h8_c32"
+
+
+def probe_evoformer(torch, api, inputs, dev):
+    """The dispatches the Evoformer counter runs read: one row call (pair bias,
+    key mask) and one column call, a copy of known size, then the two calls
+    again."""
+    from flashattention_attention_variants_amd import profiling
+    wl = inputs.WORKLOADS[EVO_WORKLOAD]
+    t = inputs.make(wl)
+    g = {n: t[n].to(dev) for n in ("q", "k", "v", "gate", "pair_bias", "key_mask")}
+    out = torch.empty_like(g["q"])
+
+    def calls():
+        for axis in wl.variants:
+            pb = g["pair_bias"] if axis == "row" else None
+            api.fl_evoformer_gated_attn_fwd(g["q"], g["k"], g["v"], g["gate"], pair_bias=pb,
+                                            key_mask=g["key_mask"], axis=axis, out=out)
+
+    calls()
+    src = torch.ones(profiling.PROBE_COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    calls()
+    torch.cuda.synchronize()
+    print("probe: copy of %d bytes, then one call each of %s"
+          % (profiling.PROBE_COPY_BYTES, ",".join(wl.variants)), flush=True)
 
 
 if __name__ == "__main__":

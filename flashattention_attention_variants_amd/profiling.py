@@ -241,6 +241,43 @@ def traffic_markdown(rec: dict) -> str:
     return "\n".join(out)
 
 
+EVO_WORKLOAD = "evoformer_bf16_nseq128_nres256_h8_c32"
+
+
+def evo_traffic_markdown(dir_fetch: str, dir_write: str) -> str:
+    """Calibrated HBM bytes of the Evoformer row (pair bias) and column
+    launches against their algorithmic bytes."""
+    from flashattention_attention_variants_amd import flops, inputs
+    wl = inputs.WORKLOADS[EVO_WORKLOAD]
+    sh = wl.shape
+    rec = traffic(dir_fetch, dir_write, list(wl.variants))
+    out = ["# HBM traffic per launch -- attn_mfma_kernel, %s" % EVO_WORKLOAD, "",
+           "Two counter runs of the Evoformer probe (`bench.py --probe-evoformer`: one row call "
+           "with the pair bias and one column call, a %d-byte device copy, then both calls "
+           "again), then the summary:" % rec["probe_copy_bytes"], "", "```",
+           "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/evo_fetch -o run "
+           "-- python3 $REPO/bench.py --probe-evoformer",
+           "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/evo_write -o run "
+           "-- python3 $REPO/bench.py --probe-evoformer",
+           "python -m flashattention_attention_variants_amd.profiling evo-traffic gpurun_out/evo_fetch "
+           "gpurun_out/evo_write", "```", "",
+           "Calibration: the copy of %d bytes read %.0f KiB of FETCH_SIZE and %.0f KiB of WRITE_SIZE, "
+           "so counter KiB are scaled by %.4f (fetch) and %.4f (write) to bytes."
+           % (rec["probe_copy_bytes"], rec["copy_fetch_kib"], rec["copy_write_kib"],
+              rec["fetch_factor"], rec["write_factor"]), "",
+           "| form | kernel | fetch MB | write MB | traffic MB | algorithmic MB | ratio |",
+           "|---|---|---:|---:|---:|---:|---:|"]
+    for k, v in rec["per_variant"].items():
+        alg = flops.evoformer_bytes(sh["N_seq"], sh["N_res"], sh["H"], sh["C"], k)
+        out.append("| %s | `%s` | %.1f | %.1f | %.1f | %.1f | %.2f |" % (
+            k, v["kernel"].replace("fl::", ""), v["fetch_bytes"] / 1e6, v["write_bytes"] / 1e6,
+            v["traffic_bytes"] / 1e6, alg / 1e6, v["traffic_bytes"] / alg))
+    out += ["", "Algorithmic bytes = q, k, v, gate read once, o written once (bf16), the u8 key "
+            "mask, and for the row form the pair bias [H, N_res, N_res] read once.", "",
+            "kernel_digest: %s" % rec["kernel_digest"], ""]
+    return "\n".join(out)
+
+
 COUNTER_PASSES = (
     "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_ACTIVE_INST_VALU "
     "SQ_WAVE_CYCLES SQ_INSTS_SALU GRBM_GUI_ACTIVE",
@@ -308,6 +345,9 @@ def main(argv=None):
     c = sub.add_parser("counters-md")
     c.add_argument("dirs", nargs="+")
     c.add_argument("--workload", required=True)
+    e = sub.add_parser("evo-traffic")
+    e.add_argument("dir_fetch")
+    e.add_argument("dir_write")
     t = sub.add_parser("traffic")
     t.add_argument("dir_fetch")
     t.add_argument("dir_write")
@@ -337,6 +377,11 @@ def main(argv=None):
         path = os.path.join(ROOT, "profiles", "attn_mfma_kernel_%s_stats.md" % b["decode"]["workload"])
         with open(path, "w") as fh:
             fh.write(decode_stats_markdown(a.dir, a.bench))
+        print("wrote", path)
+    elif a.cmd == "evo-traffic":
+        path = os.path.join(ROOT, "profiles", "traffic_%s.md" % EVO_WORKLOAD)
+        with open(path, "w") as fh:
+            fh.write(evo_traffic_markdown(a.dir_fetch, a.dir_write))
         print("wrote", path)
     elif a.cmd == "stats-md":
         path = os.path.join(ROOT, "profiles", "attn_mfma_kernel_%s_stats.md" % a.workload)

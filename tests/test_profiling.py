@@ -67,3 +67,21 @@ def test_decode_kernel_names():
     assert profiling.is_decode_kernel(dec)
     assert profiling.is_decode_kernel("_ZN2fl12merge_kernelIDF16bEEvPKfS2_iliPT_Pf")
     assert not profiling.is_decode_kernel(pre) and not profiling.is_decode_kernel(evo)
+
+
+def test_evoformer_traffic_table(tmp_path):
+    from flashattention_attention_variants_amd import flops
+    row = "void fl::attn_mfma_kernel<fl::MfmaCfg<32, 32, 1, 2, 0, true, true, true, false> >(fl::KernelArgs)"
+    col = "void fl::attn_mfma_kernel<fl::MfmaCfg<32, 32, 1, 1, 0, false, true, true, false> >(fl::KernelArgs)"
+    copy_kib = profiling.PROBE_COPY_BYTES / 1024
+    alg_row = flops.evoformer_bytes(128, 256, 8, 32, "row")
+    # the row launch moves exactly its algorithmic bytes, the column twice its own
+    _write_counters(tmp_path / "f", "FETCH_SIZE",
+                    [(row, 1.0), (col, 1.0), ("__amd_rocclr_copyBuffer", copy_kib),
+                     (row, alg_row / 1024), (col, 2 * flops.evoformer_bytes(128, 256, 8, 32, "col") / 1024)])
+    _write_counters(tmp_path / "w", "WRITE_SIZE",
+                    [(row, 1.0), (col, 1.0), ("__amd_rocclr_copyBuffer", copy_kib), (row, 0.0),
+                     (col, 0.0)])
+    md = profiling.evo_traffic_markdown(str(tmp_path / "f"), str(tmp_path / "w"))
+    lines = [l for l in md.splitlines() if l.startswith("| row |") or l.startswith("| col |")]
+    assert lines[0].endswith("| 1.00 |") and lines[1].endswith("| 2.00 |"), lines
