@@ -210,3 +210,31 @@ def test_bwd_validation(lib):
     assert f(params(variant=1, mask=2)) == api.FL_ERR_PARAM
     assert f(params(), dk=MISALIGNED) == api.FL_ERR_ALIGN
     assert f(params(), B=0, q=None, k=None, v=None) == api.FL_OK
+
+
+def test_span_limits(lib):
+    # Byte offsets within one (batch, head) block must stay below 2^31 for
+    # every row up to 63 past the last (a partial key tile addresses them):
+    # ((rows + 63) * row_elems + width) * 2 < 2^31.  Rejected on the host.
+    sk = 16777152  # D = 64: (S_k + 63) * 64 + 64 reaches 2^30
+    assert ((sk + 63) * 64 + 64) * 2 >= 1 << 31 and ((sk + 62) * 64 + 64) * 2 < 1 << 31
+    assert attn(lib, params(), Sq=8, Sk=sk) == api.FL_ERR_SHAPE
+    # DiffAttn with D_v = 128: the V rows set the limit
+    sv = 8388544
+    assert ((sv + 63) * 128 + 128) * 2 >= 1 << 31 and ((sv + 62) * 128 + 128) * 2 < 1 << 31
+    d = lib.fl_diffattn_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1, 2, 8, sv, 64, 128,
+                            api.FL_BF16, 0.125, 0.8, 0, None)
+    assert d == api.FL_ERR_SHAPE
+    # Evoformer column form: a row of the transposed problem is N_res*H*C apart
+    n_res, H, C = 16, 2, 32
+    ns = ((1 << 30) - C) // (n_res * H * C) - 63 + 1
+    assert ((ns + 63) * n_res * H * C + C) * 2 >= 1 << 31
+    e = lib.fl_evoformer_gated_attn_fwd(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, ns, n_res, H, C,
+                                        1, api.FL_BF16, 0.17, None)
+    assert e == api.FL_ERR_SHAPE
+    # decode: the cache capacity sets the block
+    assert decode(lib, params(), S_cap=sk, max_len=256) == api.FL_ERR_SHAPE
+    # backward: either length
+    b = lambda Sq, Sk: lib.fl_attn_bwd(*([FAKE] * 10), 1, 2, 2, Sq, Sk, 64, api.FL_BF16,
+                                       ctypes.byref(params()), None)
+    assert b(8, sk) == api.FL_ERR_SHAPE and b(sk, 8) == api.FL_ERR_SHAPE
