@@ -209,3 +209,23 @@ def test_merge_of_attention_over_key_halves():
     ro, rl = oracle.attn(np64(q), np64(k), np64(v))
     check(np64(o), ro, "f32", "merged halves")
     check(np64(lse), rl, "f32", "merged halves lse")
+
+
+def test_decode_large_cache_offsets_bshd():
+    # One sequence whose [S_cap, H_kv, D] cache block spans 1.5 GiB, so tile
+    # byte offsets run past 2^30 (the launcher's limit is 2^31).  The cache is
+    # a seeded 4096-row block repeated with a position ramp added to V, so a
+    # wrong row (or a zero read) anywhere changes the output.
+    Hq, Hkv, D, S_cap = 4, 4, 64, 3_000_000
+    L = S_cap - 37
+    q, kb, vb = inputs.decode_inputs(1, Hq, Hkv, 1, 4096, D, seed=990, layout="bshd")
+    reps = (S_cap + 4095) // 4096
+    kc = kb.repeat(1, reps, 1, 1)[:, :S_cap].contiguous()
+    ramp = torch.linspace(-1.0, 1.0, S_cap, dtype=torch.float32).view(1, S_cap, 1, 1)
+    vc = (vb.repeat(1, reps, 1, 1)[:, :S_cap].float() + ramp).to(torch.bfloat16).contiguous()
+    seqlens = torch.tensor([L], dtype=torch.int32)
+    o, lse = run_decode(q, kc, vc, seqlens, layout="bshd", variant="causal", num_splits=0)
+    ro, rl = run_oracle(q, kc, vc, seqlens, layout="bshd", variant="causal")
+    check(np64(o), ro, "bf16", "1.5 GiB cache block")
+    mx, _, _ = errors(np64(lse), rl)
+    assert mx <= 2e-2, "lse %g" % mx
