@@ -167,7 +167,7 @@ def test_decode_split_choice(lib):
     assert ns(2, 8, 2, 1, 256, 100) == 4          # capped at the 4 tiles of 64 keys
     assert ns(1, 8, 8, 1, 300, 2) == 2
     # chosen: enough work-groups, but ranges of at least 16 tiles
-    assert ns(64, 32, 8, 1, 8192, 0) == 4         # 512 (sequence, head) pairs x 4
+    assert ns(64, 32, 8, 1, 8192, 0) == 8         # 512 (sequence, head) pairs x 8
     assert ns(1, 32, 8, 1, 8192, 0) == 8          # 128 tiles / 16
     assert ns(1, 32, 8, 1, 1024, 0) == 1
     # a sliding window bounds the keys a row needs, whatever the cache length
