@@ -111,6 +111,12 @@ struct MfmaCfg {
   static_assert(!(ALIBI_FOLD && KMASK), "ALiBi and the key mask share a folded k-slot");
   // bounded softcap: fixed reference 0
   static constexpr bool SCAPB = MOD == MOD_SOFTCAP_BOUNDED;
+  // Plain folded scores (no ALiBi, key mask, bias; one stream; not decode or
+  // gated): a first pass keeps the reference m = 0 with no per-unit test and
+  // sums rows on the matrix cores; if any row of the work-group ends outside
+  // [2^-64, 2^100] (or not finite) with keys allowed, the pass is discarded
+  // and the checked pass runs instead.
+  static constexpr bool FASTP = (MOD == MOD_NONE) && !BIAS_ && !KMASK_ && !GATE_ && !DEC_ && NS_ == 1;
   static_assert(!SCAPB || (!BIAS && !KMASK), "bounded softcap takes no bias or key mask");
   static_assert(!DEC || (QB == 1 && NS == 1 && !BIAS && !KMASK && !GATE), "decode form");
   static_assert(STAGES >= 3 && STAGES <= 6, "pipeline depth");
@@ -424,7 +430,7 @@ void attn_mfma_kernel(KernelArgs a) {
   // 16x16 accumulator (registers 0 and 1 of lanes 0..15) collect them.
   f32x4 lacc[NSU][QB];
   bf16x8 lsel = {};
-  if constexpr (C::SCAPB) {
+  if constexpr (C::SCAPB || C::FASTP) {
     const int m = lane & 15, kgrp = lane >> 4;
     const bf16 v = (bf16)((m == 0 && (kgrp & 1) == 0) || (m == 1 && (kgrp & 1) == 1) ? 1.0f : 0.0f);
     lsel = bf16x8{v, v, v, v, v, v, v, v};
@@ -652,9 +658,10 @@ void attn_mfma_kernel(KernelArgs a) {
   // Consume tile kt from LDS stage `stage`.  Folded scores: FOLDED adds the
   // extra k-step to every S^T product; without it the tile assumes that
   // every row of the wave still has the reference m = 0 (see need_fold).
-  auto compute_tile = [&](int stage, int kt, auto masked_tag, auto folded_tag) {
+  auto compute_tile = [&](int stage, int kt, auto masked_tag, auto folded_tag, auto fast_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     constexpr bool FOLDED = decltype(folded_tag)::value;
+    constexpr bool FAST = decltype(fast_tag)::value;
     constexpr int U = NSU * 2 * QB;
     cur_stage = stage;
     const bf16* ks = lds + stage * C::STAGE;
@@ -707,7 +714,7 @@ void attn_mfma_kernel(KernelArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = fast_exp2(x[8 * h2 + e] - shift);
         pk[h2] = __builtin_convertvector(p, bf16x8);
-        if constexpr (C::SCAPB) continue;  // summed by the matrix cores
+        if constexpr (C::SCAPB || FAST) continue;  // summed by the matrix cores
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           bf16x2 pr = {pk[h2][e], pk[h2][e + 1]};
@@ -768,6 +775,12 @@ void attn_mfma_kernel(KernelArgs a) {
           x[r] = fmaf(fast_rcp(fast_exp2(sc[r]) + 1.0f), -2.0f * c2, c2);
         if constexpr (MASKED) mask(x, kb, qb);
         exp_pack(x, pk, 0.0f);
+        lacc[s][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pk[0], lacc[s][qb], 0, 0, 0);
+        lacc[s][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pk[1], lacc[s][qb], 0, 0, 0);
+      } else if constexpr (FAST) {
+        // first pass: reference 0 throughout, rows summed by the matrix cores
+        if constexpr (MASKED) mask(sc, kb, qb);
+        exp_pack(sc, pk, 0.0f);
         lacc[s][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pk[0], lacc[s][qb], 0, 0, 0);
         lacc[s][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pk[1], lacc[s][qb], 0, 0, 0);
       } else if constexpr (C::FOLD) {
@@ -967,8 +980,9 @@ void attn_mfma_kernel(KernelArgs a) {
   };
   // normalise, combine, gate and store the rows of batch entry b
   // the full row sum of this lane's row (both lane halves)
+  bool fast_ok = false;  // the first pass stands (its sums are in lacc)
   auto row_sum = [&](int s, int qb) {
-    if constexpr (C::SCAPB) {
+    if (C::SCAPB || (C::FASTP && fast_ok)) {
       const float l0 = __shfl(lacc[s][qb][0], c & 15);
       const float l1 = __shfl(lacc[s][qb][1], c & 15);
       return c < 16 ? l0 : l1;
@@ -1085,7 +1099,53 @@ void attn_mfma_kernel(KernelArgs a) {
     else
       load_tile(b, tile_of(it), stage);
   };
-  if (n_total > 0) {
+  if constexpr (C::FASTP) {
+    using F = std::integral_constant<bool, false>;
+    using T = std::integral_constant<bool, true>;
+    if (n_total > 0) {
+      issue(0, 0);
+#pragma unroll
+      for (int t = 1; t < AHEAD; ++t)
+        if (t < n_total) issue(t, t);
+      sync_tile(min(AHEAD, n_total) - 1);
+    }
+    for (int it = 0; it < n_total; ++it) {
+      const int kt = tile_of(it);
+      const int stage = it % C::STAGES;
+      const int j0 = kt * BN, j1 = j0 + BN - 1;
+      const bool empty = wave_idle || j0 > w_hi_max || j1 < w_lo_min;
+      const bool full = j0 >= w_lo_max && j1 <= w_hi_min;
+      if (it + AHEAD < n_total) issue(it + AHEAD, stage == 0 ? C::STAGES - 1 : stage - 1);
+      if (!empty) {
+        if (full)
+          compute_tile(stage, kt, F{}, F{}, T{});
+        else
+          compute_tile(stage, kt, T{}, F{}, T{});
+      }
+      if (it + 1 < n_total) sync_tile(min(AHEAD - 1, n_total - 2 - it));
+    }
+    // every row with allowed keys must end with a sum in [2^-64, 2^100]:
+    // then no term overflowed and the largest terms stayed normal
+    bool bad = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float l0 = __shfl(lacc[0][qb][0], c & 15);
+      const float l1 = __shfl(lacc[0][qb][1], c & 15);
+      const float l = c < 16 ? l0 : l1;
+      const bool has = row_lo[qb] <= row_hi[qb];
+      bad |= (has & !(l >= 0x1p-64f)) | !(l <= 0x1p100f);
+    }
+    __shared__ int pass_bad;
+    if (tid == 0) pass_bad = 0;
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) pass_bad = 1;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    fast_ok = pass_bad == 0;
+    if (!fast_ok) reset_state();
+  }
+  if (C::FASTP && fast_ok) {
+    // the first pass stands
+  } else if (n_total > 0) {
     // the key-mask column of a tile goes to LDS one step after its load
     // was issued; the prologue stores all but the newest
     issue(0, 0);
@@ -1099,7 +1159,8 @@ void attn_mfma_kernel(KernelArgs a) {
     if (n_total < AHEAD) store_kmask(n_total - 1);
     sync_tile(min(AHEAD, n_total) - 1);
   }
-  for (int it = 0; it < n_total; ++it) {
+  const int n_careful = C::FASTP && fast_ok ? 0 : n_total;  // tiles of the checked pass
+  for (int it = 0; it < n_careful; ++it) {
     const int kt = C::PERSIST ? tile_of(it % n_kt) : tile_of(it);
     const int stage = it % C::STAGES;
     const bool next = it + 1 < n_total, next2 = it + AHEAD < n_total;
@@ -1114,14 +1175,14 @@ void attn_mfma_kernel(KernelArgs a) {
       using T = std::integral_constant<bool, true>;
       if (!C::FOLD || C::ALIBI_FOLD || C::KMASK || need_fold) {
         if (full)
-          compute_tile(stage, kt, F{}, T{});
+          compute_tile(stage, kt, F{}, T{}, F{});
         else
-          compute_tile(stage, kt, T{}, T{});
+          compute_tile(stage, kt, T{}, T{}, F{});
       } else if constexpr (C::FOLD && !C::ALIBI_FOLD && !C::KMASK) {
         if (full)
-          compute_tile(stage, kt, F{}, F{});
+          compute_tile(stage, kt, F{}, F{}, F{});
         else
-          compute_tile(stage, kt, T{}, F{});
+          compute_tile(stage, kt, T{}, F{}, F{});
       }
     }
     bool boundary = false;
