@@ -102,8 +102,6 @@ struct MfmaCfg {
   static constexpr bool GATE_LDS = GATE && QB == 2;
   static constexpr int G_ELEMS = GATE_LDS ? BM * DV : 0;
   static constexpr int GCH = G_ELEMS / 8 / (NW * 64);  // 16-byte gate chunks per thread
-  // Folded scores: the scale, the running reference and (for ALiBi) the
-  // distance penalty all enter the S^T product itself.
   // Folded scores: the scale, the running reference, the ALiBi distance
   // penalty or the key mask all enter the S^T product itself.
   static constexpr bool FOLD = (MOD == MOD_NONE || MOD == MOD_ALIBI) && !BIAS;
@@ -111,12 +109,12 @@ struct MfmaCfg {
   static_assert(!(ALIBI_FOLD && KMASK), "ALiBi and the key mask share a folded k-slot");
   // bounded softcap: fixed reference 0
   static constexpr bool SCAPB = MOD == MOD_SOFTCAP_BOUNDED;
-  // Plain folded scores (no ALiBi, key mask, bias; one stream; not decode or
-  // gated): a first pass keeps the reference m = 0 with no per-unit test and
-  // sums rows on the matrix cores; if any row of the work-group ends outside
-  // [2^-64, 2^100] (or not finite) with keys allowed, the pass is discarded
-  // and the checked pass runs instead.
-  static constexpr bool FASTP = (MOD == MOD_NONE) && !BIAS_ && !KMASK_ && !GATE_ && !DEC_ && NS_ == 1;
+  // Folded scores without a key mask (plain or ALiBi; one stream; not decode
+  // or gated): a first pass keeps the reference m = 0 with no per-unit test
+  // and sums rows on the matrix cores; if any row of the work-group ends
+  // outside [2^-64, 2^100] (or not finite) with keys allowed, the pass is
+  // discarded and the checked pass runs instead.
+  static constexpr bool FASTP = FOLD && !KMASK && !GATE && !DEC && NS == 1;
   static_assert(!SCAPB || (!BIAS && !KMASK), "bounded softcap takes no bias or key mask");
   static_assert(!DEC || (QB == 1 && NS == 1 && !BIAS && !KMASK && !GATE), "decode form");
   static_assert(STAGES >= 3 && STAGES <= 6, "pipeline depth");
@@ -779,6 +777,7 @@ void attn_mfma_kernel(KernelArgs a) {
         lacc[s][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pk[1], lacc[s][qb], 0, 0, 0);
       } else if constexpr (FAST) {
         // first pass: reference 0 throughout, rows summed by the matrix cores
+        alibi_fix(j0, sc, kb, qb);
         if constexpr (MASKED) mask(sc, kb, qb);
         exp_pack(sc, pk, 0.0f);
         lacc[s][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pk[0], lacc[s][qb], 0, 0, 0);
@@ -1102,6 +1101,7 @@ void attn_mfma_kernel(KernelArgs a) {
   if constexpr (C::FASTP) {
     using F = std::integral_constant<bool, false>;
     using T = std::integral_constant<bool, true>;
+    using FD = std::integral_constant<bool, C::ALIBI_FOLD>;  // the penalty rides on the fold
     if (n_total > 0) {
       issue(0, 0);
 #pragma unroll
@@ -1118,9 +1118,9 @@ void attn_mfma_kernel(KernelArgs a) {
       if (it + AHEAD < n_total) issue(it + AHEAD, stage == 0 ? C::STAGES - 1 : stage - 1);
       if (!empty) {
         if (full)
-          compute_tile(stage, kt, F{}, F{}, T{});
+          compute_tile(stage, kt, F{}, FD{}, T{});
         else
-          compute_tile(stage, kt, T{}, F{}, T{});
+          compute_tile(stage, kt, T{}, FD{}, T{});
       }
       if (it + 1 < n_total) sync_tile(min(AHEAD - 1, n_total - 2 - it));
     }
