@@ -245,6 +245,60 @@ __device__ __forceinline__ void unit_hint_scapb() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Document mask work order.  A query tile costs as many key tiles as its
+// rows' documents span, which varies along the sequence, so the plain order
+// can leave a long tile for the end of the grid.  Here the (batch entry,
+// query tile) items go out longest first, the heads of one item adjacent
+// (work-group id = rank * H + head).  Every work-group ranks all items
+// itself in LDS: it needs no buffer and no second launch, and the keys
+// (span, index) are unique, so the ranks form a permutation whatever the
+// offsets hold.  `ws` needs room for kDocOrderMaxOffsets + 2 NT ints.
+// Returns false (the caller keeps the plain order) when the items outnumber
+// the work-group's NT threads or the offsets do not fit.
+constexpr int kDocOrderMaxOffsets = 1024;
+template <int NT, int BN>
+__device__ bool doc_order_tile(const KernelArgs& a, int bm, int* ws, int& bh, int& qt) {
+  const int n = a.nb * a.n_qt, n_off = a.nb * (a.n_docs + 1);
+  if (n > NT || n_off > kDocOrderMaxOffsets) return false;
+  const int tid = threadIdx.x;
+  int* off = ws;
+  int* key = ws + kDocOrderMaxOffsets;
+  int* perm = key + NT;
+  for (int t = tid; t < n_off; t += NT) off[t] = a.doc_offsets[t];
+  __syncthreads();
+  if (tid < n) {
+    const int b = tid / a.n_qt, t = tid % a.n_qt;
+    const int* o = off + b * (a.n_docs + 1);
+    // the document of row i: the largest d < n_docs with o[d] <= i
+    auto doc_of = [&](int i) {
+      int lo = 0, hi = a.n_docs - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (o[mid] <= i) lo = mid; else hi = mid - 1;
+      }
+      return lo;
+    };
+    // rows' key intervals are monotone: the tile spans lo(first) .. hi(last)
+    const int q0 = t * bm, q1 = min(q0 + bm, a.sq) - 1;
+    const int lo = max(o[doc_of(q0)], 0), hi = min(o[doc_of(q1) + 1] - 1, a.sk - 1);
+    const int span = lo <= hi ? hi / BN - lo / BN + 1 : 0;
+    key[tid] = (min(span, 0x7fff) << 16) | (0xffff - tid);
+  }
+  __syncthreads();
+  if (tid < n) {
+    const int mine = key[tid];
+    int rank = 0;
+    for (int j = 0; j < n; ++j) rank += key[j] > mine;
+    perm[rank] = tid;
+  }
+  __syncthreads();
+  const int item = perm[blockIdx.x / a.nh];
+  __syncthreads();  // the LDS holds K/V tiles next
+  bh = (item / a.n_qt) * a.nh + blockIdx.x % a.nh;
+  qt = item % a.n_qt;
+  return true;
+}
+
 template <class C>
 __global__ __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_EU)))
 void attn_mfma_kernel(KernelArgs a) {
@@ -285,7 +339,10 @@ void attn_mfma_kernel(KernelArgs a) {
     n_rep = min(a.rows_per_wg, a.nb - b_first);
     bh = b_first * a.nh + hh;
   } else {
-    decode_tile(a, blockIdx.x, bh, qt);
+    static_assert(sizeof(lds) >= (kDocOrderMaxOffsets + 2 * C::NW * 64) * sizeof(int),
+                  "LDS for the document order");
+    if (!(a.doc_order && doc_order_tile<C::NW * 64, BN>(a, C::BM, (int*)lds, bh, qt)))
+      decode_tile(a, blockIdx.x, bh, qt);
   }
   int b = bh / a.nh;  // the batch entry whose rows are in flight
   const int h = bh % a.nh, hk = h / a.group;

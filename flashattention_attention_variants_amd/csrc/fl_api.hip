@@ -150,6 +150,7 @@ int variant_args(const fl_attn_params* p, int S_k, KernelArgs& a) {
       a.iv_kind = IV_DOCUMENT;
       a.n_docs = p->n_docs;
       a.doc_offsets = p->doc_offsets;
+      a.doc_order = 1;
       break;
     default:
       break;

@@ -67,6 +67,7 @@ struct KernelArgs {
   float alibi_max_bias;
   float lambda;
   int heavy_first;             // schedule the most expensive query tiles first
+  int doc_order;               // document mask: deal query tiles longest first
   int head_major;              // deal a head's query tiles to its XCD consecutively
   int alibi_nh;                // query heads in the ALiBi slope formula
   int rows_per_wg;             // gated launches: batch entries per work-group

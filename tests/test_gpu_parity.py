@@ -103,6 +103,24 @@ def test_bf16_variants(variant, S):
     assert mx <= 2e-2, "lse %g" % mx
 
 
+@pytest.mark.parametrize("B,S,n_docs,H", [(3, 1000, 5, 2), (2, 640, 40, 2), (1, 300, 300, 1),
+                                          (2, 2048, 2, 8), (52, 520, 3, 1)])
+def test_document_work_order(B, S, n_docs, H):
+    """Under the document mask the (batch entry, query tile) items go out
+    longest first when one work-group can rank them (at most 256 items and
+    1024 offsets), else in the plain order: 52 entries of 520 rows are 260
+    items and take the plain order, the rest the ranked one, with documents
+    of one row each, many short ones, a few long ones and two per entry
+    across eight heads.  Every row is compared with the oracle."""
+    q, k, v = inputs.attn_inputs(B, H, H, S, S, 64, "bf16", seed=400 + S)
+    kw = dict(variant="document", doc_offsets=inputs.doc_offsets(B, S, n_docs, seed=401 + S))
+    o, lse = run_gpu_attn(q, k, v, **kw)
+    ro, rl = run_oracle_attn(q, k, v, **kw)
+    check(np64(o), ro, "bf16", "document B=%d S=%d docs=%d" % (B, S, n_docs))
+    mx, _, _ = errors(np64(lse), rl)
+    assert mx <= 2e-2, "lse %g" % mx
+
+
 @pytest.mark.parametrize("window_causal", [True, False])
 @pytest.mark.parametrize("window", [1, 64, 100, 1000])
 def test_bf16_window_shapes(window, window_causal):
