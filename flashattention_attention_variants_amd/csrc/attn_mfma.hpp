@@ -109,12 +109,13 @@ struct MfmaCfg {
   static_assert(!(ALIBI_FOLD && KMASK), "ALiBi and the key mask share a folded k-slot");
   // bounded softcap: fixed reference 0
   static constexpr bool SCAPB = MOD == MOD_SOFTCAP_BOUNDED;
-  // Folded scores without a key mask (plain or ALiBi; one stream; not decode
-  // or gated): a first pass keeps the reference m = 0 with no per-unit test
-  // and sums rows on the matrix cores; if any row of the work-group ends
-  // outside [2^-64, 2^100] (or not finite) with keys allowed, the pass is
-  // discarded and the checked pass runs instead.
-  static constexpr bool FASTP = FOLD && !KMASK && !GATE && !DEC && NS == 1;
+  // Folded scores without a key mask (plain or ALiBi) and the bounded
+  // softcap (one stream; not decode or gated): a first pass keeps a fixed
+  // reference (0; c = cap log2(e) for the softcap) with no per-unit test and
+  // sums rows on the matrix cores; if any row of the work-group ends with a
+  // sum out of range (or not finite) with keys allowed, the pass is
+  // discarded and the checked pass (for the softcap: reference 0) runs.
+  static constexpr bool FASTP = (FOLD || SCAPB) && !KMASK && !GATE && !DEC && NS == 1;
   static_assert(!SCAPB || (!BIAS && !KMASK), "bounded softcap takes no bias or key mask");
   static_assert(!DEC || (QB == 1 && NS == 1 && !BIAS && !KMASK && !GATE), "decode form");
   static_assert(STAGES >= 3 && STAGES <= 6, "pipeline depth");
@@ -424,9 +425,21 @@ void attn_mfma_kernel(KernelArgs a) {
   // ---- Q operands in registers ---------------------------------------------
   // B operand of S^T = K Q^T: lane (c, g) holds Q[row c][16t + 8g .. +7].
   // Folded scores: Q is pre-multiplied by scale*log2(e) (one bf16 rounding),
-  // so S^T comes out in base-2 units; bounded softcap: by the tanh argument
-  // 2*scale*log2(e)/cap, so S^T is t below.
+  // so S^T comes out in base-2 units; bounded softcap: by the power-of-two
+  // part of the tanh argument 2*scale*log2(e)/cap (exact), so S^T is t / scap_m.
+  // (Folded scores likewise take only the power-of-two part of the scale.)
   bf16x8 qreg[NSU][QB][DQK / 16];
+  // bounded softcap: tanh argument = scap_m * scap_q, scap_q a power of two
+  int scap_e = 0;
+  const float scap_m = C::SCAPB ? frexpf(a.softcap_arg, &scap_e) : 1.0f;
+  const float scap_q = C::SCAPB ? ldexpf(1.0f, scap_e) : 1.0f;
+  // folded scores: scale*log2(e) = fold_m * fold_q, fold_q a power of two.
+  // Q takes fold_q (exact), so S^T, the folded terms and the running
+  // reference are in units of 1/fold_m base-2 units; fold_m enters where
+  // a term is exponentiated (one fused multiply-add per score).
+  int fold_e = 0;
+  const float fold_m = C::FOLD ? frexpf(a.scale_log2, &fold_e) : 1.0f;
+  const float fold_q = C::FOLD ? ldexpf(1.0f, fold_e) : 1.0f;
   auto load_q = [&](int bb) {
 #pragma unroll
     for (int s = 0; s < NSU; ++s) {
@@ -441,9 +454,10 @@ void attn_mfma_kernel(KernelArgs a) {
         for (int t = 0; t < DQK / 16; ++t) {
           qreg[s][qb][t] = load16(qrs, (32 * qb + c) * (int)q_row_b + 32 * t + 16 * g);
           if constexpr (C::FOLD || C::SCAPB) {
-            // folded: scale*log2(e); bounded softcap: the tanh argument
-            // 2*scale*log2(e)/cap, so that S^T is 2^t's exponent at once
-            const float qs = C::FOLD ? a.scale_log2 : a.softcap_arg;
+            // folded: scale*log2(e); bounded softcap: the power-of-two part
+            // of the tanh argument 2*scale*log2(e)/cap (exact in bf16; the
+            // mantissa multiplies each score)
+            const float qs = C::FOLD ? fold_q : scap_q;
             f32x8 f = __builtin_convertvector(qreg[s][qb][t], f32x8);
             qreg[s][qb][t] = __builtin_convertvector(f * qs, bf16x8);
           }
@@ -520,15 +534,16 @@ void attn_mfma_kernel(KernelArgs a) {
   // decode rows of one K/V head belong to G query heads with their own slopes
   const int h_alibi = C::DEC ? hk * a.grp + min(wq0 + c, a.sq - 1) / a.sq_new : h;
   const float alibi_l2 = C::MOD == MOD_ALIBI ? alibi_slope_log2(a, h_alibi) : 0.0f;
+  const float alibi_f = alibi_l2 / fold_m;  // the folded slope, in the units of S^T
   bf16 sl0, sl1, sl2;
-  split3(alibi_l2, sl0, sl1, sl2);
+  split3(alibi_f, sl0, sl1, sl2);
   // query-side operand for reference m (bf16-exact) and, under ALiBi, the
   // tile at j0
   auto set_qext = [&](int s, int qb, float m, int j0) {
     const bf16 mt = (bf16)(-m);
     if constexpr (C::ALIBI_FOLD) {
       bf16 x0, x1, x2;
-      split3(-alibi_l2 * (float)(lane_pos[qb] - j0), x0, x1, x2);
+      split3(-alibi_f * (float)(lane_pos[qb] - j0), x0, x1, x2);
       qext[s][qb] = bf16x8{mt, x0, x1, x2, sl0, sl1, sl2, zero};
     } else if constexpr (C::KMASK) {
       qext[s][qb] = bf16x8{mt, one, zero, zero, zero, zero, zero, zero};
@@ -697,7 +712,7 @@ void attn_mfma_kernel(KernelArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int dj = j0 + 32 * kb + 4 * g + acc_row(r) - qi;
-          acc[r] = dj > 0 ? acc[r] - 2.0f * alibi_l2 * (float)dj : acc[r];
+          acc[r] = dj > 0 ? acc[r] - 2.0f * alibi_f * (float)dj : acc[r];
         }
       }
     }
@@ -710,6 +725,7 @@ void attn_mfma_kernel(KernelArgs a) {
     if constexpr (C::FOLD && decltype(folded_tag)::value) fold(j0, s, kb, qb, acc);
   };
 
+  const float scap_k = C::SCAPB ? 0.5f / a.softcap_log2 : 0.0f;  // 1 / (2c)
   // Consume tile kt from LDS stage `stage`.  Folded scores: FOLDED adds the
   // extra k-step to every S^T product; without it the tile assumes that
   // every row of the wave still has the reference m = 0 (see need_fold).
@@ -758,16 +774,19 @@ void attn_mfma_kernel(KernelArgs a) {
         acc[r] = (j >= row_lo[qb] && j <= row_hi[qb]) ? acc[r] : kNegInf;
       }
     };
-    // p = 2^(x - shift) of a unit's 16 scores, rounded to bf16 in the
+    // p = 2^(x - shift) of a unit's 16 scores (folded scores: x and shift
+    // in the units of S^T, 2^(fold_m (x - shift))), rounded to bf16 in the
     // B-operand order of the P.V product (16-key steps 2kb and 2kb+1);
     // returns this lane's sum of the rounded values.
     auto exp_pack = [&](const f32x16& x, bf16x8 (&pk)[2], float shift) {
       float part[2] = {0.0f, 0.0f};  // two partial sums keep the add chain short
+      const float fshift = shift * fold_m;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         f32x8 p;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = fast_exp2(x[8 * h2 + e] - shift);
+        for (int e = 0; e < 8; ++e)
+          p[e] = fast_exp2(C::FOLD ? fmaf(x[8 * h2 + e], fold_m, -fshift) : x[8 * h2 + e] - shift);
         pk[h2] = __builtin_convertvector(p, bf16x8);
         if constexpr (C::SCAPB || FAST) continue;  // summed by the matrix cores
 #pragma unroll
@@ -818,16 +837,28 @@ void attn_mfma_kernel(KernelArgs a) {
       const int jb = j0 + 32 * kb + 4 * g;  // key of register 0 in this lane
       bf16x8 pk[2];
 
-      if constexpr (C::SCAPB) {
-        // With t = 2 y log2(e) for y = scale q.k / cap (S^T holds t), the softcapped
-        // base-2 score is cap log2(e) tanh(y) = c - 2c / (2^t + 1), where
-        // c = cap log2(e) <= 100: the terms 2^score stay within fp32's normal
-        // range with the fixed reference 0.
+      if constexpr (C::SCAPB && FAST) {
+        // first pass, reference c: 2^(score - c) = 2^(-2c / (2^t + 1)) lies in
+        // (2^-2c, 1]; 1 / (2c) folds into one fused multiply-add before the
+        // reciprocal, and the exponential takes the negation as a modifier
+        f32x16 x;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          x[r] = -fast_rcp(fmaf(fast_exp2(sc[r] * scap_m), scap_k, scap_k));
+        if constexpr (MASKED) mask(x, kb, qb);
+        exp_pack(x, pk, 0.0f);
+        lacc[s][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pk[0], lacc[s][qb], 0, 0, 0);
+        lacc[s][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pk[1], lacc[s][qb], 0, 0, 0);
+      } else if constexpr (C::SCAPB) {
+        // With t = 2 y log2(e) for y = scale q.k / cap (S^T holds t / scap_m),
+        // the softcapped base-2 score is cap log2(e) tanh(y) = c - 2c / (2^t + 1),
+        // where c = cap log2(e) <= 100: the terms 2^score stay within fp32's
+        // normal range with the fixed reference 0.
         const float c2 = a.softcap_log2;
         f32x16 x;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          x[r] = fmaf(fast_rcp(fast_exp2(sc[r]) + 1.0f), -2.0f * c2, c2);
+          x[r] = fmaf(fast_rcp(fast_exp2(sc[r] * scap_m) + 1.0f), -2.0f * c2, c2);
         if constexpr (MASKED) mask(x, kb, qb);
         exp_pack(x, pk, 0.0f);
         lacc[s][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lsel, pk[0], lacc[s][qb], 0, 0, 0);
@@ -873,9 +904,10 @@ void attn_mfma_kernel(KernelArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) xm = fmaxf(xm, rs[r]);
           xm = fmaxf(xm, __shfl_xor(xm, 32));
-          // move when terms reach 2^32, or when the row (both lane halves,
-          // this unit included) has no mass and its terms are below 2^-32;
-          // both halves of a row decide alike
+          // move when the row maximum passes 32 units of S^T (terms of 2^16
+          // to 2^32), or when the row (both lane halves, this unit included)
+          // has no mass and its maximum is below -32 units; both halves of a
+          // row decide alike
           const float lr = l_run[s][qb] + lsum;
           const float l_row = lr + __shfl_xor(lr, 32);
           const bool move = xm != kNegInf && (xm > 32.0f || (l_row == 0.0f && xm < -32.0f));
@@ -885,7 +917,7 @@ void attn_mfma_kernel(KernelArgs a) {
           const float shift = m_new - m_run[s][qb];
           // (a row without mass has nothing to rescale; moving its reference
           // down could overflow the factor)
-          const float alpha = !move ? 1.0f : (l_run[s][qb] == 0.0f ? 0.0f : fast_exp2(-shift));
+          const float alpha = !move ? 1.0f : (l_run[s][qb] == 0.0f ? 0.0f : fast_exp2(-shift * fold_m));
           l_run[s][qb] *= alpha;
 #pragma unroll
           for (int db = 0; db < DV / 32; ++db) oacc[s][qb][db] *= alpha;
@@ -1062,7 +1094,7 @@ void attn_mfma_kernel(KernelArgs a) {
         const int qi = wq0 + 32 * qb + c;
         float* lse_out = a.lse[stream_of(s)];
         if (lse_out && g == 0 && qi < a.sq) {
-          const float m = m_run[s][qb];
+          const float m = m_run[s][qb] * fold_m;  // base-2 units
           const float lse = l > 0.0f ? (m + __builtin_log2f(l)) * kLn2 : kNegInf;
           lse_out[b * a.lse_sb + h * a.lse_sh + qi] = lse;
         }
@@ -1155,7 +1187,10 @@ void attn_mfma_kernel(KernelArgs a) {
     else
       load_tile(b, tile_of(it), stage);
   };
-  if constexpr (C::FASTP) {
+  // The softcap pass runs against the reference c = cap log2(e): it is
+  // tried for c <= 76, where rows of scores near 0 end far above its bound.
+  const bool fast_try = !C::SCAPB || a.softcap_log2 <= 76.0f;
+  if constexpr (C::FASTP) if (fast_try) {
     using F = std::integral_constant<bool, false>;
     using T = std::integral_constant<bool, true>;
     using FD = std::integral_constant<bool, C::ALIBI_FOLD>;  // the penalty rides on the fold
@@ -1181,8 +1216,12 @@ void attn_mfma_kernel(KernelArgs a) {
       }
       if (it + 1 < n_total) sync_tile(min(AHEAD - 1, n_total - 2 - it));
     }
-    // every row with allowed keys must end with a sum in [2^-64, 2^100]:
-    // then no term overflowed and the largest terms stayed normal
+    // Every row with allowed keys must end with a sum in [lo, 2^100]: then no
+    // term overflowed, and the largest is at least lo / S_k, so the terms
+    // below fp32's normal range (2^-126) that may have been lost hold at most
+    // S_k 2^-126 / lo of the mass: under 2^-22 for S_k <= 2^24 with the
+    // softcap's lo = 2^-80 (terms relative to 2^c), far less with 2^-64.
+    constexpr float lo = C::SCAPB ? 0x1p-80f : 0x1p-64f;
     bool bad = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -1190,7 +1229,7 @@ void attn_mfma_kernel(KernelArgs a) {
       const float l1 = __shfl(lacc[0][qb][1], c & 15);
       const float l = c < 16 ? l0 : l1;
       const bool has = row_lo[qb] <= row_hi[qb];
-      bad |= (has & !(l >= 0x1p-64f)) | !(l <= 0x1p100f);
+      bad |= (has & !(l >= lo)) | !(l <= 0x1p100f);
     }
     __shared__ int pass_bad;
     if (tid == 0) pass_bad = 0;
@@ -1199,6 +1238,12 @@ void attn_mfma_kernel(KernelArgs a) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     fast_ok = pass_bad == 0;
     if (!fast_ok) reset_state();
+    if constexpr (C::SCAPB) {
+      // the softcap pass ran against the reference c
+      if (fast_ok)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) m_run[0][qb] = a.softcap_log2;
+    }
   }
   if (C::FASTP && fast_ok) {
     // the first pass stands
@@ -1298,7 +1343,7 @@ void attn_mfma_kernel(KernelArgs a) {
       if (qi < a.sq) {
         const int64_t prow = ((int64_t)(split * a.nb + b) * a.nh + h) * a.sq + qi;
         if (g == 0)
-          a.lse_part[prow] = l > 0.0f ? (m_run[0][0] + __builtin_log2f(l)) * kLn2 : kNegInf;
+          a.lse_part[prow] = l > 0.0f ? (m_run[0][0] * fold_m + __builtin_log2f(l)) * kLn2 : kNegInf;
         float* op = a.o_part + prow * DV;
 #pragma unroll
         for (int db = 0; db < DV / 32; ++db)

@@ -180,7 +180,7 @@ def test_softcap_small_cap_sharpened():
     assert np.abs(ro - rv).max() > 0.3
 
 
-@pytest.mark.parametrize("cap", [2.0, 30.0, 80.0, 400.0])
+@pytest.mark.parametrize("cap", [2.0, 30.0, 60.0, 80.0, 400.0])
 @pytest.mark.parametrize("S", [77, 300])
 def test_softcap_caps_and_extremes(cap, S):
     """Softcap over a range of caps on both kernel paths (cap log2(e) <= 100
@@ -195,6 +195,34 @@ def test_softcap_caps_and_extremes(cap, S):
         ro, rl = run_oracle_attn(q, k, v, variant=variant, softcap=cap)
         check(np64(o), ro, "bf16", "softcap %g S=%d" % (cap, S))
         assert np.abs(np64(lse) - rl).max() < 2e-2 * max(1.0, np.abs(rl).max() / 64)
+
+
+@pytest.mark.parametrize("case", ["low", "mixed"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_softcap_first_pass_fallback(case, causal):
+    """cap = 50 (c = cap log2(e) = 72.1): the first pass takes its terms
+    relative to 2^c.  Rows whose every score sits near -cap end with sums
+    near S_k 2^-2c, below its bound, and their work-group must redo the tile
+    walk against the reference 0.  'low' makes every row so, 'mixed' only
+    the rows from 150 on (the first work-group's rows pass, the others fall
+    back); O and LSE against the oracle."""
+    B, H, S, D = 1, 2, 300, 64
+    q, k, v = inputs.attn_inputs(B, H, H, S, S, D, "bf16", seed=66)
+    u = torch.full((D,), 1.0 / 8.0)  # unit vector
+    k = (k.float() * 0.1 + 20 * u).to(torch.bfloat16)
+    low = q.float() * 0.1 - 80 * u
+    if case == "low":
+        q = low.to(torch.bfloat16)
+    else:
+        q = torch.cat([q.float()[:, :, :150], low[:, :, 150:]], 2).to(torch.bfloat16)
+    kw = dict(variant="softcap", softcap=50.0)
+    if causal:
+        kw["mask"] = "causal"
+    o, lse = run_gpu_attn(q, k, v, **kw)
+    ro, rl = run_oracle_attn(q, k, v, **kw)
+    check(np64(o), ro, "bf16", "softcap fallback %s causal=%s" % (case, causal))
+    assert np.abs(np64(lse) - rl).max() < 2e-2, np.abs(np64(lse) - rl).max()
+    assert rl[:, :, 150:].max() < -40  # the low rows really are near -cap
 
 
 def test_alibi_closed_form_on_gpu():
@@ -252,6 +280,24 @@ def test_bf16_extreme_scores(variant, case):
     assert np.abs(np64(lse) - rl).max() < 1e-2, np.abs(np64(lse) - rl).max()
     if case == "low":
         assert rl.max() < -100  # the scores really are that low
+
+
+@pytest.mark.parametrize("mul", [5, 25])
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_bf16_large_logits_default_scale(variant, mul):
+    """Logits of standard deviation 5 and 25 (Q scaled up) with the default
+    scale 1/sqrt(D), whose scale * log2(e) is no power of two: the kernel
+    must not round Q times that factor to bf16 (an error that grows with
+    the logits), so O stays within the bf16 tolerance of the oracle."""
+    B, H, S, D = 1, 2, 300, 64
+    q, k, v = inputs.attn_inputs(B, H, H, S, S, D, "bf16", seed=70 + mul)
+    q = (q.float() * mul).to(torch.bfloat16)
+    kw = variant_kw(variant, S, B, seed=71)
+    o, lse = run_gpu_attn(q, k, v, **kw)
+    ro, rl = run_oracle_attn(q, k, v, **kw)
+    check(np64(o), ro, "bf16", "%s logits x%d" % (variant, mul))
+    mx, _, _ = errors(np64(lse), rl)
+    assert mx <= 2e-2 * max(1.0, np.abs(rl).max() / 64), "lse %g" % mx
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
