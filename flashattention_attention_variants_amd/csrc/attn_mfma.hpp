@@ -419,6 +419,11 @@ void attn_mfma_kernel(KernelArgs a) {
       lane_pos[qb] = wq0 + 32 * qb + c;
       blk_pmin[qb] = wq0 + 32 * qb;
       blk_pmax[qb] = wq0 + 32 * qb + 31;
+      if constexpr (C::ALIBI_FOLD) {
+        // wave-uniform: the per-unit diagonal tests become scalar compares
+        blk_pmin[qb] = __builtin_amdgcn_readfirstlane(blk_pmin[qb]);
+        blk_pmax[qb] = __builtin_amdgcn_readfirstlane(blk_pmax[qb]);
+      }
     }
   }
 
