@@ -110,12 +110,12 @@ struct MfmaCfg {
   // bounded softcap: fixed reference 0
   static constexpr bool SCAPB = MOD == MOD_SOFTCAP_BOUNDED;
   // Folded scores without a key mask (plain or ALiBi) and the bounded
-  // softcap (one stream; not decode or gated): a first pass keeps a fixed
+  // softcap (one stream per wave; not decode or gated): a first pass keeps a fixed
   // reference (0; c = cap log2(e) for the softcap) with no per-unit test and
   // sums rows on the matrix cores; if any row of the work-group ends with a
   // sum out of range (or not finite) with keys allowed, the pass is
   // discarded and the checked pass (for the softcap: reference 0) runs.
-  static constexpr bool FASTP = (FOLD || SCAPB) && !KMASK && !GATE && !DEC && NS == 1;
+  static constexpr bool FASTP = (FOLD || SCAPB) && !KMASK && !GATE && !DEC && NSU == 1;
   static_assert(!SCAPB || (!BIAS && !KMASK), "bounded softcap takes no bias or key mask");
   static_assert(!DEC || (QB == 1 && NS == 1 && !BIAS && !KMASK && !GATE), "decode form");
   static_assert(STAGES >= 3 && STAGES <= 6, "pipeline depth");
@@ -1037,7 +1037,7 @@ void attn_mfma_kernel(KernelArgs a) {
       pkp[0] = pk[0];
       pkp[1] = pk[1];
       if constexpr (C::SCAPB) unit_hint_scapb();
-      else if constexpr (FAST && C::FOLD && !C::ALIBI_FOLD) unit_hint_fast();
+      else if constexpr (FAST && C::FOLD && !C::ALIBI_FOLD && NS == 1) unit_hint_fast();
     }
     if ((U - 1) % (NSU * QB) == 0) take_v();
     pv(((U - 1) / QB) % NSU, (U - 1) % QB, pkp);

@@ -368,6 +368,30 @@ def test_diffattn_small(dtype, causal, Dv):
     check(np64(o0), rv, dtype, "diffattn lambda 0")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_diffattn_one_stream_out_of_range(causal):
+    """The second stream's rows from 150 on have every score near -290 in
+    base 2 (their terms underflow against a reference of 0), the first
+    stream's stay ordinary.  The waves of the two streams share a
+    work-group, so that work-group must redo both streams with a running
+    reference; O and both LSEs against the oracle."""
+    B, H, S, D = 1, 2, 300, 64
+    q1, q2, k1, k2, v = inputs.diffattn_inputs(B, H, S, D, 128, "bf16", seed=72)
+    u = torch.full((D,), 1.0 / 8.0)  # unit vector
+    k2 = (k2.float() * 0.1 + 20 * u).to(torch.bfloat16)
+    low = q2.float() * 0.1 - 80 * u
+    q2 = torch.cat([q2.float()[:, :, :150], low[:, :, 150:]], 2).to(torch.bfloat16)
+    g = [t.to(DEV) for t in (q1, q2, k1, k2, v)]
+    o, l1, l2 = api.fl_diffattn_fwd(*g, lam=0.8, causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl1, rl2 = oracle.diffattn(*(np64(t) for t in (q1, q2, k1, k2, v)), lam=0.8, causal=causal,
+                                   scale=0.125)
+    check(np64(o), ro, "bf16", "diffattn one stream low")
+    check(np64(l1), rl1, "bf16", "lse1")
+    assert np.abs(np64(l2) - rl2).max() < 2e-2 * max(1.0, np.abs(rl2).max() / 64)
+    assert rl2[:, :, 150:].max() < -150  # the low rows really are that low
+
+
 @pytest.mark.parametrize("Dv", [64, 128])
 def test_diffattn_cross_lengths_and_cancellation(Dv):
     # 70 queries against 200 keys (a partial query tile whose missing rows
