@@ -79,6 +79,20 @@ def test_decode_small(mod, mask, splits):
             **variant_kw(mod, mask))
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("mod", MODS)
+def test_decode_large_logits(mod, splits):
+    """Query rows scaled by 25 (logits of standard deviation about 25) at the
+    default scale, whose scale * log2(e) is no power of two: the decode form
+    applies the scale exactly, so O stays within the bf16 tolerance."""
+    B, Hq, Hkv, Sq, S_cap = 3, 8, 2, 4, 500
+    q, kc, vc = inputs.decode_inputs(B, Hq, Hkv, Sq, S_cap, 64, seed=830)
+    q = (q.float() * 25).to(torch.bfloat16)
+    seqlens = torch.tensor([500, 200, 37], dtype=torch.int32)
+    compare(q, kc, vc, seqlens, "%s large logits splits=%d" % (mod, splits), num_splits=splits,
+            **variant_kw(mod, "causal"))
+
+
 @pytest.mark.parametrize("mask", MASKS)
 @pytest.mark.parametrize("mod", MODS)
 def test_decode_several_new_tokens_bshd(mod, mask):

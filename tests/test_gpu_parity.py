@@ -441,6 +441,25 @@ def test_evoformer_row(dtype, with_bias, N_res):
     assert (np64(o)[1] == 0).all()
 
 
+@pytest.mark.parametrize("axis", ["row", "col"])
+def test_evoformer_large_logits(axis):
+    """Queries scaled by 25 at the scale 1/sqrt(C), whose scale * log2(e) is
+    no power of two: both forms (the row form with the pair bias on the
+    vector path, the column form on the folded one) stay within the bf16
+    tolerance of the oracle."""
+    q, k, v, gate, bias, km = evo_small("bf16", N_seq=40 if axis == "col" else 6,
+                                        N_res=24 if axis == "col" else 72)
+    q = (q.float() * 25).to(torch.bfloat16)
+    pb = bias if axis == "row" else None
+    o = api.fl_evoformer_gated_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), gate.to(DEV),
+                                        pair_bias=None if pb is None else pb.to(DEV),
+                                        key_mask=km.to(DEV), axis=axis)
+    torch.cuda.synchronize()
+    ro = oracle.evoformer(np64(q), np64(k), np64(v), np64(gate),
+                          pair_bias=None if pb is None else np64(pb), key_mask=km.numpy(), axis=axis)
+    check(np64(o), ro, "bf16", "evoformer %s large logits" % axis)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("N_seq", [40, 129, 200])
 def test_evoformer_col(dtype, N_seq):
