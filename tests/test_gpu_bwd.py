@@ -91,6 +91,22 @@ def test_bwd_small(mod, mask, S):
         check_grad(gg, rr, "%s %s+%s S=%d" % (name, mod, mask, S))
 
 
+@pytest.mark.parametrize("mask", [None, "causal"])
+@pytest.mark.parametrize("mod", MODS)
+def test_bwd_large_logits(mod, mask):
+    """Queries scaled by 5 (logits of standard deviation about 5) at the
+    default scale: the forward's O and LSE and the backward's recomputed P
+    keep the scale exact, so the gradients stay within tolerance."""
+    B, Hq, Hkv, S, D = 1, 4, 2, 200, 64
+    seed = 1700 + MODS.index(mod) + (mask is not None)
+    q, k, v = inputs.attn_inputs(B, Hq, Hkv, S, S, D, "bf16", seed=seed)
+    q = (q.float() * 5).to(torch.bfloat16)
+    do = inputs.randn(inputs._gen(seed + 1), (B, Hq, S, D), "bf16")
+    got, ref = run(q, k, v, do, **variant_kw(mod, mask, S, B, seed + 2))
+    for name, gg, rr in zip(("dq", "dk", "dv"), got, ref):
+        check_grad(gg, rr, "%s %s+%s large logits" % (name, mod, mask))
+
+
 @pytest.mark.parametrize("S", [1, 64, 129])
 def test_bwd_edges(S):
     B, Hq, Hkv, D = 1, 8, 1, 64   # one K/V head for eight query heads
