@@ -26,6 +26,8 @@ import json
 import os
 import sys
 
+CMD_VARS = "($REPO is the repository root and $OUT a scratch directory for the profiler's output.)"
+
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 
@@ -132,13 +134,13 @@ def stats_markdown(dirname: str, bench_json: str, workload: str) -> str:
     b = json.load(open(bench_json))
     out = ["# attn_mfma_kernel -- %s, all variants" % workload, "",
            "Kernel trace of the default bench command (one step = one call of each variant; "
-           "1 s clock settle, %d warmup and %d timed steps), one MI355X." % (b["warmup"], b["steps"]), "",
+           "1 s clock settle, %d warmup and %d timed steps), one MI355X." % (b["warmup"], b["steps"]), "", CMD_VARS, "",
            "```",
-           "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/kt -o run "
+           "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/kt -o run "
            "-- python3 $REPO/bench.py",
-           "python3 $REPO/bench.py > gpurun_out/bench.json",
-           "python -m flashattention_attention_variants_amd.profiling stats-md gpurun_out/kt "
-           "--bench gpurun_out/bench.json --workload %s" % workload,
+           "python3 $REPO/bench.py > $OUT/bench.json",
+           "python -m flashattention_attention_variants_amd.profiling stats-md $OUT/kt "
+           "--bench $OUT/bench.json --workload %s" % workload,
            "```", "", stats_table(dirname, lambda n: not is_decode_kernel(n) and not is_bwd_kernel(n)), "",
            "Kernel names: `MfmaCfg<D_qk, D_v, streams, QB, MOD, bias, key mask, gate>` with QB the "
            "32-query blocks per wave and MOD 0 = none (vanilla, causal, window, PrefixLM, document), "
@@ -163,13 +165,13 @@ def decode_stats_markdown(dirname: str, bench_json: str) -> str:
     out = ["# attn_mfma_kernel (decode form) and merge_kernel -- %s" % d["workload"], "",
            "Kernel trace of the default bench command, which times each decode variant after the "
            "step (a settle, then three batches of back-to-back calls; one call = the decode kernel "
-           "plus the merge kernel), one MI355X.", "",
+           "plus the merge kernel), one MI355X.", "", CMD_VARS, "",
            "```",
-           "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/kt -o run "
+           "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/kt -o run "
            "-- python3 $REPO/bench.py",
-           "python3 $REPO/bench.py > gpurun_out/bench.json",
-           "python -m flashattention_attention_variants_amd.profiling decode-stats-md gpurun_out/kt "
-           "--bench gpurun_out/bench.json",
+           "python3 $REPO/bench.py > $OUT/bench.json",
+           "python -m flashattention_attention_variants_amd.profiling decode-stats-md $OUT/kt "
+           "--bench $OUT/bench.json",
            "```", "", stats_table(dirname, is_decode_kernel), "",
            "Kernel names: `MfmaCfg<64, 64, 1, 1, MOD, false, false, false, true>` is the decode form "
            "with MOD 0 = none (causal, window), 1 = ALiBi, 3 = bounded softcap; `merge_kernel<bf16>` "
@@ -191,13 +193,13 @@ def bwd_stats_markdown(dirname: str, bench_json: str, workload: str) -> str:
     out = ["# attn_bwd_kernel -- %s, all variants" % workload, "",
            "Kernel trace of the default bench command, which times the backward of each variant "
            "after the step (a settle, then three batches of back-to-back calls; one call = the dQ "
-           "launch plus the dK, dV launch), one MI355X.", "",
+           "launch plus the dK, dV launch), one MI355X.", "", CMD_VARS, "",
            "```",
-           "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/kt -o run "
+           "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/kt -o run "
            "-- python3 $REPO/bench.py",
-           "python3 $REPO/bench.py > gpurun_out/bench.json",
-           "python -m flashattention_attention_variants_amd.profiling bwd-stats-md gpurun_out/kt "
-           "--bench gpurun_out/bench.json --workload %s" % workload,
+           "python3 $REPO/bench.py > $OUT/bench.json",
+           "python -m flashattention_attention_variants_amd.profiling bwd-stats-md $OUT/kt "
+           "--bench $OUT/bench.json --workload %s" % workload,
            "```", "", stats_table(dirname, is_bwd_kernel), "",
            "Kernel names: `BwdCfg<role, MOD>` with role 0 = dQ (rows are queries, K and V "
            "streamed), 1 = dK, dV (rows are keys, Q and dO of every query head of the group "
@@ -216,13 +218,13 @@ def traffic_markdown(rec: dict) -> str:
     out = ["# HBM traffic per launch -- attn_mfma_kernel, %s" % rec.get("workload", ""), "",
            "Two counter runs of the traffic probe (`bench.py --probe-traffic`: one call of each "
            "variant, a %d-byte device copy, then one more call of each variant), then the summary:"
-           % rec["probe_copy_bytes"], "", "```",
-           "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch -o run "
+           % rec["probe_copy_bytes"], "", CMD_VARS, "", "```",
+           "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/pmc_fetch -o run "
            "-- python3 $REPO/bench.py --probe-traffic",
-           "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write -o run "
+           "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/pmc_write -o run "
            "-- python3 $REPO/bench.py --probe-traffic",
-           "python -m flashattention_attention_variants_amd.profiling traffic gpurun_out/pmc_fetch "
-           "gpurun_out/pmc_write --workload %s --out profiles/traffic_%s.json --md profiles/traffic_%s.md"
+           "python -m flashattention_attention_variants_amd.profiling traffic $OUT/pmc_fetch "
+           "$OUT/pmc_write --workload %s --out profiles/traffic_%s.json --md profiles/traffic_%s.md"
            % (rec.get("workload"), rec.get("workload"), rec.get("workload")), "```", "",
            "Calibration: the copy of %d bytes read %.0f KiB of FETCH_SIZE and %.0f KiB of WRITE_SIZE, "
            "so counter KiB are scaled by %.4f (fetch) and %.4f (write) to bytes."
@@ -254,13 +256,13 @@ def evo_traffic_markdown(dir_fetch: str, dir_write: str) -> str:
     out = ["# HBM traffic per launch -- attn_mfma_kernel, %s" % EVO_WORKLOAD, "",
            "Two counter runs of the Evoformer probe (`bench.py --probe-evoformer`: one row call "
            "with the pair bias and one column call, a %d-byte device copy, then both calls "
-           "again), then the summary:" % rec["probe_copy_bytes"], "", "```",
-           "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/evo_fetch -o run "
+           "again), then the summary:" % rec["probe_copy_bytes"], "", CMD_VARS, "", "```",
+           "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/evo_fetch -o run "
            "-- python3 $REPO/bench.py --probe-evoformer",
-           "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/evo_write -o run "
+           "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/evo_write -o run "
            "-- python3 $REPO/bench.py --probe-evoformer",
-           "python -m flashattention_attention_variants_amd.profiling evo-traffic gpurun_out/evo_fetch "
-           "gpurun_out/evo_write", "```", "",
+           "python -m flashattention_attention_variants_amd.profiling evo-traffic $OUT/evo_fetch "
+           "$OUT/evo_write", "```", "",
            "Calibration: the copy of %d bytes read %.0f KiB of FETCH_SIZE and %.0f KiB of WRITE_SIZE, "
            "so counter KiB are scaled by %.4f (fetch) and %.4f (write) to bytes."
            % (rec["probe_copy_bytes"], rec["copy_fetch_kib"], rec["copy_write_kib"],
@@ -305,12 +307,12 @@ def counters_markdown(dirs: list[str], variants: list[str], workload: str, units
             per[v].update(x)
     out = ["# Counters -- attn_mfma_kernel, %s" % workload, "",
            "One rocprofv3 --pmc run per counter group over the traffic probe (the last call of each "
-           "variant is read):", "", "```"]
+           "variant is read):", "", CMD_VARS, "", "```"]
     for i, grp in enumerate(COUNTER_PASSES):
-        out.append("cd /tmp && rocprofv3 --pmc %s --output-format csv -d $REPO/gpurun_out/ctr%d -o run "
+        out.append("cd /tmp && rocprofv3 --pmc %s --output-format csv -d $OUT/ctr%d -o run "
                    "-- python3 $REPO/bench.py --probe-traffic" % (grp, i + 1))
-    out += ["python -m flashattention_attention_variants_amd.profiling counters-md gpurun_out/ctr1 "
-            "gpurun_out/ctr2 --workload %s" % workload, "```", "",
+    out += ["python -m flashattention_attention_variants_amd.profiling counters-md $OUT/ctr1 "
+            "$OUT/ctr2 --workload %s" % workload, "```", "",
             "| variant | MFMA busy | MFMA / unit | VALU / unit | SALU / unit | LDS / unit | "
             "LDS conflict cycles / LDS instr |", "|---|---:|---:|---:|---:|---:|---:|"]
     for v in variants:
