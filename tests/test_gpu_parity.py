@@ -300,6 +300,34 @@ def test_bf16_large_logits_default_scale(variant, mul):
     assert mx <= 2e-2 * max(1.0, np.abs(rl).max() / 64), "lse %g" % mx
 
 
+@pytest.mark.parametrize("case", ["plain", "sharp", "low", "mixed"])
+def test_alibi_two_blocks(case):
+    """ALiBi on a grid deep enough for two query blocks per wave (1 x 128
+    heads x 1024 rows: 512 work-groups of 256 rows), on sampled rows: plain
+    inputs; 'sharp' and 'low' scores as in the extreme-score test, which
+    every work-group's first pass must hand to the checked pass; 'mixed'
+    makes only the first 64 heads low, so some work-groups keep their first
+    pass and others redo the walk."""
+    B, H, S, D = 1, 128, 1024, 64
+    q, k, v = inputs.attn_inputs(B, H, H, S, S, D, "bf16", seed=74)
+    u = torch.full((D,), 1.0 / 8.0)  # unit vector
+    if case == "sharp":
+        q = (q.float() * 30).to(torch.bfloat16)
+    elif case in ("low", "mixed"):
+        hs = slice(0, H if case == "low" else 64)
+        kf, qf = k.float(), q.float()
+        kf[:, hs] = kf[:, hs] * 0.1 + 20 * u
+        qf[:, hs] = qf[:, hs] * 0.1 - 80 * u
+        k, q = kf.to(torch.bfloat16), qf.to(torch.bfloat16)
+    kw = dict(variant="alibi", alibi_max_bias=8.0)
+    o, lse = run_gpu_attn(q, k, v, **kw)
+    rows = sample_rows(B, H, S, 400, seed=75)
+    ro, rl = oracle.attn(np64(q), np64(k), np64(v), rows=rows, **kw)
+    check(gpu_rows(o, rows), ro, "bf16", "alibi two blocks %s" % case)
+    mx, _, _ = errors(np64(lse).reshape(-1)[rows], rl)
+    assert mx < 2e-2 * max(1.0, np.abs(rl).max() / 64), mx
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_fully_masked_rows(dtype):
     """A -inf bias row and an empty key set give O = 0 and LSE = -inf."""
