@@ -233,8 +233,8 @@ fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* b
   if (mod == MOD_SOFTCAP && !bias && p->softcap * kLog2e <= 100.0f) mod = MOD_SOFTCAP_BOUNDED;
   // Two 32-row blocks per wave halve the LDS operand traffic per product.
   // Dense rows take them when that still leaves two work-groups per compute
-  // unit (ALiBi too: its two-block form keeps a few registers in scratch,
-  // touched outside the unchecked first pass, and is 8% faster).  Under a positional mask the taller tiles cross more partial key
+  // unit (ALiBi too: its two-block form spills a few registers, about one
+  // dword per lane per tile of extra traffic, and is still 8% faster).  Under a positional mask the taller tiles cross more partial key
   // tiles and balance worse, so masked rows take them only when the grid is
   // deep (eight work-groups per unit); a sliding window, whose rows see few
   // keys, never does.
