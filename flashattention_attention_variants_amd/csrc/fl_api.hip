@@ -243,7 +243,9 @@ fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* b
   const int qb = FL_FORCE_QB;
 #else
   int qb;
-  if (a.iv_kind == IV_FULL)
+  if (mod == MOD_ALIBI && bias)
+    qb = 1;  // the vector path's ALiBi with a bias: two blocks spill more, unmeasured
+  else if (a.iv_kind == IV_FULL)
     qb = wg2 >= 512 ? 2 : 1;
   else if (a.iv_kind == IV_WINDOW_CAUSAL || a.iv_kind == IV_WINDOW_TWO_SIDED)
     qb = 1;
