@@ -4,27 +4,47 @@ One step = one forward call of each of the seven FlexAttention-class variants
 (vanilla, ALiBi, softcap, causal, causal sliding window 256, PrefixLM 512,
 document mask) on the MHA workload B=4, H=16, S=4096, D=64, bf16 (inputs
 resident in HBM before timing).  ``value`` is the useful TFLOP/s of the whole
-step; per-variant figures, the roofline of the dominant kernel (live HIP
-event timing on the launch stream) and the CPU oracle's throughput on a
-bounded sample of the same workload are printed on the same JSON line, with
-the backward of each variant (TFLOP/s of its five products) and the decode
-workload (64 sequences, 32/8 heads, KV caches of 512-8192 tokens, GB/s
-against the HBM roofline) timed beside it.
+step over the wall clock of the timed steps.  The same JSON line carries:
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
-    python bench.py --report        # extra lines: every workload, every variant
+* ``per_variant``: each launch's time in the timed steps (HIP events on the
+  launch stream; mean, median, min), TFLOP/s and fraction of peak; the rows
+  whose working set would sit in the 256 MB Infinity Cache (sliding window,
+  document) are also timed cold, with a 1 GiB buffer written before each
+  call outside the events;
+* ``roofline`` of the dominant (slowest) launch and ``cpu_baseline``, the
+  float64 oracle on a bounded sample of the same workload;
+* ``clocks``: shader and memory clocks read with amd-smi while the step runs,
+  before and after the timed region;
+* ``configs``: every other workload timed per call (10 warm-up calls, then
+  at least 30 and about 0.3 s of timed calls; median and min), each with the
+  fraction of its own roofline -- the float32 MHA case, the S=2048 variant
+  sweep, GQA at S=16384, differential attention, the Evoformer row and
+  column forms (cold) and Invariant Point Attention;
+* ``backward`` of each headline variant and ``decode`` against a KV cache
+  (cold and warm).
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-configs]
+    python bench.py --report        # also one line per config entry
 """
 from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
+import re
+import shutil
+import subprocess
 import sys
 import time
 
 METRIC = "attention fwd useful TFLOP/s + % bf16 MFMA peak (S=4k, D=64, per variant)"
 HEADLINE = "mha_bf16_b4_h16_s4096_d64"
 DECODE_WORKLOAD = "decode_bf16_b64_hq32_hkv8_cap8192_d64"
+EVO_WORKLOAD = "evoformer_bf16_nseq128_nres256_h8_c32"
+# rows whose working set fits the Infinity Cache are timed cold as well
+COLD_VARIANTS = ("sliding_window", "document")
+FLUSH_BYTES = 1 << 30
 
 
 def parse():
@@ -44,18 +64,111 @@ def parse():
                     help="skip the backward measurement printed beside the step")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode measurement printed beside the step")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config measurements printed beside the step")
+    ap.add_argument("--no-clocks", action="store_true", help="do not read clocks with amd-smi")
     ap.add_argument("--report", action="store_true",
-                    help="also print one JSON line per workload and variant")
+                    help="also print one JSON line per config entry")
     ap.add_argument("--traffic", default=None,
                     help="JSON file with HBM bytes per launch measured by rocprofv3 counters "
                          "(default: profiles/traffic_<workload>.json)")
     ap.add_argument("--probe-traffic", action="store_true",
-                    help="make only the dispatches the counter runs read: a copy of known "
-                         "size, then one call per variant")
+                    help="make only the dispatches the counter runs read: one call per "
+                         "variant, a copy of known size, then one call per variant")
     ap.add_argument("--probe-evoformer", action="store_true",
                     help="as --probe-traffic, for the Evoformer workload (row with pair bias, "
                          "then column)")
     return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# timing helpers
+
+
+def time_calls(torch, fn, *, warmup=10, min_calls=30, min_s=0.3, max_calls=3000, flush=None):
+    """Per-call times in ms of ``fn``: ``warmup`` untimed calls, then n timed
+    calls (at least min_calls and about min_s seconds of calls), each
+    bracketed by HIP events on the current stream, which the calls launch
+    on.  ``flush``, if given, runs before every call outside its events (the
+    cold-cache form)."""
+    import numpy as np
+    for _ in range(warmup):
+        if flush is not None:
+            flush()
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    fn()
+    b.record()
+    torch.cuda.synchronize()
+    t = max(a.elapsed_time(b), 1e-3)
+    n = int(min(max_calls, max(min_calls, math.ceil(min_s * 1e3 / t))))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for s, e in evs:
+        if flush is not None:
+            flush()
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    ts = np.array([s.elapsed_time(e) for s, e in evs])
+    return dict(ms_median=round(float(np.median(ts)), 5), ms_min=round(float(ts.min()), 5),
+                ms_mean=round(float(ts.mean()), 5), calls=n)
+
+
+def make_flush(torch, dev):
+    """A 1 GiB buffer written before each cold call: it evicts the L2 and the
+    256 MB Infinity Cache."""
+    buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    state = [0]
+
+    def flush():
+        state[0] = (state[0] + 1) & 0x7f
+        buf.fill_(state[0])
+    return flush
+
+
+def _parse_amd_smi_clocks(text):
+    """Shader (GFX_n) and memory (MEM_0) clocks in MHz per GPU block of
+    ``amd-smi metric -c`` text output."""
+    gpus = []
+    for block in re.split(r"^GPU:\s*\d+\s*$", text, flags=re.M)[1:]:
+        gfx = [int(m) for m in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", block)]
+        mem = [int(m) for m in re.findall(r"MEM_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", block)]
+        if gfx:
+            gpus.append(dict(sclk_mhz_mean=round(sum(gfx) / len(gfx), 1), sclk_mhz_min=min(gfx),
+                             sclk_mhz_max=max(gfx), mclk_mhz=mem[0] if mem else None))
+    return gpus
+
+
+def clocks_under_load(torch, fn, max_s=20.0):
+    """Clocks read by ``amd-smi metric -c`` (a child process) while ``fn``
+    keeps the GPU busy; None when amd-smi is missing or does not answer."""
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    try:
+        p = subprocess.Popen([exe, "metric", "-c"], stdout=subprocess.PIPE,
+                             stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+    t_end = time.perf_counter() + max_s
+    while p.poll() is None and time.perf_counter() < t_end:
+        fn()
+        torch.cuda.synchronize()
+    if p.poll() is None:
+        p.kill()
+        p.wait()
+        return None
+    gpus = _parse_amd_smi_clocks(p.stdout.read())
+    if not gpus:
+        return None
+    return gpus[0] if len(gpus) == 1 else dict(per_gpu=gpus)
+
+
+# ---------------------------------------------------------------------------
 
 
 def main():
@@ -64,6 +177,7 @@ def main():
         print("bench.py runs on one GPU only: there is no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    import numpy as np
     import torch
 
     from flashattention_attention_variants_amd import api, flops, inputs
@@ -87,17 +201,7 @@ def main():
     variants = args.variants.split(",") if args.variants else list(wl.variants)
     pr = wl.params
     outs = {vname: torch.empty_like(q) for vname in variants}
-
-    def kw_for(vname):
-        kw = dict(variant=vname)
-        for key in ("softcap", "alibi_max_bias", "window", "window_causal", "prefix"):
-            if key in pr:
-                kw[key] = pr[key]
-        if vname == "document":
-            kw["doc_offsets"] = docs_dev
-        return kw
-
-    kws = {vname: kw_for(vname) for vname in variants}
+    kws = {vname: attn_kw(vname, pr, docs_dev) for vname in variants}
     fl = {vname: flops.attn_flops(vname, B, Hq, S, S, D, window=pr.get("window", 256),
                                   window_causal=pr.get("window_causal", True),
                                   prefix=pr.get("prefix", 512),
@@ -127,6 +231,8 @@ def main():
               % (profiling.PROBE_COPY_BYTES, ",".join(variants)), flush=True)
         return
 
+    # settle: the clocks reach their loaded state (read meanwhile)
+    clk_before = None if args.no_clocks else clocks_under_load(torch, step)
     t_end = time.perf_counter() + args.settle
     while time.perf_counter() < t_end:
         step()
@@ -143,37 +249,46 @@ def main():
         step({vname: ev[vname][i] for vname in variants})
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = {vname: sum(a.elapsed_time(b) for a, b in ev[vname]) / args.steps for vname in variants}
+    clk_after = None if args.no_clocks else clocks_under_load(torch, step)
+    times = {vname: np.array([a.elapsed_time(b) for a, b in ev[vname]]) for vname in variants}
+    ms = {vname: float(times[vname].mean()) for vname in variants}
     total_flops = sum(fl.values())
     value = total_flops * args.steps / wall / 1e12
 
+    flush = make_flush(torch, dev)
     per = {}
     for vname in variants:
         tf = fl[vname] / (ms[vname] * 1e-3) / 1e12
         bound, roof = flops.roofline_tflops(fl[vname], nbytes)
-        per[vname] = dict(ms=round(ms[vname], 4), tflops=round(tf, 1),
-                          frac_bf16_peak=round(tf / flops.PEAK_BF16_TFLOPS, 4), bound=bound,
-                          roofline_tflops=round(roof, 1), frac_roofline=round(tf / roof, 4),
-                          useful_gflop=round(fl[vname] / 1e9, 2))
+        e = dict(ms=round(ms[vname], 5), ms_median=round(float(np.median(times[vname])), 5),
+                 ms_min=round(float(times[vname].min()), 5), tflops=round(tf, 1),
+                 frac_bf16_peak=round(tf / flops.PEAK_BF16_TFLOPS, 4), bound=bound,
+                 roofline_tflops=round(roof, 1), frac_roofline=round(tf / roof, 4),
+                 useful_gflop=round(fl[vname] / 1e9, 2),
+                 gbs=round(nbytes / (ms[vname] * 1e-3) / 1e9, 1))
+        if vname in COLD_VARIANTS:
+            c = time_calls(torch, lambda: api.fl_attn_fwd(q, k, v, out=outs[vname], **kws[vname]),
+                           flush=flush, max_calls=1000)
+            ctf = fl[vname] / (c["ms_median"] * 1e-3) / 1e12
+            e["cold"] = dict(c, tflops=round(ctf, 1), frac_roofline=round(ctf / roof, 4),
+                             gbs=round(nbytes / (c["ms_median"] * 1e-3) / 1e9, 1))
+        per[vname] = e
     dom = max(variants, key=lambda vname: ms[vname])
     achieved = fl[dom] / (ms[dom] * 1e-3) / 1e12
     bound, roof = flops.roofline_tflops(fl[dom], nbytes)
     # HBM bytes per launch from the committed counter runs, unless the
-    # kernels changed since they were taken
+    # kernels changed since they were taken or the record was edited
     from flashattention_attention_variants_amd import profiling
-    traffic = None
     tpath = args.traffic or os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                          "traffic_%s.json" % wl.name)
-    if os.path.exists(tpath):
-        rec = json.load(open(tpath))
-        if rec.get("kernel_digest") == profiling.kernel_digest() and dom in rec.get("per_variant", {}):
-            traffic = rec["per_variant"][dom]["traffic_bytes"]
+    traffic = profiling.traffic_for(tpath, dom)
     roofline = dict(bound=bound, achieved=round(achieved, 1),
                     peak=flops.PEAK_BF16_TFLOPS if bound == "mfma" else flops.PEAK_HBM_GBS,
                     unit="TFLOP/s" if bound == "mfma" else "GB/s",
                     frac=round(achieved / flops.PEAK_BF16_TFLOPS, 4), traffic=traffic,
-                    kernel="attn_mfma_kernel (%s)" % dom, ms_per_launch=round(ms[dom], 4),
-                    useful_flop_per_launch=fl[dom], algorithmic_bytes_per_launch=nbytes)
+                    kernel="attn_mfma_kernel (%s)" % dom, ms_per_launch=round(ms[dom], 5),
+                    useful_flop_per_launch=fl[dom], algorithmic_bytes_per_launch=nbytes,
+                    timing="mean of the launch's HIP-event durations over the timed steps")
     if bound == "hbm":
         gbs = nbytes / (ms[dom] * 1e-3) / 1e9
         roofline.update(achieved=round(gbs, 1), frac=round(gbs / flops.PEAK_HBM_GBS, 4))
@@ -192,33 +307,23 @@ def main():
         bper = {}
         for vname in variants:
             o_, lse_ = api.fl_attn_fwd(q, k, v, return_lse=True, **kws[vname])
-            bms = timeit(torch, lambda: api.fl_attn_bwd(q, k, v, o_, lse_, d_o, dq=dq, dk=dk, dv=dv,
-                                                        workspace=ws, **kws[vname]))
+            r = time_calls(torch, lambda: api.fl_attn_bwd(q, k, v, o_, lse_, d_o, dq=dq, dk=dk, dv=dv,
+                                                          workspace=ws, **kws[vname]))
             bf = fl[vname] * 5 // 2
-            btf = bf / (bms * 1e-3) / 1e12
-            bper[vname] = dict(ms=round(bms, 4), tflops=round(btf, 1),
+            btf = bf / (r["ms_median"] * 1e-3) / 1e12
+            bper[vname] = dict(r, tflops=round(btf, 1),
                                frac_bf16_peak=round(btf / flops.PEAK_BF16_TFLOPS, 4))
         backward = dict(per_variant=bper, useful_flop="2.5 x the forward's (five products)",
-                        timing="best of 3 batches of back-to-back calls, both launches")
+                        timing="per call (both launches): median and min of HIP-event times; "
+                               "tflops from the median")
 
-    # decode against a KV cache (split keys + merge), HBM-bound: its own
-    # workload, timed after the step, reported beside it
     decode = None
     if not args.no_decode:
-        dwl = inputs.WORKLOADS[DECODE_WORKLOAD]
-        dt = inputs.make(dwl)
-        dg = {k_: v_.to(dev) for k_, v_ in dt.items()}
-        dper = {}
-        for vname in dwl.variants:
-            dms, df, dnb = decode_case(torch, api, flops, dwl, dt, dg, vname, dev)
-            gbs = dnb / (dms * 1e-3) / 1e9
-            dper[vname] = dict(ms=round(dms, 4), gbs=round(gbs, 1),
-                               frac_hbm=round(gbs / flops.PEAK_HBM_GBS, 4),
-                               tflops=round(df / (dms * 1e-3) / 1e12, 2),
-                               algorithmic_bytes=dnb, bound="hbm")
-        decode = dict(workload=dwl.name, per_variant=dper,
-                      timing="best of 3 batches of back-to-back calls, decode and merge kernels")
-        del dg
+        decode = measure_decode(torch, api, flops, inputs, dev, flush)
+
+    configs = None
+    if not args.no_configs:
+        configs = measure_configs(torch, api, flops, inputs, dev, flush)
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -229,12 +334,171 @@ def main():
                    "variants": variants, "step": "one forward call per variant",
                    "seed": wl.seed},
         "frac_bf16_peak": round(value / flops.PEAK_BF16_TFLOPS, 4),
-        "roofline": roofline, "cpu_baseline": cpu, "per_variant": per, "backward": backward,
-        "decode": decode,
+        "roofline": roofline, "cpu_baseline": cpu,
+        "clocks": dict(before=clk_before, after=clk_after,
+                       note="amd-smi metric -c read while the step runs, before and after the "
+                            "timed region"),
+        "per_variant": per, "configs": configs, "backward": backward, "decode": decode,
     }
     print(json.dumps(line), flush=True)
-    if args.report:
-        report(torch, api, flops, inputs, dev)
+    if args.report and configs:
+        for name, entry in configs.items():
+            print(json.dumps({"report": name, **entry}), flush=True)
+
+
+def attn_kw(vname, pr, docs_dev):
+    kw = dict(variant=vname)
+    for key in ("softcap", "alibi_max_bias", "window", "window_causal", "prefix"):
+        if key in pr:
+            kw[key] = pr[key]
+    if vname == "document":
+        kw["doc_offsets"] = docs_dev
+    return kw
+
+
+def _entry(flops, f, nb, r, cold=None, peak=None, bound_override=None):
+    """One measured case: time, TFLOP/s, GB/s and the fraction of its own
+    roofline (from the primary timing: cold where given)."""
+    peak = peak or flops.PEAK_BF16_TFLOPS
+    bound, roof = flops.roofline_tflops(f, nb, peak_tflops=peak)
+    prim = cold if cold is not None else r
+    ms = prim["ms_median"]
+    tf = f / (ms * 1e-3) / 1e12
+    gbs = nb / (ms * 1e-3) / 1e9
+    e = dict(warm=r, ms_median=ms, tflops=round(tf, 2), frac_bf16_peak=round(tf / peak, 4),
+             gbs=round(gbs, 1), bound=bound_override or bound, roofline_tflops=round(roof, 1),
+             frac_roofline=round(tf / roof, 4), useful_flop=int(f), algorithmic_bytes=int(nb),
+             timing="cold (1 GiB written before each call), median" if cold is not None
+             else "warm, median")
+    if cold is not None:
+        e["cold"] = cold
+    if bound == "hbm":
+        e["frac_hbm"] = round(gbs / flops.PEAK_HBM_GBS, 4)
+    return e
+
+
+def measure_configs(torch, api, flops, inputs, dev, flush):
+    """Every other workload per call, each against its own roofline."""
+    out = {}
+    # float32 MHA with LSE: latency-bound at this size
+    wl = inputs.WORKLOADS["mha_f32_b1_h2_s128_d64"]
+    t = inputs.make(wl)
+    g = {n: x.to(dev) for n, x in t.items()}
+    s = wl.shape
+    o = torch.empty_like(g["q"])
+    lse = torch.empty(s["B"], s["Hq"], s["S"], dtype=torch.float32, device=dev)
+    r = time_calls(torch, lambda: api.fl_attn_fwd(g["q"], g["k"], g["v"], out=o, lse=lse))
+    f = flops.attn_flops("vanilla", s["B"], s["Hq"], s["S"], s["S"], s["D"])
+    nb = flops.attn_bytes(s["B"], s["Hq"], s["Hkv"], s["S"], s["S"], s["D"], elem=4, lse=True)
+    out["%s/vanilla" % wl.name] = _entry(flops, f, nb, r, peak=flops.PEAK_F32_VALU_TFLOPS,
+                                         bound_override="latency")
+    # bf16 MHA sweep at S=2048 and GQA at S=16384
+    for name in ("mha_bf16_b4_h16_s2048_d64", "gqa_bf16_b1_hq32_hkv8_s16384_d64"):
+        wl = inputs.WORKLOADS[name]
+        t = inputs.make(wl)
+        g = {n: x.to(dev) for n, x in t.items()}
+        s = wl.shape
+        o = torch.empty_like(g["q"])
+        for vname in wl.variants:
+            kw = attn_kw(vname, wl.params, g.get("doc_offsets"))
+            fn = lambda: api.fl_attn_fwd(g["q"], g["k"], g["v"], out=o, **kw)  # noqa: E731
+            r = time_calls(torch, fn)
+            f = flops.attn_flops(vname, s["B"], s["Hq"], s["S"], s["S"], s["D"],
+                                 window=wl.params.get("window", 256),
+                                 window_causal=wl.params.get("window_causal", True),
+                                 prefix=wl.params.get("prefix", 512),
+                                 doc_offsets=None if "doc_offsets" not in t else t["doc_offsets"].numpy())
+            nb = flops.attn_bytes(s["B"], s["Hq"], s["Hkv"], s["S"], s["S"], s["D"])
+            cold = None
+            if vname in COLD_VARIANTS or flops.roofline_tflops(f, nb)[0] == "hbm":
+                cold = time_calls(torch, fn, flush=flush, max_calls=1000)
+            out["%s/%s" % (name, vname)] = _entry(flops, f, nb, r, cold)
+        del g
+    # differential attention
+    wl = inputs.WORKLOADS["diffattn_bf16_b4_h16_s4096_dqk64_dv128"]
+    t = inputs.make(wl)
+    g = [t[n].to(dev) for n in ("q1", "q2", "k1", "k2", "v")]
+    s = wl.shape
+    o = torch.empty(s["B"], s["H"], s["S"], s["Dv"], dtype=torch.bfloat16, device=dev)
+    for vname in wl.variants:
+        causal = vname == "causal"
+        r = time_calls(torch, lambda: api.fl_diffattn_fwd(*g, lam=wl.params["lam"], causal=causal,
+                                                          out=o))
+        f = flops.diffattn_flops(s["B"], s["H"], s["S"], s["Dqk"], s["Dv"], causal)
+        nb = flops.diffattn_bytes(s["B"], s["H"], s["S"], s["Dqk"], s["Dv"])
+        out["%s/%s" % (wl.name, vname)] = _entry(flops, f, nb, r)
+    del g
+    # Evoformer row (pair bias, key mask, gate) and column: HBM-bound, cold
+    wl = inputs.WORKLOADS[EVO_WORKLOAD]
+    t = inputs.make(wl)
+    g = {n: x.to(dev) for n, x in t.items()}
+    s = wl.shape
+    o = torch.empty_like(g["q"])
+    for axis in wl.variants:
+        pb = g["pair_bias"] if axis == "row" else None
+        fn = lambda: api.fl_evoformer_gated_attn_fwd(  # noqa: E731
+            g["q"], g["k"], g["v"], g["gate"], pair_bias=pb, key_mask=g["key_mask"], axis=axis, out=o)
+        r = time_calls(torch, fn)
+        cold = time_calls(torch, fn, flush=flush, max_calls=1000)
+        f = flops.evoformer_flops(s["N_seq"], s["N_res"], s["H"], s["C"], axis)
+        nb = flops.evoformer_bytes(s["N_seq"], s["N_res"], s["H"], s["C"], axis)
+        out["%s/%s" % (wl.name, axis)] = _entry(flops, f, nb, r, cold)
+    del g
+    ipa = measure_ipa(torch, api, flops, inputs, dev, flush)
+    if ipa:
+        out.update(ipa)
+    return out
+
+
+def measure_ipa(torch, api, flops, inputs, dev, flush):
+    """Invariant Point Attention core, if the library exports it."""
+    if not hasattr(api, "fl_ipa_attn_fwd") or "ipa_bf16_nres256_h12" not in inputs.WORKLOADS:
+        return None
+    wl = inputs.WORKLOADS["ipa_bf16_nres256_h12"]
+    t = inputs.make(wl)
+    g = {n: x.to(dev) for n, x in t.items()}
+    res = api.fl_ipa_attn_fwd(**g)
+    outs = res if isinstance(res, tuple) else (res,)
+    fn = lambda: api.fl_ipa_attn_fwd(**g, out=outs)  # noqa: E731
+    r = time_calls(torch, fn)
+    cold = time_calls(torch, fn, flush=flush, max_calls=1000)
+    f, nb = flops.ipa_work(**wl.shape)
+    return {"%s/ipa" % wl.name: _entry(flops, f, nb, r, cold)}
+
+
+def measure_decode(torch, api, flops, inputs, dev, flush):
+    """Decode against a KV cache (split keys + merge), HBM-bound: cold
+    (primary) and warm per call."""
+    dwl = inputs.WORKLOADS[DECODE_WORKLOAD]
+    dt = inputs.make(dwl)
+    dg = {k_: v_.to(dev) for k_, v_ in dt.items()}
+    s = dwl.shape
+    dper = {}
+    for vname in dwl.variants:
+        kw = dict(variant=vname)
+        for key in ("softcap", "alibi_max_bias", "window", "window_causal"):
+            if key in dwl.params:
+                kw[key] = dwl.params[key]
+        L = dt["seqlens"]
+        max_len = int(L.max())
+        ws_bytes = api.fl_attn_decode_workspace_size(
+            s["B"], s["Hq"], s["Hkv"], s["Sq"], max_len, s["D"], variant=vname,
+            window=kw.get("window", 256), window_causal=kw.get("window_causal", True))
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        out = torch.empty_like(dg["q"])
+        fn = lambda: api.fl_attn_decode_fwd(  # noqa: E731
+            dg["q"], dg["k_cache"], dg["v_cache"], dg["seqlens"], max_seqlen=max_len, workspace=ws,
+            out=out, **kw)
+        r = time_calls(torch, fn)
+        cold = time_calls(torch, fn, flush=flush, max_calls=1000)
+        mask = vname if vname in ("causal", "sliding_window", "prefix_lm") else None
+        f, nb = flops.decode_work(mask, L.tolist(), s["Hq"], s["Hkv"], s["Sq"], s["D"],
+                                  window=dwl.params.get("window", 256),
+                                  window_causal=dwl.params.get("window_causal", True))
+        dper[vname] = _entry(flops, f, nb, r, cold)
+    return dict(workload=dwl.name, per_variant=dper,
+                timing="per call (decode and merge kernels): median and min of HIP-event times, "
+                       "cold (1 GiB written before each call) and warm")
 
 
 def cpu_baseline(t, variants, kws, wl, seconds):
@@ -243,7 +507,6 @@ def cpu_baseline(t, variants, kws, wl, seconds):
     import numpy as np
 
     import oracle
-    from flashattention_attention_variants_amd import flops
 
     oracle.build()
     s = wl.shape
@@ -303,114 +566,6 @@ def cpu_baseline(t, variants, kws, wl, seconds):
             "kind": "oracle",
             "sample": "%d random query rows per variant (x%d variants) of %s, float64 two-pass, "
                       "%.1f s" % (n, len(variants), wl.name, total_s)}
-
-
-def timeit(torch, fn, settle=0.3, batches=3, batch_s=0.05):
-    """ms per call: a short settle at this case's load, then the fastest of a
-    few timed batches of back-to-back calls (events on the current stream,
-    which the calls launch on)."""
-    t_end = time.perf_counter() + settle
-    n = 0
-    while time.perf_counter() < t_end or n < 3:
-        fn()
-        torch.cuda.synchronize()
-        n += 1
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    fn()
-    b.record()
-    torch.cuda.synchronize()
-    iters = max(5, int(batch_s * 1e3 / max(a.elapsed_time(b), 1e-3)))
-    best = float("inf")
-    for _ in range(batches):
-        a.record()
-        for _ in range(iters):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        best = min(best, a.elapsed_time(b) / iters)
-    return best
-
-
-def decode_case(torch, api, flops, wl, t, g, vname, dev):
-    """(ms, useful flops, algorithmic bytes) of one decode call of workload wl."""
-    s = wl.shape
-    kw = dict(variant=vname)
-    for key in ("softcap", "alibi_max_bias", "window", "window_causal"):
-        if key in wl.params:
-            kw[key] = wl.params[key]
-    L = t["seqlens"]
-    max_len = int(L.max())
-    ws_bytes = api.fl_attn_decode_workspace_size(
-        s["B"], s["Hq"], s["Hkv"], s["Sq"], max_len, s["D"], variant=vname,
-        window=kw.get("window", 256), window_causal=kw.get("window_causal", True))
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    out = torch.empty_like(g["q"])
-    ms = timeit(torch, lambda: api.fl_attn_decode_fwd(
-        g["q"], g["k_cache"], g["v_cache"], g["seqlens"], max_seqlen=max_len, workspace=ws,
-        out=out, **kw))
-    mask = vname if vname in ("causal", "sliding_window", "prefix_lm") else None
-    f, nb = flops.decode_work(mask, L.tolist(), s["Hq"], s["Hkv"], s["Sq"], s["D"],
-                              window=wl.params.get("window", 256),
-                              window_causal=wl.params.get("window_causal", True))
-    return ms, f, nb
-
-
-def report(torch, api, flops, inputs, dev):
-    """One JSON line per (workload, variant): time, TFLOP/s, roofline fraction."""
-
-    for name, wl in inputs.WORKLOADS.items():
-        t = inputs.make(wl)
-        g = {k: v.to(dev) for k, v in t.items()}
-        s = wl.shape
-        for vname in wl.variants:
-            if wl.kind == "attn":
-                kw = dict(variant=vname)
-                for key in ("softcap", "alibi_max_bias", "window", "window_causal", "prefix"):
-                    if key in wl.params:
-                        kw[key] = wl.params[key]
-                if vname == "document":
-                    kw["doc_offsets"] = g["doc_offsets"]
-                out = torch.empty_like(g["q"])
-                ms = timeit(torch, lambda: api.fl_attn_fwd(g["q"], g["k"], g["v"], out=out, **kw))
-                f = flops.attn_flops(vname, s["B"], s["Hq"], s["S"], s["S"], s["D"],
-                                     window=wl.params.get("window", 256),
-                                     window_causal=wl.params.get("window_causal", True),
-                                     prefix=wl.params.get("prefix", 512),
-                                     doc_offsets=None if "doc_offsets" not in t else t["doc_offsets"].numpy())
-                nb = flops.attn_bytes(s["B"], s["Hq"], s["Hkv"], s["S"], s["S"], s["D"],
-                                      elem=2 if wl.dtype == "bf16" else 4)
-                peak = flops.PEAK_BF16_TFLOPS if wl.dtype == "bf16" else flops.PEAK_F32_VALU_TFLOPS
-            elif wl.kind == "diffattn":
-                out = torch.empty(s["B"], s["H"], s["S"], s["Dv"], dtype=torch.bfloat16, device=dev)
-                causal = vname == "causal"
-                ms = timeit(torch, lambda: api.fl_diffattn_fwd(g["q1"], g["q2"], g["k1"], g["k2"], g["v"],
-                                                        lam=wl.params["lam"], causal=causal, out=out))
-                f = flops.diffattn_flops(s["B"], s["H"], s["S"], s["Dqk"], s["Dv"], causal)
-                nb = flops.diffattn_bytes(s["B"], s["H"], s["S"], s["Dqk"], s["Dv"])
-                peak = flops.PEAK_BF16_TFLOPS
-            elif wl.kind == "decode":
-                ms, f, nb = decode_case(torch, api, flops, wl, t, g, vname, dev)
-                peak = flops.PEAK_BF16_TFLOPS
-            else:
-                out = torch.empty_like(g["q"])
-                pb = g["pair_bias"] if vname == "row" else None
-                ms = timeit(torch, lambda: api.fl_evoformer_gated_attn_fwd(
-                    g["q"], g["k"], g["v"], g["gate"], pair_bias=pb, key_mask=g["key_mask"],
-                    axis=vname, out=out))
-                f = flops.evoformer_flops(s["N_seq"], s["N_res"], s["H"], s["C"], vname)
-                nb = flops.evoformer_bytes(s["N_seq"], s["N_res"], s["H"], s["C"], vname)
-                peak = flops.PEAK_BF16_TFLOPS
-            tf = f / (ms * 1e-3) / 1e12
-            bound, roof = flops.roofline_tflops(f, nb, peak_tflops=peak)
-            print(json.dumps({"report": name, "variant": vname, "ms": round(ms, 4),
-                              "tflops": round(tf, 2), "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
-                              "bound": bound, "roofline_tflops": round(roof, 1),
-                              "frac_roofline": round(tf / roof, 4),
-                              "frac_peak": round(tf / peak, 4)}), flush=True)
-
-
-EVO_WORKLOAD = "evoformer_bf16_nseq128_nres256_h8_c32"
 
 
 def probe_evoformer(torch, api, inputs, dev):

@@ -450,22 +450,29 @@ void attn_mfma_kernel(KernelArgs a) {
 
   // ---- Q operands in registers ---------------------------------------------
   // B operand of S^T = K Q^T: lane (c, g) holds Q[row c][16t + 8g .. +7].
-  // Folded scores: Q is pre-multiplied by scale*log2(e) (one bf16 rounding),
-  // so S^T comes out in base-2 units; bounded softcap: by the power-of-two
-  // part of the tanh argument 2*scale*log2(e)/cap (exact), so S^T is t / scap_m.
-  // (Folded scores likewise take only the power-of-two part of the scale.)
+  // Folded scores: Q is multiplied by the signed power-of-two part of
+  // scale*log2(e) (exact), so S^T is the base-2 score over fold_m; bounded
+  // softcap: by that part of the tanh argument 2*scale*log2(e)/cap, so S^T
+  // is t / scap_m.
   bf16x8 qreg[NSU][QB][DQK / 16];
   // bounded softcap: tanh argument = scap_m * scap_q, scap_q a power of two
-  int scap_e = 0;
-  const float scap_m = C::SCAPB ? frexpf(a.softcap_arg, &scap_e) : 1.0f;
-  const float scap_q = C::SCAPB ? ldexpf(1.0f, scap_e) : 1.0f;
-  // folded scores: scale*log2(e) = fold_m * fold_q, fold_q a power of two.
-  // Q takes fold_q (exact), so S^T, the folded terms and the running
+  // Both factors split as x = m * q with m in [0.5, 1) (so a larger S^T is
+  // always a larger score) and q = +-2^e carrying the sign (a negative
+  // scale flips Q exactly); a zero factor gives q = 0, m = 1.
+  auto split_pow2 = [](float x, float& m, float& q) {
+    int e = 0;
+    const float f = frexpf(x, &e);
+    m = x == 0.0f ? 1.0f : __builtin_fabsf(f);
+    q = x == 0.0f ? 0.0f : __builtin_copysignf(ldexpf(1.0f, e), x);
+  };
+  float scap_m = 1.0f, scap_q = 1.0f;
+  if constexpr (C::SCAPB) split_pow2(a.softcap_arg, scap_m, scap_q);
+  // folded scores: scale*log2(e) = fold_m * fold_q, fold_q a signed power of
+  // two.  Q takes fold_q (exact), so S^T, the folded terms and the running
   // reference are in units of 1/fold_m base-2 units; fold_m enters where
   // a term is exponentiated (one fused multiply-add per score).
-  int fold_e = 0;
-  const float fold_m = C::FOLD ? frexpf(a.scale_log2, &fold_e) : 1.0f;
-  const float fold_q = C::FOLD ? ldexpf(1.0f, fold_e) : 1.0f;
+  float fold_m = 1.0f, fold_q = 1.0f;
+  if constexpr (C::FOLD) split_pow2(a.scale_log2, fold_m, fold_q);
   auto load_q = [&](int bb) {
 #pragma unroll
     for (int s = 0; s < NSU; ++s) {
@@ -1255,8 +1262,11 @@ void attn_mfma_kernel(KernelArgs a) {
       const float l0 = __shfl(lacc[0][qb][0], c & 15);
       const float l1 = __shfl(lacc[0][qb][1], c & 15);
       const float l = c < 16 ? l0 : l1;
+      // rows past S_q (zero queries, under ALiBi possibly far below range)
+      // produce no output and are left out
+      const bool real = wq0 + 32 * qb + c < a.sq;
       const bool has = row_lo[qb] <= row_hi[qb];
-      bad |= (has & !(l >= lo)) | !(l <= 0x1p100f);
+      bad |= real & ((has & !(l >= lo)) | !(l <= 0x1p100f));
     }
     __shared__ int pass_bad;
     if (tid == 0) pass_bad = 0;

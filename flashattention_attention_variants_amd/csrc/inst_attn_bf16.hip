@@ -21,7 +21,12 @@ static hipError_t pick_bias(const KernelArgs& a, bool bias, hipStream_t st) {
 template <int QB>
 static hipError_t pick_mod(const KernelArgs& a, int mod, bool bias, hipStream_t st) {
   switch (mod) {
-    case MOD_ALIBI: return pick_bias<QB, MOD_ALIBI>(a, bias, st);
+    case MOD_ALIBI:
+      // ALiBi with a bias takes one query block per wave (its two-block
+      // form would spill); that instance is not built
+      if (QB == 2 && bias) return hipErrorInvalidConfiguration;
+      if constexpr (QB == 1) return pick_bias<QB, MOD_ALIBI>(a, bias, st);
+      return go<MfmaCfg<64, 64, 1, QB, MOD_ALIBI, false, false, false>>(a, st);
     case MOD_SOFTCAP: return pick_bias<QB, MOD_SOFTCAP>(a, bias, st);
     case MOD_SOFTCAP_BOUNDED:  // chosen only without a bias
       return go<MfmaCfg<64, 64, 1, QB, MOD_SOFTCAP_BOUNDED, false, false, false>>(a, st);

@@ -47,12 +47,45 @@ def kernel_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def _csv(dirname: str, suffix: str) -> list[dict]:
+def _csv_path(dirname: str, suffix: str) -> str:
     hits = sorted(glob.glob(os.path.join(dirname, "**", "*" + suffix), recursive=True))
     if not hits:
         raise FileNotFoundError("no *%s under %s" % (suffix, dirname))
-    with open(hits[0], newline="") as fh:
+    return hits[0]
+
+
+def _csv(dirname: str, suffix: str) -> list[dict]:
+    with open(_csv_path(dirname, suffix), newline="") as fh:
         return list(csv.DictReader(fh))
+
+
+def _file_sha256(path: str) -> str:
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def record_digest(rec: dict) -> str:
+    """sha256 over the fields of a traffic record that its counter runs
+    fixed: the kernel digest, the hashes of the counter CSVs read, the
+    calibration factors and the per-variant bytes.  A record whose fields
+    were edited after the tool wrote it no longer matches."""
+    keys = ("kernel_digest", "csv_sha256", "fetch_factor", "write_factor", "per_variant")
+    body = json.dumps({k: rec.get(k) for k in keys}, sort_keys=True)
+    return hashlib.sha256(body.encode()).hexdigest()[:16]
+
+
+def traffic_for(path: str, variant: str):
+    """HBM bytes per launch of ``variant`` from a traffic record, or None
+    when the record is missing, was taken with other kernel sources, or
+    does not match its own record digest."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_digest") != kernel_digest() or rec.get("record_digest") != record_digest(rec):
+        return None
+    v = rec.get("per_variant", {}).get(variant)
+    return None if v is None else v["traffic_bytes"]
 
 
 def short_name(name: str) -> str:
@@ -96,7 +129,9 @@ def _per_dispatch(dirname: str, counter: str) -> list[tuple[int, str, float]]:
 
 def traffic(dir_fetch: str, dir_write: str, variants: list[str]) -> dict:
     res = {}
+    csv_sha = {}
     for key, dirname, counter in (("fetch", dir_fetch, "FETCH_SIZE"), ("write", dir_write, "WRITE_SIZE")):
+        csv_sha[key] = _file_sha256(_csv_path(dirname, "counter_collection.csv"))
         disp = _per_dispatch(dirname, counter)
         copies = [(i, v) for i, (_, name, v) in enumerate(disp) if "copy" in name.lower()]
         if not copies:
@@ -111,7 +146,8 @@ def traffic(dir_fetch: str, dir_write: str, variants: list[str]) -> dict:
         res[key] = dict(copy_kib=cv, factor=factor,
                         per_variant={vn: (short_name(nm), kib * 1024.0 * factor)
                                      for vn, (nm, kib) in zip(variants, attn)})
-    out = {"kernel_digest": kernel_digest(), "probe_copy_bytes": PROBE_COPY_BYTES,
+    out = {"kernel_digest": kernel_digest(), "csv_sha256": csv_sha,
+           "probe_copy_bytes": PROBE_COPY_BYTES,
            "fetch_factor": res["fetch"]["factor"], "write_factor": res["write"]["factor"],
            "copy_fetch_kib": res["fetch"]["copy_kib"], "copy_write_kib": res["write"]["copy_kib"],
            "per_variant": {}}
@@ -120,12 +156,14 @@ def traffic(dir_fetch: str, dir_write: str, variants: list[str]) -> dict:
         _, wb = res["write"]["per_variant"][vn]
         out["per_variant"][vn] = dict(kernel=kname, fetch_bytes=round(fb), write_bytes=round(wb),
                                       traffic_bytes=round(fb + wb))
+    out["record_digest"] = record_digest(out)
     return out
 
 
 ALGO_BYTES_NOTE = ("Algorithmic bytes = Q, K, V read once and O written once (bf16).  "
                    "`kernel_digest` names the kernel and launcher sources the counters were "
-                   "taken with; bench.py reports `traffic` only while it matches.")
+                   "taken with, `record_digest` the record's own fields as the tool wrote them; "
+                   "bench.py reports `traffic` only while both match.")
 
 
 def stats_markdown(dirname: str, bench_json: str, workload: str) -> str:
@@ -239,7 +277,10 @@ def traffic_markdown(rec: dict) -> str:
             k, v["kernel"].replace("fl::", ""), v["fetch_bytes"] / 1e6, v["write_bytes"] / 1e6,
             v["traffic_bytes"] / 1e6, "%.1f" % (alg / 1e6) if alg else "-",
             "%.2f" % (v["traffic_bytes"] / alg) if alg else "-"))
-    out += ["", ALGO_BYTES_NOTE, "", "kernel_digest: %s" % rec["kernel_digest"], ""]
+    out += ["", ALGO_BYTES_NOTE, "", "kernel_digest: %s" % rec["kernel_digest"],
+            "record_digest: %s" % rec["record_digest"],
+            "counter CSV sha256: fetch %s, write %s" % (rec["csv_sha256"]["fetch"],
+                                                       rec["csv_sha256"]["write"]), ""]
     return "\n".join(out)
 
 
@@ -276,7 +317,9 @@ def evo_traffic_markdown(dir_fetch: str, dir_write: str) -> str:
             v["traffic_bytes"] / 1e6, alg / 1e6, v["traffic_bytes"] / alg))
     out += ["", "Algorithmic bytes = q, k, v, gate read once, o written once (bf16), the u8 key "
             "mask, and for the row form the pair bias [H, N_res, N_res] read once.", "",
-            "kernel_digest: %s" % rec["kernel_digest"], ""]
+            "kernel_digest: %s" % rec["kernel_digest"], "record_digest: %s" % rec["record_digest"],
+            "counter CSV sha256: fetch %s, write %s" % (rec["csv_sha256"]["fetch"],
+                                                       rec["csv_sha256"]["write"]), ""]
     return "\n".join(out)
 
 

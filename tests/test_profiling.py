@@ -85,3 +85,26 @@ def test_evoformer_traffic_table(tmp_path):
     md = profiling.evo_traffic_markdown(str(tmp_path / "f"), str(tmp_path / "w"))
     lines = [l for l in md.splitlines() if l.startswith("| row |") or l.startswith("| col |")]
     assert lines[0].endswith("| 1.00 |") and lines[1].endswith("| 2.00 |"), lines
+
+
+def test_traffic_record_guard(tmp_path):
+    """bench.py takes traffic from a record only while the kernel sources and
+    the record's own fields are as the tool wrote them."""
+    import json
+    attn = "void fl::attn_mfma_kernel<fl::MfmaCfg<64, 64, 1, 2, 0> >(fl::KernelArgs)"
+    copy_kib = profiling.PROBE_COPY_BYTES / 1024
+    _write_counters(tmp_path / "f", "FETCH_SIZE",
+                    [("__amd_rocclr_copyBuffer", copy_kib / 2), (attn, 1000.0)])
+    _write_counters(tmp_path / "w", "WRITE_SIZE", [("__amd_rocclr_copyBuffer", copy_kib), (attn, 64.0)])
+    rec = profiling.traffic(str(tmp_path / "f"), str(tmp_path / "w"), ["vanilla"])
+    assert len(rec["csv_sha256"]["fetch"]) == 64
+    path = tmp_path / "t.json"
+    path.write_text(json.dumps(rec))
+    assert profiling.traffic_for(str(path), "vanilla") == 1000 * 1024 * 2 + 64 * 1024
+    assert profiling.traffic_for(str(path), "causal") is None
+    # an edited kernel digest (or any other field) voids the record
+    for key, val in (("kernel_digest", "0" * 16), ("fetch_factor", 3.0)):
+        bad = dict(rec, **{key: val})
+        path.write_text(json.dumps(bad))
+        assert profiling.traffic_for(str(path), "vanilla") is None, key
+    assert profiling.traffic_for(str(tmp_path / "missing.json"), "vanilla") is None
