@@ -136,3 +136,18 @@ def roofline_tflops(flops: float, nbytes: float, peak_tflops=PEAK_BF16_TFLOPS,
     """(bound, attainable TFLOP/s) of a kernel with that work and traffic."""
     mem = hbm_gbs * 1e9 * flops / nbytes / 1e12
     return ("mfma", peak_tflops) if peak_tflops <= mem else ("hbm", mem)
+
+
+def ipa_work(B, L, H, C, Pq, Pv, Cz, elem=2, masked_keys=0):
+    """(useful FLOPs, algorithmic bytes) of one Invariant Point Attention
+    core call.  Per allowed (query, key, head) triple the products are
+    counted as multiply-adds: the scalar logit (C), the point distances
+    (3 Pq), and the three weighted sums (C values, 3 Pv point coordinates,
+    Cz pair features).  Bytes: q, k, v, pair bias, z and the outputs o,
+    o_pair in the compute dtype; points, frames and o_pts in float32; gamma
+    and the u8 key mask."""
+    pairs = B * H * L * (L - masked_keys)
+    f = 2 * pairs * (C + 3 * Pq + C + 3 * Pv + Cz)
+    nb = elem * (3 * B * L * H * C + B * H * L * L + B * L * L * Cz + B * L * H * (C + Cz))
+    nb += 4 * (B * L * H * 3 * (2 * Pq + Pv) + B * L * 12 + H + B * L * H * 3 * Pv) + B * L
+    return f, nb

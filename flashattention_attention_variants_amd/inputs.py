@@ -109,6 +109,49 @@ def decode_inputs(B, Hq, Hkv, S_q, S_cap, D, dtype="bf16", seed=0, layout="bhsd"
     return q, k, v
 
 
+def rotations(n: int, g: torch.Generator) -> torch.Tensor:
+    """n rotation matrices [n, 3, 3] (float32, row-major), uniform over the
+    rotation group: unit quaternions from normalised 4-d Gaussian draws,
+    written out as matrices."""
+    u = torch.randn(n, 4, generator=g, dtype=torch.float64)
+    w, x, y, z = (u / u.norm(dim=1, keepdim=True)).unbind(1)
+    R = torch.stack([
+        1 - 2 * (y * y + z * z), 2 * (x * y - w * z), 2 * (x * z + w * y),
+        2 * (x * y + w * z), 1 - 2 * (x * x + z * z), 2 * (y * z - w * x),
+        2 * (x * z - w * y), 2 * (y * z + w * x), 1 - 2 * (x * x + y * y)], 1)
+    return R.reshape(n, 3, 3).to(torch.float32)
+
+
+def ipa_inputs(B, L, H, C, Pq, Pv, Cz, dtype="bf16", seed=0, masked_frac=0.0, step=3.8):
+    """Invariant Point Attention inputs, drawn in this order:
+    q, k, v [B,L,H,C] (N(0,1), dtype); q_pts, k_pts [B,L,H,Pq,3] and v_pts
+    [B,L,H,Pv,3] (N(0,1) float32, local coordinates); rot [B,L,3,3] (uniform
+    random rotations, float32); trans [B,L,3] (a chain: each residue
+    ``step`` apart from the previous one in a uniformly random direction,
+    like a protein's C-alpha trace, float32); gamma [H] (softplus of N(0,1),
+    float32); pair_bias [B,H,L,L] and z [B,L,L,Cz] (N(0,1), dtype);
+    key_mask [B,L] uint8 with each residue excluded with probability
+    ``masked_frac``."""
+    g = _gen(seed)
+    q = randn(g, (B, L, H, C), dtype)
+    k = randn(g, (B, L, H, C), dtype)
+    v = randn(g, (B, L, H, C), dtype)
+    q_pts = randn(g, (B, L, H, Pq, 3), "f32")
+    k_pts = randn(g, (B, L, H, Pq, 3), "f32")
+    v_pts = randn(g, (B, L, H, Pv, 3), "f32")
+    rot = rotations(B * L, g).reshape(B, L, 3, 3).contiguous()
+    d = torch.randn(B, L, 3, generator=g, dtype=torch.float64)
+    d = d / d.norm(dim=2, keepdim=True) * step
+    trans = d.cumsum(1).to(torch.float32).contiguous()
+    gamma = torch.nn.functional.softplus(torch.randn(H, generator=g, dtype=torch.float32)).contiguous()
+    pair_bias = randn(g, (B, H, L, L), dtype)
+    z = randn(g, (B, L, L, Cz), dtype)
+    u = torch.rand(B, L, generator=g, dtype=torch.float32)
+    key_mask = (u >= masked_frac).to(torch.uint8).contiguous()
+    return dict(q=q, k=k, v=v, q_pts=q_pts, k_pts=k_pts, v_pts=v_pts, rot=rot, trans=trans,
+                gamma=gamma, pair_bias=pair_bias, z=z, key_mask=key_mask)
+
+
 @dataclass(frozen=True)
 class Workload:
     """A named synthetic workload: shapes, dtype, variants and seeds."""
@@ -157,6 +200,13 @@ WORKLOADS = {
         "evoformer_bf16_nseq128_nres256_h8_c32", "evoformer", "bf16",
         dict(N_seq=128, N_res=256, H=8, C=32), ("row", "col"), seed=5,
         params=dict(masked_frac=0.05)),
+    # Invariant Point Attention at AlphaFold2's structure-module shape: 256
+    # residues, 12 heads of 16 channels, 4 query/key points and 8 value
+    # points per head, a 128-channel pair representation
+    "ipa_bf16_nres256_h12": Workload(
+        "ipa_bf16_nres256_h12", "ipa", "bf16",
+        dict(B=1, L=256, H=12, C=16, Pq=4, Pv=8, Cz=128), ("ipa",), seed=8,
+        params=dict(masked_frac=0.0)),
     # decode against a KV cache: one new token per sequence, GQA 32/8 with head
     # dim 64 (the shape of the small LLM the pages serve), cache lengths mixed
     # uniformly between 512 and 8192 tokens in place of a serving trace
@@ -189,6 +239,9 @@ def make(wl: Workload, S: int | None = None):
         q, k, v, gate, bias, km = evoformer_inputs(s["N_seq"], s["N_res"], s["H"], s["C"],
                                                    wl.dtype, wl.seed, wl.params["masked_frac"])
         return dict(q=q, k=k, v=v, gate=gate, pair_bias=bias, key_mask=km)
+    if wl.kind == "ipa":
+        return ipa_inputs(s["B"], s["L"], s["H"], s["C"], s["Pq"], s["Pv"], s["Cz"], wl.dtype,
+                          wl.seed, wl.params["masked_frac"])
     if wl.kind == "decode":
         q, k, v = decode_inputs(s["B"], s["Hq"], s["Hkv"], s["Sq"], s["S_cap"], s["D"], wl.dtype,
                                 wl.seed)

@@ -32,13 +32,17 @@ VARIANTS = {
 }
 
 
+_SOURCES = ("oracle.c", "ipa.c", "oracle.h")
+
+
 def build(force: bool = False) -> str:
-    """Compile ``oracle.c`` into ``liboracle.so`` with gcc (no GPU code)."""
-    src = os.path.join(_HERE, "oracle.c")
-    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(src):
+    """Compile ``oracle.c`` and ``ipa.c`` into ``liboracle.so`` with gcc (no GPU code)."""
+    srcs = [os.path.join(_HERE, f) for f in _SOURCES]
+    newest = max(os.path.getmtime(f) for f in srcs)
+    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < newest:
         tmp = _SO + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
-                               "-Wall", "-o", tmp, src, "-lm"])
+                               "-Wall", "-o", tmp, *[f for f in srcs if f.endswith(".c")], "-lm"])
         os.replace(tmp, _SO)
     return _SO
 
@@ -77,8 +81,10 @@ def _load():
         lib.oracle_decode_rows.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I,
                                            ctypes.POINTER(_Params), P, I64, I, I]
         lib.oracle_merge_rows.argtypes = [P, P, P, P, I, I64, I]
+        lib.oracle_ipa_rows.argtypes = [P] * 15 + [I] * 7 + [P, I64, I]
         for f in (lib.oracle_attn_rows, lib.oracle_diffattn_rows, lib.oracle_evoformer_row,
-                  lib.oracle_evoformer_col, lib.oracle_decode_rows, lib.oracle_merge_rows):
+                  lib.oracle_evoformer_col, lib.oracle_decode_rows, lib.oracle_merge_rows,
+                  lib.oracle_ipa_rows):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -323,3 +329,39 @@ def evoformer(q, k, v, gate, *, pair_bias=None, key_mask=None, axis="row", scale
             return o.reshape(N_res, N_seq, H, C).transpose(1, 0, 2, 3).copy()
         return o
     raise ValueError("axis must be 'row' or 'col'")
+
+
+def ipa(q, k, v, q_pts, k_pts, v_pts, rot, trans, gamma, *, pair_bias=None, z=None,
+        key_mask=None, rows=None, threads=None):
+    """Attention core of Invariant Point Attention (see ``ipa.c``).
+
+    q, k, v [B,L,H,C]; q_pts, k_pts [B,L,H,Pq,3]; v_pts [B,L,H,Pv,3] (local
+    frames); rot [B,L,3,3], trans [B,L,3]; gamma [H]; pair_bias [B,H,L,L];
+    z [B,L,L,Cz]; key_mask [B,L] uint8.  Returns (o, o_pts, o_pair): with
+    ``rows`` (flat (b*L + i)*H + h) compact [n,C], [n,Pv,3], [n,Cz]; else
+    [B,L,H,C], [B,L,H,Pv,3], [B,L,H,Cz].  o_pair is None without z.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    q_pts, k_pts, v_pts = _f64(q_pts), _f64(k_pts), _f64(v_pts)
+    rot, trans, gamma = _f64(rot), _f64(trans), _f64(gamma)
+    pair_bias, z = _f64(pair_bias), _f64(z)
+    B, L, H, C = q.shape
+    Pq, Pv = q_pts.shape[3], v_pts.shape[3]
+    Cz = 0 if z is None else z.shape[3]
+    assert k.shape == v.shape == q.shape and k_pts.shape == q_pts.shape
+    assert rot.shape == (B, L, 3, 3) and trans.shape == (B, L, 3) and gamma.shape == (H,)
+    km = None if key_mask is None else np.ascontiguousarray(key_mask, dtype=np.uint8)
+    r, n = _rows(rows, B * L * H)
+    o = np.zeros((n, C))
+    op = np.zeros((n, Pv, 3))
+    oz = None if z is None else np.zeros((n, Cz))
+    rc = _load().oracle_ipa_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(q_pts), _ptr(k_pts), _ptr(v_pts),
+                                 _ptr(rot), _ptr(trans), _ptr(gamma), _ptr(pair_bias), _ptr(z),
+                                 _ptr(km), _ptr(o), _ptr(op), _ptr(oz), B, L, H, C, Pq, Pv, Cz,
+                                 _ptr(r), n, threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_ipa_rows failed: %d" % rc)
+    if rows is None:
+        o, op = o.reshape(B, L, H, C), op.reshape(B, L, H, Pv, 3)
+        oz = None if oz is None else oz.reshape(B, L, H, Cz)
+    return o, op, oz

@@ -142,6 +142,27 @@ int oracle_evoformer_col(const double* q, const double* k, const double* v,
                          int N_seq, int N_res, int H, int C, double scale,
                          const int64_t* rows, int64_t n_rows, int nthreads);
 
+/*
+ * Invariant Point Attention, attention core (ipa.c; the definition is
+ * AlphaFold2's, the pages only name the variant).  Per batch entry b, query
+ * residue i and head h:
+ *   q, k, v [B, L, H, C]; q_pts, k_pts [B, L, H, Pq, 3] and v_pts
+ *   [B, L, H, Pv, 3] in the residues' local frames; rot [B, L, 3, 3]
+ *   (row-major) and trans [B, L, 3] map local to global (R x + t);
+ *   gamma [H] (the per-head point weight, >= 0); pair_bias NULL or
+ *   [B, H, L, L] (query i, key j); z NULL or [B, L, L, Cz] (the pair
+ *   representation, query i, key j); key_mask NULL or [B, L] (0 = excluded).
+ * rows: NULL for all, else flat indices (b*L + i)*H + h.  Outputs per row:
+ *   o [n_rows, C], o_pts [n_rows, Pv, 3] (in the query residue's frame),
+ *   o_pair [n_rows, Cz] (NULL exactly when z is NULL).
+ */
+int oracle_ipa_rows(const double* q, const double* k, const double* v, const double* q_pts,
+                    const double* k_pts, const double* v_pts, const double* rot,
+                    const double* trans, const double* gamma, const double* pair_bias,
+                    const double* z, const uint8_t* key_mask, double* o, double* o_pts,
+                    double* o_pair, int B, int L, int H, int C, int Pq, int Pv, int Cz,
+                    const int64_t* rows, int64_t n_rows, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif
