@@ -26,7 +26,7 @@ EVO_AXES = {"row": 0, "col": 1}
 KV_LAYOUTS = {"bhsd": 0, "bshd": 1}
 SYMBOLS = ("fl_attn_fwd", "fl_diffattn_fwd", "fl_evoformer_gated_attn_fwd", "fl_attn_decode_fwd",
            "fl_attn_decode_workspace_size", "fl_attn_decode_num_splits", "fl_attn_merge",
-           "fl_attn_bwd", "fl_status_str", "fl_abi_version")
+           "fl_attn_bwd", "fl_ipa_attn_fwd", "fl_status_str", "fl_abi_version")
 
 
 class FlError(RuntimeError):
@@ -80,8 +80,9 @@ def load_library(path: str | None = None):
     lib.fl_attn_merge.argtypes = [V, V, V, V, I, I64, I, I, V]
     lib.fl_attn_bwd.argtypes = [V, V, V, V, V, V, V, V, V, V, I, I, I, I, I, I, I,
                                 ctypes.POINTER(AttnParams), V]
+    lib.fl_ipa_attn_fwd.argtypes = [V] * 15 + [I] * 8 + [V]
     for f in (lib.fl_attn_fwd, lib.fl_diffattn_fwd, lib.fl_evoformer_gated_attn_fwd,
-              lib.fl_attn_decode_fwd, lib.fl_attn_merge, lib.fl_attn_bwd):
+              lib.fl_attn_decode_fwd, lib.fl_attn_merge, lib.fl_attn_bwd, lib.fl_ipa_attn_fwd):
         f.restype = ctypes.c_int
     lib.fl_status_str.argtypes = [I]
     lib.fl_status_str.restype = ctypes.c_char_p
@@ -332,3 +333,38 @@ def fl_evoformer_gated_attn_fwd(q, k, v, gate, *, pair_bias=None, key_mask=None,
         float(scale if scale is not None else 1.0 / math.sqrt(C)), _stream(stream))
     _check("fl_evoformer_gated_attn_fwd", st)
     return out
+
+
+def fl_ipa_attn_fwd(q, k, v, q_pts, k_pts, v_pts, rot, trans, gamma, *, pair_bias=None, z=None,
+                    key_mask=None, out=None, stream=None):
+    """Attention core of Invariant Point Attention.
+
+    q, k, v [B,L,H,C] bf16; q_pts, k_pts [B,L,H,Pq,3], v_pts [B,L,H,Pv,3],
+    rot [B,L,3,3], trans [B,L,3], gamma [H] float32; pair_bias [B,H,L,L] and
+    z [B,L,L,Cz] bf16; key_mask [B,L] uint8.  Returns (o, o_pts, o_pair);
+    o_pair is None without z.  ``out`` may pass the three output tensors.
+    """
+    q = _dev(q, "q")
+    dt = q.dtype
+    k, v = _dev(k, "k", dt), _dev(v, "v", dt)
+    f32 = torch.float32
+    q_pts, k_pts, v_pts = _dev(q_pts, "q_pts", f32), _dev(k_pts, "k_pts", f32), _dev(v_pts, "v_pts", f32)
+    rot, trans, gamma = _dev(rot, "rot", f32), _dev(trans, "trans", f32), _dev(gamma, "gamma", f32)
+    pair_bias, z = _dev(pair_bias, "pair_bias", dt), _dev(z, "z", dt)
+    key_mask = _dev(key_mask, "key_mask", torch.uint8)
+    B, L, H, C = q.shape
+    Pq, Pv = q_pts.shape[3], v_pts.shape[3]
+    Cz = 0 if z is None else z.shape[3]
+    if out is None:
+        out = (torch.empty_like(q), torch.empty(B, L, H, Pv, 3, dtype=f32, device=q.device),
+               None if z is None else torch.empty(B, L, H, Cz, dtype=dt, device=q.device))
+    o, o_pts, o_pair = out
+    _dev(o, "o", dt)
+    _dev(o_pts, "o_pts", f32)
+    _dev(o_pair, "o_pair", dt)
+    st = load_library().fl_ipa_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(q_pts), _ptr(k_pts), _ptr(v_pts), _ptr(rot), _ptr(trans),
+        _ptr(gamma), _ptr(pair_bias), _ptr(z), _ptr(key_mask), _ptr(o), _ptr(o_pts), _ptr(o_pair),
+        B, L, H, C, Pq, Pv, Cz, _dtype_code(q), _stream(stream))
+    _check("fl_ipa_attn_fwd", st)
+    return o, o_pts, o_pair

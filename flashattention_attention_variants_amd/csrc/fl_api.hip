@@ -5,6 +5,7 @@
 
 #include "flattn.h"
 #include "fl_launch.hpp"
+#include "ipa.hpp"
 
 using namespace fl;
 
@@ -519,6 +520,59 @@ fl_status fl_attn_decode_fwd(const void* q, const void* k_cache, const void* v_c
   const fl_status rc = launch_status(launch_decode_bf16(a, mod, st));
   if (rc != FL_OK || n_split == 1) return rc;
   return launch_status(launch_merge(a.o_part, a.lse_part, n_split, rows, D, o, true, lse, st));
+}
+
+fl_status fl_ipa_attn_fwd(const void* q, const void* k, const void* v, const float* q_pts,
+                          const float* k_pts, const float* v_pts, const float* rot,
+                          const float* trans, const float* gamma, const void* pair_bias,
+                          const void* z, const uint8_t* key_mask, void* o, float* o_pts,
+                          void* o_pair, int B, int L, int H, int C, int P_q, int P_v, int C_z,
+                          fl_dtype dtype, void* stream) {
+  if (B < 0 || L < 0 || H < 1 || C < 1 || P_q < 1 || P_v < 1 || C_z < 0) return FL_ERR_SHAPE;
+  if (L > kMaxSeq) return FL_ERR_SHAPE;
+  if ((z == nullptr) != (o_pair == nullptr)) return FL_ERR_NULL;
+  if (z && C_z < 1) return FL_ERR_SHAPE;
+  if (dtype != FL_BF16) return FL_ERR_UNSUPPORTED;
+  if (C != 16 || P_q != 4 || P_v != 8) return FL_ERR_UNSUPPORTED;
+  if (z && C_z != 64 && C_z != 128) return FL_ERR_UNSUPPORTED;
+  if ((int64_t)B * L == 0) return FL_OK;
+  if (!q || !k || !v || !q_pts || !k_pts || !v_pts || !rot || !trans || !gamma || !o || !o_pts)
+    return FL_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(q_pts, 16) ||
+      !aligned(k_pts, 16) || !aligned(v_pts, 16) || !aligned(o, 16) || !aligned(o_pts, 16) ||
+      !aligned(z, 16) || !aligned(o_pair, 16) || !aligned(rot, 4) || !aligned(trans, 4) ||
+      !aligned(gamma, 4) || !aligned(pair_bias, 2))
+    return FL_ERR_ALIGN;
+  // one residue's pair rows z[b, i, :, :] go through a 32-bit buffer resource
+  if (z && (int64_t)L * C_z * 2 >= ((int64_t)1 << 31)) return FL_ERR_SHAPE;
+  const int64_t n_hg = (H + 3) / 4;
+  if ((int64_t)B * L * n_hg > kMaxGrid) return FL_ERR_SHAPE;
+  IpaArgs a = {};
+  a.q = (const bf16*)q;
+  a.k = (const bf16*)k;
+  a.v = (const bf16*)v;
+  a.q_pts = q_pts;
+  a.k_pts = k_pts;
+  a.v_pts = v_pts;
+  a.rot = rot;
+  a.trans = trans;
+  a.gamma = gamma;
+  a.bias = (const bf16*)pair_bias;
+  a.z = (const bf16*)z;
+  a.kmask = key_mask;
+  a.o = (bf16*)o;
+  a.o_pts = o_pts;
+  a.o_pair = (bf16*)o_pair;
+  a.B = B;
+  a.L = L;
+  a.H = H;
+  // AlphaFold2's weights: w_L = sqrt(1/3) over the three logit terms,
+  // w_C = sqrt(2 / (9 P_q)) on the point distances; base-2 units
+  const double w_l = sqrt(1.0 / 3.0), w_c = sqrt(2.0 / (9.0 * P_q));
+  a.w_scalar = (float)(w_l / sqrt((double)C) * 1.4426950408889634);
+  a.w_bias = (float)(w_l * 1.4426950408889634);
+  a.w_point = (float)(w_l * w_c * 0.5 * 1.4426950408889634);
+  return launch_status(launch_ipa_bf16(a, z ? C_z : 0, (hipStream_t)stream));
 }
 
 fl_status fl_attn_merge(const float* o_parts, const float* lse_parts, void* o, float* lse,

@@ -32,6 +32,11 @@ hipError_t launch_merge(const float* o_part, const float* lse_part, int n_parts,
 // dK, dV launch.
 hipError_t launch_bwd_bf16(const KernelArgs& a, const BwdArgs& g, int mod, hipStream_t st);
 
+// Invariant Point Attention core (ipa.hpp), C = 16, 4 query/key points,
+// 8 value points; cz = pair channels (0: no pair output, 64 or 128).
+struct IpaArgs;
+hipError_t launch_ipa_bf16(const IpaArgs& a, int cz, hipStream_t st);
+
 // float32 path: (dqk, dv, ns, mod) as built in inst_f32.hip.
 hipError_t launch_f32(const KernelArgs& a, int dqk, int dv, int ns, int mod, hipStream_t st);
 

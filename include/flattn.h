@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define FL_ABI_VERSION 2
+#define FL_ABI_VERSION 3
 
 typedef enum {
   FL_OK = 0,
@@ -266,6 +266,45 @@ fl_status fl_attn_bwd(const void* q, const void* k, const void* v, const void* o
                       const float* lse, void* dq, void* dk, void* dv, float* workspace, int B,
                       int H_q, int H_kv, int S_q, int S_k, int D, fl_dtype dtype,
                       const fl_attn_params* params, void* stream);
+
+/*
+ * Attention core of Invariant Point Attention.  The pages name IPA among the
+ * data-dependent variants a score_mod/block_mask template cannot express
+ * (gist.science explainer, "Technical Summary: Problem Statement";
+ * papers.lqhl.me wiki, "问题与动机") but give no formula; the form computed
+ * is AlphaFold2's.  Per batch entry b, query residue i, head h, with frames
+ * T_r = (R_r, t_r) mapping local to global coordinates (x -> R x + t):
+ *   logit_ij = w_L ( q_i.k_j / sqrt(C) + pair_bias_hij
+ *                    - gamma_h w_C / 2 sum_p |T_i q_ip - T_j k_jp|^2 ),
+ *   w_L = sqrt(1/3), w_C = sqrt(2 / (9 P_q));
+ *   a_ij = softmax over the keys key_mask keeps;
+ *   o_i = sum_j a_ij v_j;  o_pts_ip = T_i^-1 sum_j a_ij T_j v_jp;
+ *   o_pair_i = sum_j a_ij z_ij.
+ *   q, k, v        [B, L, H, C] (dtype)
+ *   q_pts, k_pts   [B, L, H, P_q, 3] float32, local coordinates
+ *   v_pts          [B, L, H, P_v, 3] float32, local coordinates
+ *   rot, trans     [B, L, 3, 3] (row-major) and [B, L, 3] float32
+ *   gamma          [H] float32 per-head point weight (AlphaFold2 passes a
+ *                  softplus, so >= 0)
+ *   pair_bias      nullable [B, H, L, L] (query i, key j) (dtype)
+ *   z              nullable [B, L, L, C_z] pair representation (dtype);
+ *                  o_pair is computed exactly when it is given
+ *   key_mask       nullable [B, L] uint8, 0 = the residue is no key
+ *   o              [B, L, H, C] output (dtype)
+ *   o_pts          [B, L, H, P_v, 3] float32 output, in the query's frame
+ *   o_pair         [B, L, H, C_z] output (dtype), NULL exactly when z is
+ * A query with no key gets zero outputs.  Points and frames stay float32
+ * (absolute coordinates of tens of angstroms would lose the distances in
+ * bfloat16).  Supported: FL_BF16 with C = 16, P_q = 4, P_v = 8, C_z in
+ * {64, 128} (or no z), 1 <= H; q/k/v/point/output pointers 16-byte
+ * aligned, rot/trans/gamma 4-byte aligned.  Errors as fl_attn_fwd.
+ */
+fl_status fl_ipa_attn_fwd(const void* q, const void* k, const void* v, const float* q_pts,
+                          const float* k_pts, const float* v_pts, const float* rot,
+                          const float* trans, const float* gamma, const void* pair_bias,
+                          const void* z, const uint8_t* key_mask, void* o, float* o_pts,
+                          void* o_pair, int B, int L, int H, int C, int P_q, int P_v, int C_z,
+                          fl_dtype dtype, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* fl_status_str(fl_status status);

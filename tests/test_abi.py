@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.fl_abi_version() == 2
+    assert lib.fl_abi_version() == 3
     for s in range(7):
         assert lib.fl_status_str(s)
     assert lib.fl_status_str(99) == b"unknown status"
@@ -238,3 +238,30 @@ def test_span_limits(lib):
     b = lambda Sq, Sk: lib.fl_attn_bwd(*([FAKE] * 10), 1, 2, 2, Sq, Sk, 64, api.FL_BF16,
                                        ctypes.byref(params()), None)
     assert b(8, sk) == api.FL_ERR_SHAPE and b(sk, 8) == api.FL_ERR_SHAPE
+
+
+def test_ipa_validation(lib):
+    names = ("q", "k", "v", "q_pts", "k_pts", "v_pts", "rot", "trans", "gamma")
+
+    def f(**kw):
+        return lib.fl_ipa_attn_fwd(*[kw.get(n, FAKE) for n in names], kw.get("bias"), kw.get("z"),
+                                   kw.get("mask"), kw.get("o", FAKE), kw.get("o_pts", FAKE),
+                                   kw.get("o_pair"), kw.get("B", 1), kw.get("L", 16), kw.get("H", 12),
+                                   kw.get("C", 16), kw.get("Pq", 4), kw.get("Pv", 8),
+                                   kw.get("Cz", 0), kw.get("dt", api.FL_BF16), None)
+    assert f(gamma=None) == api.FL_ERR_NULL
+    assert f(o_pts=None) == api.FL_ERR_NULL
+    assert f(z=FAKE, Cz=128) == api.FL_ERR_NULL             # z without o_pair
+    assert f(o_pair=FAKE, Cz=128) == api.FL_ERR_NULL        # o_pair without z
+    assert f(L=-1) == api.FL_ERR_SHAPE
+    assert f(H=0) == api.FL_ERR_SHAPE
+    assert f(C=32) == api.FL_ERR_UNSUPPORTED
+    assert f(Pq=3) == api.FL_ERR_UNSUPPORTED
+    assert f(z=FAKE, o_pair=FAKE, Cz=96) == api.FL_ERR_UNSUPPORTED
+    assert f(dt=api.FL_F32) == api.FL_ERR_UNSUPPORTED
+    assert f(k_pts=MISALIGNED) == api.FL_ERR_ALIGN
+    assert f(rot=P(0x10002)) == api.FL_ERR_ALIGN
+    assert f(z=FAKE, o_pair=MISALIGNED, Cz=128) == api.FL_ERR_ALIGN
+    # one residue's pair rows stay below 2^31 bytes
+    assert f(z=FAKE, o_pair=FAKE, Cz=128, L=1 << 23) == api.FL_ERR_SHAPE
+    assert f(B=0, q=None, o=None) == api.FL_OK
