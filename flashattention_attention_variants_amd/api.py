@@ -18,7 +18,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libflattn.so")
 
-FL_OK, FL_ERR_NULL, FL_ERR_SHAPE, FL_ERR_ALIGN, FL_ERR_UNSUPPORTED, FL_ERR_PARAM, FL_ERR_LAUNCH = range(7)
+(FL_OK, FL_ERR_NULL, FL_ERR_SHAPE, FL_ERR_ALIGN, FL_ERR_UNSUPPORTED, FL_ERR_PARAM, FL_ERR_LAUNCH,
+ FL_ERR_SCRATCH) = range(8)
 FL_BF16, FL_F32 = 0, 1
 VARIANTS = {"vanilla": 0, "alibi": 1, "softcap": 2, "causal": 3, "sliding_window": 4,
             "prefix_lm": 5, "document": 6}
@@ -26,7 +27,8 @@ EVO_AXES = {"row": 0, "col": 1}
 KV_LAYOUTS = {"bhsd": 0, "bshd": 1}
 SYMBOLS = ("fl_attn_fwd", "fl_diffattn_fwd", "fl_evoformer_gated_attn_fwd", "fl_attn_decode_fwd",
            "fl_attn_decode_workspace_size", "fl_attn_decode_num_splits", "fl_attn_merge",
-           "fl_attn_bwd", "fl_ipa_attn_fwd", "fl_status_str", "fl_abi_version")
+           "fl_attn_decode_fwd_noalloc", "fl_attn_bwd", "fl_ipa_attn_fwd", "fl_status_str",
+           "fl_abi_version")
 
 
 class FlError(RuntimeError):
@@ -81,8 +83,11 @@ def load_library(path: str | None = None):
     lib.fl_attn_bwd.argtypes = [V, V, V, V, V, V, V, V, V, V, I, I, I, I, I, I, I,
                                 ctypes.POINTER(AttnParams), V]
     lib.fl_ipa_attn_fwd.argtypes = [V] * 15 + [I] * 8 + [V]
+    lib.fl_attn_decode_fwd_noalloc.argtypes = [V, V, V, V, V, V, I, I, I, I, I, I, I, I, I,
+                                               ctypes.POINTER(AttnParams), I, V]
     for f in (lib.fl_attn_fwd, lib.fl_diffattn_fwd, lib.fl_evoformer_gated_attn_fwd,
-              lib.fl_attn_decode_fwd, lib.fl_attn_merge, lib.fl_attn_bwd, lib.fl_ipa_attn_fwd):
+              lib.fl_attn_decode_fwd, lib.fl_attn_merge, lib.fl_attn_bwd, lib.fl_ipa_attn_fwd,
+              lib.fl_attn_decode_fwd_noalloc):
         f.restype = ctypes.c_int
     lib.fl_status_str.argtypes = [I]
     lib.fl_status_str.restype = ctypes.c_char_p
@@ -239,6 +244,37 @@ def fl_attn_decode_fwd(q, k_cache, v_cache, cache_seqlens, *, max_seqlen=None, l
         lay, _dtype_code(q), ctypes.byref(p), int(num_splits), _stream(stream))
     _check("fl_attn_decode_fwd", st)
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def fl_attn_decode_fwd_noalloc(q, k_cache, v_cache, cache_seqlens, *, out, lse=None,
+                               max_seqlen=None, layout="bhsd", variant="vanilla", mask=None,
+                               scale=None, softcap=50.0, alibi_max_bias=8.0, window=256,
+                               window_causal=True, prefix=512, num_splits=0, stream=None):
+    """:func:`fl_attn_decode_fwd` with the library's static scratch buffer in
+    place of a workspace; ``out`` (and ``lse``, if wanted) are the caller's
+    tensors, so nothing is allocated here either.  Returns ``out`` or
+    ``(out, lse)``."""
+    q = _dev(q, "q")
+    dt = q.dtype
+    k_cache, v_cache = _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt)
+    seqlens = _dev(cache_seqlens, "cache_seqlens", torch.int32)
+    B, Hq, Sq, D = q.shape
+    lay = KV_LAYOUTS[layout]
+    if lay == 0:
+        _, Hkv, S_cap, _ = k_cache.shape
+    else:
+        _, S_cap, Hkv, _ = k_cache.shape
+    if max_seqlen is None:
+        max_seqlen = S_cap
+    _dev(out, "out", dt)
+    _dev(lse, "lse", torch.float32)
+    p = _params(variant, mask, scale, D, softcap, alibi_max_bias, window, window_causal, prefix)
+    st = load_library().fl_attn_decode_fwd_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq,
+        S_cap, int(max_seqlen), D, lay, _dtype_code(q), ctypes.byref(p), int(num_splits),
+        _stream(stream))
+    _check("fl_attn_decode_fwd_noalloc", st)
+    return (out, lse) if lse is not None else out
 
 
 def fl_attn_merge(o_parts, lse_parts, *, out_dtype=torch.bfloat16, out=None, lse=None,

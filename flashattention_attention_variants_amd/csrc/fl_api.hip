@@ -172,6 +172,7 @@ const char* fl_status_str(fl_status s) {
     case FL_ERR_UNSUPPORTED: return "head dimension / dtype combination not built";
     case FL_ERR_PARAM: return "variant parameter out of range";
     case FL_ERR_LAUNCH: return "kernel launch failed";
+    case FL_ERR_SCRATCH: return "the call needs more than the library's static scratch buffer";
   }
   return "unknown status";
 }
@@ -408,11 +409,15 @@ int64_t fl_attn_decode_workspace_size(int B, int H_q, int H_kv, int S_q, int max
   return decode_workspace(B, H_q, S_q, D, n_split);
 }
 
-fl_status fl_attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache,
-                             const int32_t* cache_seqlens, void* o, float* lse, void* workspace,
-                             size_t workspace_bytes, int B, int H_q, int H_kv, int S_q, int S_cap,
-                             int max_seqlen, int D, fl_kv_layout layout, fl_dtype dtype,
-                             const fl_attn_params* p, int num_splits, void* stream) {
+}  // extern "C"
+
+namespace fl {
+
+fl_status decode_fwd(const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* cache_seqlens, void* o, float* lse, DecodeWorkspaceFn get_ws,
+                     void* ws_ctx, int B, int H_q, int H_kv, int S_q, int S_cap, int max_seqlen,
+                     int D, fl_kv_layout layout, fl_dtype dtype, const fl_attn_params* p,
+                     int num_splits, void* stream) {
   if (!p) return FL_ERR_NULL;
   if (!decode_sizes_ok(B, H_q, H_kv, S_q, max_seqlen) || S_cap < 0 || S_cap > kMaxSeq || D < 1)
     return FL_ERR_SHAPE;
@@ -434,14 +439,12 @@ fl_status fl_attn_decode_fwd(const void* q, const void* k_cache, const void* v_c
   if ((int64_t)B * H_q * S_q == 0) return FL_OK;  // no output element
   if (!q || !o || !cache_seqlens || (S_cap > 0 && (!k_cache || !v_cache))) return FL_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
-      !aligned(lse, 4) || !aligned(cache_seqlens, 4) || !aligned(workspace, 16))
+      !aligned(lse, 4) || !aligned(cache_seqlens, 4))
     return FL_ERR_ALIGN;
 
   const int G = H_q / H_kv;
   const int n_split = decode_split(B, H_q, H_kv, S_q, max_seqlen, p, num_splits);
   const int64_t ws = decode_workspace(B, H_q, S_q, D, n_split);
-  if (ws > 0 && !workspace) return FL_ERR_NULL;
-  if ((int64_t)workspace_bytes < ws) return FL_ERR_PARAM;
 
   KernelArgs a;
   init_args(a);
@@ -511,15 +514,52 @@ fl_status fl_attn_decode_fwd(const void* q, const void* k_cache, const void* v_c
   a.n_split = n_split;
   if ((int64_t)a.n_qt * B * H_kv * n_split > kMaxGrid) return FL_ERR_SHAPE;
   const int64_t rows = (int64_t)B * H_q * S_q;
+  if (n_split > 1 && (rows + 3) / 4 > kMaxGrid) return FL_ERR_SHAPE;
+  // everything checked: only now is the workspace asked for
+  void* workspace = nullptr;
+  const fl_status wrc = get_ws(ws, ws_ctx, &workspace);
+  if (wrc != FL_OK) return wrc;
   if (n_split > 1) {
     a.o_part = (float*)workspace;
     a.lse_part = (float*)((char*)workspace + (int64_t)n_split * rows * D * 4);
-    if ((rows + 3) / 4 > kMaxGrid) return FL_ERR_SHAPE;
   }
   hipStream_t st = (hipStream_t)stream;
   const fl_status rc = launch_status(launch_decode_bf16(a, mod, st));
   if (rc != FL_OK || n_split == 1) return rc;
   return launch_status(launch_merge(a.o_part, a.lse_part, n_split, rows, D, o, true, lse, st));
+}
+
+}  // namespace fl
+
+namespace {
+
+// the caller's workspace: present when needed, large enough, 16-byte aligned
+struct CallerWorkspace {
+  void* ptr;
+  size_t bytes;
+};
+
+fl_status caller_workspace(int64_t need, void* ctx, void** ws) {
+  const CallerWorkspace* c = (const CallerWorkspace*)ctx;
+  if (need > 0 && !c->ptr) return FL_ERR_NULL;
+  if ((int64_t)c->bytes < need) return FL_ERR_PARAM;
+  *ws = c->ptr;
+  return FL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fl_status fl_attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* cache_seqlens, void* o, float* lse, void* workspace,
+                             size_t workspace_bytes, int B, int H_q, int H_kv, int S_q, int S_cap,
+                             int max_seqlen, int D, fl_kv_layout layout, fl_dtype dtype,
+                             const fl_attn_params* p, int num_splits, void* stream) {
+  if (!aligned(workspace, 16)) return FL_ERR_ALIGN;
+  CallerWorkspace cw = {workspace, workspace_bytes};
+  return decode_fwd(q, k_cache, v_cache, cache_seqlens, o, lse, caller_workspace, &cw, B, H_q,
+                    H_kv, S_q, S_cap, max_seqlen, D, layout, dtype, p, num_splits, stream);
 }
 
 fl_status fl_ipa_attn_fwd(const void* q, const void* k, const void* v, const float* q_pts,

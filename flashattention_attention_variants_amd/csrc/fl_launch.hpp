@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include "fl_common.hpp"
+#include "flattn.h"
 
 namespace fl {
 
@@ -39,6 +40,16 @@ hipError_t launch_ipa_bf16(const IpaArgs& a, int cz, hipStream_t st);
 
 // float32 path: (dqk, dv, ns, mod) as built in inst_f32.hip.
 hipError_t launch_f32(const KernelArgs& a, int dqk, int dv, int ns, int mod, hipStream_t st);
+
+// Decode against a KV cache with the workspace from a supplier: once the
+// call is validated, get_ws(bytes, ctx, &ptr) provides `bytes` of device
+// memory (0 when the call uses one key range) or returns the error status.
+typedef fl_status (*DecodeWorkspaceFn)(int64_t bytes, void* ctx, void** ws);
+fl_status decode_fwd(const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* cache_seqlens, void* o, float* lse, DecodeWorkspaceFn get_ws,
+                     void* ws_ctx, int B, int H_q, int H_kv, int S_q, int S_cap, int max_seqlen,
+                     int D, fl_kv_layout layout, fl_dtype dtype, const fl_attn_params* p,
+                     int num_splits, void* stream);
 
 // Query rows per work-group of each family.
 constexpr int mfma_rows_per_wg(int qb) { return 4 * 32 * qb; }

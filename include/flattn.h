@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define FL_ABI_VERSION 3
+#define FL_ABI_VERSION 4
 
 typedef enum {
   FL_OK = 0,
@@ -46,7 +46,9 @@ typedef enum {
   FL_ERR_ALIGN = 3,       /* a pointer or row is not aligned as required */
   FL_ERR_UNSUPPORTED = 4, /* head dimension / dtype combination not built */
   FL_ERR_PARAM = 5,       /* a variant parameter is out of range */
-  FL_ERR_LAUNCH = 6       /* the kernel launch failed */
+  FL_ERR_LAUNCH = 6,      /* the kernel launch failed */
+  FL_ERR_SCRATCH = 7      /* the call needs more scratch than the library's static
+                             buffer holds (fl_attn_decode_fwd_noalloc) */
 } fl_status;
 
 typedef enum { FL_BF16 = 0, FL_F32 = 1 } fl_dtype;
@@ -266,6 +268,26 @@ fl_status fl_attn_bwd(const void* q, const void* k, const void* v, const void* o
                       const float* lse, void* dq, void* dk, void* dv, float* workspace, int B,
                       int H_q, int H_kv, int S_q, int S_k, int D, fl_dtype dtype,
                       const fl_attn_params* params, void* stream);
+
+/*
+ * fl_attn_decode_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The float32 partial results of
+ * a split call go to a static device buffer of FL_DECODE_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends; the
+ * call itself allocates nothing.  Arguments, split choice, results and
+ * errors are those of fl_attn_decode_fwd, plus FL_ERR_SCRATCH (returned
+ * before anything is launched) when fl_attn_decode_workspace_size for the
+ * same arguments exceeds FL_DECODE_SCRATCH_BYTES.  Every call on one GPU
+ * shares that GPU's buffer: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller.  Added in ABI 4.
+ */
+#define FL_DECODE_SCRATCH_BYTES (32u << 20)
+fl_status fl_attn_decode_fwd_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* cache_seqlens, void* o, float* lse, int B,
+                                     int H_q, int H_kv, int S_q, int S_cap, int max_seqlen, int D,
+                                     fl_kv_layout layout, fl_dtype dtype,
+                                     const fl_attn_params* params, int num_splits, void* stream);
 
 /*
  * Attention core of Invariant Point Attention.  The pages name IPA among the

@@ -36,8 +36,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.fl_abi_version() == 3
-    for s in range(7):
+    assert lib.fl_abi_version() == 4
+    for s in range(8):
         assert lib.fl_status_str(s)
     assert lib.fl_status_str(99) == b"unknown status"
 
@@ -265,3 +265,25 @@ def test_ipa_validation(lib):
     # one residue's pair rows stay below 2^31 bytes
     assert f(z=FAKE, o_pair=FAKE, Cz=128, L=1 << 23) == api.FL_ERR_SHAPE
     assert f(B=0, q=None, o=None) == api.FL_OK
+
+
+def test_decode_noalloc_validation(lib):
+    """The no-allocation decode validates like fl_attn_decode_fwd and rejects,
+    before touching the runtime, a call whose partial results would not fit
+    the static buffer."""
+    def f(p, **kw):
+        return lib.fl_attn_decode_fwd_noalloc(
+            kw.get("q", FAKE), FAKE, FAKE, kw.get("seqlens", FAKE), kw.get("o", FAKE), None,
+            kw.get("B", 2), kw.get("Hq", 8), 2, 1, kw.get("S_cap", 256), kw.get("max_len", 256), 64,
+            0, api.FL_BF16, None if p is None else ctypes.byref(p), kw.get("splits", 1), None)
+    assert f(None) == api.FL_ERR_NULL
+    assert f(params(), seqlens=None) == api.FL_ERR_NULL
+    assert f(params(), o=MISALIGNED) == api.FL_ERR_ALIGN
+    assert f(params(variant=4, window=0)) == api.FL_ERR_PARAM
+    # 256 key ranges of 2048 rows x 65 floats: 136 MB, past the 32 MiB buffer
+    big = dict(B=64, Hq=32, S_cap=65536, max_len=65536, splits=256)
+    need = lib.fl_attn_decode_workspace_size(64, 32, 2, 1, 65536, 64, None, 256)
+    assert need > (32 << 20)
+    assert f(params(), **big) == api.FL_ERR_SCRATCH
+    assert lib.fl_status_str(api.FL_ERR_SCRATCH)
+    assert f(params(), B=0, q=None, o=None) == api.FL_OK
