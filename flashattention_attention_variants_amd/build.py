@@ -52,50 +52,32 @@ def _check_stubs(objs: list[str]) -> None:
             raise RuntimeError("%s: kernel stubs not emitted: %s" % (o, ", ".join(missing[:3])))
 
 
-def _vregs(tok: str) -> set[int]:
-    m = re.match(r"v\[(\d+):(\d+)\]", tok)
-    if m:
-        return set(range(int(m.group(1)), int(m.group(2)) + 1))
-    m = re.match(r"v(\d+)$", tok)
-    return {int(m.group(1))} if m else set()
-
-
-def _check_lds_transpose_reads(asm: str) -> None:
-    """The transposed LDS reads are inline assembly whose results are valid
-    only after the following `s_waitcnt lgkmcnt(0)`; the compiler does not
-    know that.  Fail if any instruction reads or writes one of their
-    destination registers before that wait (for instance a register copy
-    made under register pressure), which would use data not yet loaded."""
-    pending: dict[int, int] = {}
+def _check_asm_loads(asm: str) -> None:
+    """Inline assembly in the kernels may issue loads only into LDS
+    (buffer_load ... lds, which writes no register): a load written in
+    inline assembly whose destination is a register would leave that
+    register's write in flight behind the compiler's back.  Fail on any
+    register-destination load inside an inline-assembly region."""
     in_asm, kernel = False, ""
     with open(asm) as fh:
         for n, line in enumerate(fh, 1):
             t = line.strip()
             if re.match(r"^_Z\S+:", t):
-                kernel, pending = t, {}
+                kernel = t
             if t.startswith(";;#ASMSTART"):
                 in_asm = True
                 continue
             if t.startswith(";;#ASMEND"):
                 in_asm = False
                 continue
-            if not t or t[0] in ";.":
+            if not in_asm or not t or t[0] in ";.":
                 continue
-            op, *args = t.split()
-            args = [a.strip(",") for a in args]
-            if op == "s_waitcnt" and "lgkmcnt(0)" in t:
-                pending = {}
-                continue
-            if in_asm and op == "ds_read_b64_tr_b16":
-                for r in _vregs(args[0]):
-                    pending[r] = n
-                continue
-            used = set().union(*(_vregs(a) for a in args)) if args else set()
-            hit = used & pending.keys()
-            if hit:
-                raise RuntimeError("%s:%d: %s touches v%d before its LDS transpose read "
-                                   "(line %d) completed, in %s" % (asm, n, t, min(hit),
-                                                                  pending[min(hit)], kernel[:90]))
+            op = t.split()[0]
+            loads = op.startswith(("ds_read", "global_load", "flat_load", "scratch_load",
+                                   "buffer_load", "s_load", "s_buffer_load"))
+            if loads and not (op.startswith("buffer_load") and t.rstrip().endswith(" lds")):
+                raise RuntimeError("%s:%d: register-destination load in inline assembly: %s "
+                                   "(in %s)" % (asm, n, t, kernel[:90]))
 
 
 def build(jobs: int | None = None, extra: list[str] | None = None, verbose: bool = False) -> str:
@@ -108,7 +90,7 @@ def build(jobs: int | None = None, extra: list[str] | None = None, verbose: bool
     _check_stubs(objs)
     for o in objs:
         for asm in glob.glob(o[:-2] + "-hip-amdgcn-amd-amdhsa-*.s"):
-            _check_lds_transpose_reads(asm)
+            _check_asm_loads(asm)
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

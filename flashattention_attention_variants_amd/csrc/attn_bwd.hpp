@@ -244,15 +244,9 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
   auto read_tr = [&](uint32_t tb, int kb, bf16x8 (&op)[D / 32][2]) {
     u32x2 raw[D / 32 * 4];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const uint32_t ad = tb + 2 * tr[db];
-      u32x2* r = raw + 4 * db;
-      if (kb == 0)
-        ds_read_tr4<0, 16 * D, 32 * D, 48 * D>(ad, r[0], r[1], r[2], r[3]);
-      else
-        ds_read_tr4<64 * D, 80 * D, 96 * D, 112 * D>(ad, r[0], r[1], r[2], r[3]);
-    }
-    lds_fence(raw);
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) raw[4 * db + i] = ds_read_tr(tb + 2 * tr[db] + 2 * (8 * i + 32 * kb) * D);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll

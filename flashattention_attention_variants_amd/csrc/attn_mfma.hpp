@@ -68,7 +68,10 @@ struct MfmaCfg {
   // SIMD, and the streams meet through LDS at the end.
   static constexpr bool SPLIT = NS_ == 2;
   static constexpr int NSU = SPLIT ? 1 : NS_;  // streams per wave
-  static constexpr int NW = DEC ? FL_DEC_WAVES : (SPLIT ? 8 : 4);
+#ifndef FL_FWD_WAVES
+#define FL_FWD_WAVES 4
+#endif
+  static constexpr int NW = DEC ? FL_DEC_WAVES : (SPLIT ? 8 : (GATE ? 4 : FL_FWD_WAVES));
   static constexpr int RW = SPLIT ? NW / NS_ : NW;  // waves per stream (row blocks)
   static constexpr int BM = RW * 32 * QB;    // query rows per work-group
   static constexpr int BN = 64;              // keys per tile
@@ -90,7 +93,10 @@ struct MfmaCfg {
 #ifndef FL_EVO_STAGES
 #define FL_EVO_STAGES 3
 #endif
-  static constexpr int STAGES = DEC ? FL_DEC_STAGES : (GATE ? FL_EVO_STAGES : 3);
+#ifndef FL_FWD_STAGES
+#define FL_FWD_STAGES 3
+#endif
+  static constexpr int STAGES = DEC ? FL_DEC_STAGES : (GATE ? FL_EVO_STAGES : FL_FWD_STAGES);
   __device__ static constexpr int kswz(int row) { return KCPR == 4 ? (row >> 1) & 3 : row & 7; }
   __device__ static constexpr int vswz(int row) { return VCPR == 4 ? 2 * ((row >> 1) & 1) : 2 * (row & 3); }
   static constexpr int KCH = BN * DQK / 8 / (NW * 64);  // 16-byte K chunks per thread
@@ -137,14 +143,36 @@ __device__ __forceinline__ bf16x8 load16(__amdgpu_buffer_rsrc_t rs, int byte_off
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0));
 }
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes land
-// at lds + 16*l (lds is wave-uniform).  The builtin exists only in the device
-// pass; keeping it out of the host pass keeps the kernel's host-side launch
-// stub intact.
+// at lds + 16*l (lds is wave-uniform).  Issued from assembly: the compiler's
+// wait-count pass cannot tell which LDS bytes such a load writes, and would
+// make every later LDS read wait for all tiles still in flight (the next
+// tiles' loads included), which serialises the tile pipeline.  The pipeline
+// waits for these loads itself (s_waitcnt vmcnt before the barrier that
+// publishes a tile).  The load writes no register; M0, which carries the LDS
+// address, is restored before the statement ends.
 __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, void* lds, int byte_off) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
-                                           byte_off, 0, 0, 0);
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(byte_off), "s"(rs));
 #else
   (void)rs;
   (void)lds;
@@ -159,45 +187,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// LDS byte address of a pointer into __shared__ memory.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// Four transposed 8-byte LDS reads (ds_read_b64_tr_b16) from one address at
-// immediate byte offsets.  They are written as assembly because the
-// compiler's wait-count pass cannot tell them apart from the tile loads still
-// streaming into other LDS stages and would make them wait for those loads.
-// The results may be used only after lds_fence() has taken them.
-template <int O0, int O1, int O2, int O3>
-__device__ __forceinline__ void ds_read_tr4(uint32_t addr, u32x2& r0, u32x2& r1, u32x2& r2, u32x2& r3) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %4 offset:%5\n\t"
-      "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
-      "ds_read_b64_tr_b16 %2, %4 offset:%7\n\t"
-      "ds_read_b64_tr_b16 %3, %4 offset:%8"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-      : "v"(addr), "n"(O0), "n"(O1), "n"(O2), "n"(O3));
-}
-
-// Wait for this wave's outstanding LDS reads; the registers pass through the
-// statement, so no use of them can be scheduled before the wait.
-__device__ __forceinline__ void lds_fence(u32x2 (&r)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
-}
-__device__ __forceinline__ void lds_fence(u32x2 (&r)[8]) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]),
-                 "+v"(r[7]));
-}
-__device__ __forceinline__ void lds_fence(u32x2 (&r)[16]) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]),
-                 "+v"(r[7]), "+v"(r[8]), "+v"(r[9]), "+v"(r[10]), "+v"(r[11]), "+v"(r[12]),
-                 "+v"(r[13]), "+v"(r[14]), "+v"(r[15]));
+// One transposed 8-byte LDS read (ds_read_b64_tr_b16) at LDS byte address
+// `addr`: the 16 lanes of a block each point at 4 consecutive 16-bit values
+// of a 4 x 16 block (row i/4, columns 4(i%4)..+3 for lane i) and lane i
+// receives column i, rows 0..3.
+__device__ __forceinline__ u32x2 ds_read_tr(uint32_t addr) {
+  return __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)addr));
 }
 
 #ifndef FL_SCHED_INTERLEAVE
@@ -250,6 +246,7 @@ __device__ __forceinline__ void unit_hint_scapb() {
 #ifndef FL_FAST_VALU
 #define FL_FAST_VALU 5
 #endif
+
 // One unit of the unchecked first pass on plain folded scores: the K
 // operand reads, then each of the ten matrix instructions followed by a
 // share of the vector work (5 per instruction measured 1.5% faster on
@@ -777,19 +774,15 @@ void attn_mfma_kernel(KernelArgs a) {
     u32x2 vraw[DV / 32 * 4];  // [db][h2][half]
     bf16x8 vop[DV / 32][2];   // [db][h2]
     const uint32_t vbase = lds_addr(ks + NS * C::K_ELEMS);
+    // rows v_row + 8i (+ 32 for the second key half) of the V tile
     auto read_v = [&](int kb) {
 #pragma unroll
-      for (int db = 0; db < DV / 32; ++db) {
-        const uint32_t ad = vbase + 2 * v_rd[db];
-        u32x2* r = vraw + 4 * db;
-        if (kb == 0)
-          ds_read_tr4<0, 16 * DV, 32 * DV, 48 * DV>(ad, r[0], r[1], r[2], r[3]);
-        else
-          ds_read_tr4<64 * DV, 80 * DV, 96 * DV, 112 * DV>(ad, r[0], r[1], r[2], r[3]);
-      }
+      for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          vraw[4 * db + i] = ds_read_tr(vbase + 2 * v_rd[db] + 2 * (8 * i + 32 * kb) * DV);
     };
     auto take_v = [&]() {
-      lds_fence(vraw);
 #pragma unroll
       for (int db = 0; db < DV / 32; ++db)
 #pragma unroll

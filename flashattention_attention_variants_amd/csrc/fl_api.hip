@@ -240,7 +240,7 @@ fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* b
   // tiles and balance worse, so masked rows take them only when the grid is
   // deep (eight work-groups per unit); a sliding window, whose rows see few
   // keys, never does.
-  const int64_t wg2 = (int64_t)grid_qtiles(S_q, mfma_rows_per_wg(2)) * B * H_q;
+  const int64_t wg2 = (int64_t)grid_qtiles(S_q, attn_rows_per_wg(2)) * B * H_q;
 #ifdef FL_FORCE_QB
   const int qb = FL_FORCE_QB;
 #else
@@ -254,7 +254,7 @@ fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* b
   else
     qb = wg2 >= 2048 ? 2 : 1;
 #endif
-  a.n_qt = grid_qtiles(S_q, mfma_rows_per_wg(qb));
+  a.n_qt = grid_qtiles(S_q, attn_rows_per_wg(qb));
   if ((int64_t)a.n_qt * B * H_q > kMaxGrid) return FL_ERR_SHAPE;
   return launch_status(launch_attn_bf16(a, qb, mod, bias != nullptr, st));
 }

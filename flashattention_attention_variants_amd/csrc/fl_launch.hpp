@@ -53,6 +53,11 @@ fl_status decode_fwd(const void* q, const void* k_cache, const void* v_cache,
 
 // Query rows per work-group of each family.
 constexpr int mfma_rows_per_wg(int qb) { return 4 * 32 * qb; }
+#ifndef FL_FWD_WAVES
+#define FL_FWD_WAVES 4
+#endif
+// fl_attn_fwd's work-groups: FL_FWD_WAVES waves of 32 qb rows each
+constexpr int attn_rows_per_wg(int qb) { return FL_FWD_WAVES * 32 * qb; }
 constexpr int f32_rows_per_wg() { return 64; }
 
 }  // namespace fl

@@ -8,7 +8,7 @@ template <class C>
 static hipError_t go(const KernelArgs& a, hipStream_t st) {
   const int nwg = a.nb * a.nh * a.n_qt;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(attn_mfma_kernel<C>, dim3(nwg), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(attn_mfma_kernel<C>, dim3(nwg), dim3(C::NW * 64), 0, st, a);
   return hipGetLastError();
 }
 
