@@ -3,9 +3,22 @@
 // With S = scale Q K^T, s = mod(S) masked, P = softmax(s) and the saved
 // LSE, the gradients of a loss with output gradient dO are
 //
-//   D_i = sum_d dO_id O_id                     (= rowsum(P * dP))
+//   D_i = sum_j P_ij dP_ij                     (= sum_d dO_id O_id)
 //   dP  = dO V^T,   dS = P * (dP - D) * mod'(S)
 //   dQ  = scale dS K,   dK = scale dS^T Q,   dV = P^T dO
+//
+// D is never taken from the stored output, and P is renormalised: dO . O
+// with O rounded to bf16 carries an error of about 2^-9 |dO| |O|, and the P
+// recomputed from the forward's LSE sums to 1 only within the rounding of
+// the forward's row sum (up to 0.4% off at logits of standard deviation
+// 25); under a sharp softmax dP - D is a small difference of large values,
+// so either error dominates the gradients (1.1% mean relative error of dQ
+// at those logits).  The dQ launch runs its sweep with D~ = dO . O and, in
+// float32 beside it, Z = sum_j P and Dx = sum_j P dP; with P/Z exact and
+// D = Dx / Z, and dQ linear in D, one more product corrects it at the end:
+// dQ = scale / Z (dS~ K + (D~ - D) E), E = sum_j P mod' K.  It writes D
+// for the dK, dV launch, whose P keeps the factor Z (a relative error of
+// the order of the forward's rounding, not amplified).
 //
 // with mod' = 1 for plain scores and ALiBi (an additive term) and
 // 1 - tanh^2(S / cap) for softcap; P is recomputed from the scores and the
@@ -18,7 +31,8 @@
 // work-group streams 64-entry tiles of two tensors T1, T2 through LDS:
 //
 //   role   rows         T1, T2        products per 32x32 unit
-//   DQ     queries      K, V          X = S^T, Y = dP^T; dQ^T += K^T dS^T
+//   DQ     queries      K, V          X = S^T, Y = dP^T; dQ^T += K^T dS^T,
+//                                                        E^T  += K^T (P mod')^T
 //   DKDV   keys         Q, dO         X = S,   Y = dP;   dK^T += Q^T dS,
 //                                                        dV^T += dO^T P
 //
@@ -126,7 +140,6 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
     }
     delta_row = part + __shfl_xor(part, 32);
     const int64_t li = b * a.lse_sb + hr * a.lse_sh + row;
-    if (g == 0 && wr0 + c < a.sq) g2.delta[li] = delta_row;
     const float l = a.lse[0][li];
     lse2_row = l == kNegInf ? __builtin_inff() : l * kLog2e;  // no key: every p is 0
     key_interval(a, b, row, lane_lo, lane_hi);
@@ -232,7 +245,8 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
     tr[db] = tr_row * D + 8 * ((d >> 3) ^ C::swz(tr_row)) + (d & 7);
   }
 
-  f32x16 acc1[D / 32], acc2[D / 32];
+  f32x16 acc1[D / 32], acc2[D / 32];  // DQ: dQ^T and E^T; DKDV: dK^T and dV^T
+  float dex = 0.0f, zex = 0.0f;        // DQ: this lane's parts of Dx and Z
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
     acc1[db] = f32x16{};
@@ -318,7 +332,13 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
         const float dl = DQ ? delta_row : del4[r];
         float p = fast_exp2(s - l2);
         if constexpr (MASKED) p = (ent >= lane_lo && ent <= lane_hi) ? p : 0.0f;
-        pp[r] = p;
+        if constexpr (DQ) {
+          dex = fmaf(p, y[r], dex);
+          zex += p;
+          pp[r] = p * dmod;
+        } else {
+          pp[r] = p;
+        }
         ds[r] = p * (y[r] - dl) * dmod;
       }
       // B operands: 16-entry steps 2kb and 2kb + 1 in the permuted order
@@ -339,8 +359,11 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
+        for (int h2 = 0; h2 < 2; ++h2) {
           acc1[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op1[db][h2], pds[h2], acc1[db], 0, 0, 0);
+          if constexpr (DQ)
+            acc2[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op1[db][h2], ppk[h2], acc2[db], 0, 0, 0);
+        }
       if constexpr (!DQ) {
         bf16x8 op2[D / 32][2];
         read_tr(lds_addr(t2), kb, op2);
@@ -381,8 +404,23 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
   }
 
   // ---- epilogue: lane = row, registers = head dimension --------------------------
+  // DQ: the exact D (both lane halves), the correction of dQ, D for dK, dV
+  float dfix = 0.0f, zinv = 1.0f;
+  if constexpr (DQ) {
+    const float z = zex + __shfl_xor(zex, 32);
+    zinv = z > 0.0f ? 1.0f / z : 0.0f;  // no key: every product is zero
+    const float dn = (dex + __shfl_xor(dex, 32)) * zinv;
+    dfix = delta_row - dn;
+    if (g == 0 && wr0 + c < a.sq) g2.delta[b * a.lse_sb + hr * a.lse_sh + row] = dn;
+  }
   if (wr0 + c >= n_rows) return;
   const float sc = a.scale_log2 * kLn2;  // scale
+  if constexpr (DQ) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc1[db][r] = fmaf(dfix, acc2[db][r], acc1[db][r]) * zinv;
+  }
   bf16* o1;
   bf16* o2 = nullptr;
   if constexpr (DQ) {
