@@ -106,6 +106,23 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
   const int row = min(wr0 + c, n_rows - 1);        // this lane's row (clamped)
   const bool wave_idle = wr0 >= n_rows;
 
+  // Document mask: the batch entry's offsets go to LDS once, where the
+  // prologue's interval searches read them (a search through global memory
+  // costs a round trip per step); the tiles overwrite them after the
+  // barrier that closes the prologue.  A document's keys and queries are
+  // the same run of positions.
+  const bool doc_lds = a.iv_kind == IV_DOCUMENT && a.n_docs + 1 <= (int)(sizeof(lds) / sizeof(int));
+  if (doc_lds) {
+    const int32_t* off = a.doc_offsets + (int64_t)b * (a.n_docs + 1);
+    for (int t = tid; t <= a.n_docs; t += C::NW * 64) ((int*)lds)[t] = off[t];
+    __syncthreads();
+  }
+  auto doc_ivl = [&](int x, int& lo, int& hi) {
+    doc_run((const int*)lds, a.n_docs, x, lo, hi);
+    lo = max(lo, 0);
+    hi = min(hi, (DQ ? a.sk : a.sq) - 1);
+  };
+
   const int64_t q_row_b = a.q_si * 2, k_row_b = a.k_si * 2;
 
   // ---- the wave's rows in registers: B operands, lane (c, g) holds
@@ -142,21 +159,23 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
     const int64_t li = b * a.lse_sb + hr * a.lse_sh + row;
     const float l = a.lse[0][li];
     lse2_row = l == kNegInf ? __builtin_inff() : l * kLog2e;  // no key: every p is 0
-    key_interval(a, b, row, lane_lo, lane_hi);
-  } else {
-    query_interval(a, b, row, lane_lo, lane_hi);
   }
+  if (doc_lds) doc_ivl(row, lane_lo, lane_hi);
+  else if constexpr (DQ) key_interval(a, b, row, lane_lo, lane_hi);
+  else query_interval(a, b, row, lane_lo, lane_hi);
 
   // streamed range of the work-group and of this wave (union over rows)
   int lo_first, hi_first, lo_last, hi_last, w_lo_min, w_hi_min, w_lo_max, w_hi_max;
   auto ivl = [&](int x, int& lo, int& hi) {
-    if constexpr (DQ) key_interval(a, b, x, lo, hi);
+    if (doc_lds) doc_ivl(x, lo, hi);
+    else if constexpr (DQ) key_interval(a, b, x, lo, hi);
     else query_interval(a, b, x, lo, hi);
   };
   ivl(r0, lo_first, hi_first);
   ivl(min(r0 + C::BM, n_rows) - 1, lo_last, hi_last);
   ivl(min(wr0, n_rows - 1), w_lo_min, w_hi_min);
   ivl(max(min(wr0 + 31, n_rows - 1), min(wr0, n_rows - 1)), w_lo_max, w_hi_max);
+  if (doc_lds) __syncthreads();  // the last read of the LDS offsets
   const int t_lo = lo_first / BN;
   const int t_hi = hi_last >= lo_first ? (hi_last + BN) / BN : t_lo;
   const int n_t = t_hi - t_lo;

@@ -271,20 +271,20 @@ __device__ __forceinline__ void unit_hint_fast() {
 // (work-group id = rank * H + head).  Every work-group ranks all items
 // itself in LDS: it needs no buffer and no second launch, and the keys
 // (span, index) are unique, so the ranks form a permutation whatever the
-// offsets hold.  `ws` needs room for kDocOrderMaxOffsets + 2 NT ints.
-// Returns false (the caller keeps the plain order) when the items outnumber
-// the work-group's NT threads or the offsets do not fit.
+// offsets hold.  `ws` holds the offsets of every batch entry (copied by
+// the caller) and room for 2 NT ints after kDocOrderMaxOffsets.  Returns
+// false (the caller keeps the plain order) when the items outnumber the
+// work-group's NT threads.  The caller synchronises before the LDS is
+// written again.
 constexpr int kDocOrderMaxOffsets = 1024;
 template <int NT, int BN>
 __device__ bool doc_order_tile(const KernelArgs& a, int bm, int* ws, int& bh, int& qt) {
-  const int n = a.nb * a.n_qt, n_off = a.nb * (a.n_docs + 1);
-  if (n > NT || n_off > kDocOrderMaxOffsets) return false;
+  const int n = a.nb * a.n_qt;
+  if (n > NT) return false;
   const int tid = threadIdx.x;
-  int* off = ws;
+  const int* off = ws;
   int* key = ws + kDocOrderMaxOffsets;
   int* perm = key + NT;
-  for (int t = tid; t < n_off; t += NT) off[t] = a.doc_offsets[t];
-  __syncthreads();
   if (tid < n) {
     const int b = tid / a.n_qt, t = tid % a.n_qt;
     const int* o = off + b * (a.n_docs + 1);
@@ -303,16 +303,25 @@ __device__ bool doc_order_tile(const KernelArgs& a, int bm, int* ws, int& bh, in
     const int span = lo <= hi ? hi / BN - lo / BN + 1 : 0;
     key[tid] = (min(span, 0x7fff) << 16) | (0xffff - tid);
   }
+  // pad the keys to a multiple of 4 with 0, below every real key (those
+  // hold 0xffff - tid > 0 in their low half)
+  const int n4 = (n + 3) & ~3;
+  if (tid >= n && tid < n4) key[tid] = 0;
   __syncthreads();
   if (tid < n) {
+    // rank = number of larger keys; the wave reads the same 16 bytes at
+    // once (a broadcast), eight reads in flight
     const int mine = key[tid];
     int rank = 0;
-    for (int j = 0; j < n; ++j) rank += key[j] > mine;
+#pragma unroll 8
+    for (int j = 0; j < n4; j += 4) {
+      const int4 kk = *(const int4*)(key + j);
+      rank += (kk.x > mine) + (kk.y > mine) + (kk.z > mine) + (kk.w > mine);
+    }
     perm[rank] = tid;
   }
   __syncthreads();
   const int item = perm[blockIdx.x / a.nh];
-  __syncthreads();  // the LDS holds K/V tiles next
   bh = (item / a.n_qt) * a.nh + blockIdx.x % a.nh;
   qt = item % a.n_qt;
   return true;
@@ -336,6 +345,7 @@ void attn_mfma_kernel(KernelArgs a) {
 
   int bh, qt, split = 0;
   int b_first = 0, n_rep = 1;  // batch entries this work-group walks
+  bool doc_lds = false;        // the document offsets sit in LDS (prologue only)
   if constexpr (C::DEC) {
     split = blockIdx.x % a.n_split;
     const int rest = blockIdx.x / a.n_split;
@@ -358,9 +368,19 @@ void attn_mfma_kernel(KernelArgs a) {
     n_rep = min(a.rows_per_wg, a.nb - b_first);
     bh = b_first * a.nh + hh;
   } else {
+    // Document mask: the offsets of every batch entry go to LDS once, where
+    // the work order and every key interval of the prologue search them
+    // (a search through global memory costs a round trip per step).  The
+    // K/V tiles overwrite them after the prologue's closing barrier.
     static_assert(sizeof(lds) >= (kDocOrderMaxOffsets + 2 * C::NW * 64) * sizeof(int),
                   "LDS for the document order");
-    if (!(a.doc_order && doc_order_tile<C::NW * 64, BN>(a, C::BM, (int*)lds, bh, qt)))
+    const int n_off = a.nb * (a.n_docs + 1);
+    doc_lds = a.iv_kind == IV_DOCUMENT && n_off <= kDocOrderMaxOffsets;
+    if (doc_lds) {
+      for (int t = tid; t < n_off; t += C::NW * 64) ((int*)lds)[t] = a.doc_offsets[t];
+      __syncthreads();
+    }
+    if (!(doc_lds && a.doc_order && doc_order_tile<C::NW * 64, BN>(a, C::BM, (int*)lds, bh, qt)))
       decode_tile(a, blockIdx.x, bh, qt);
   }
   int b = bh / a.nh;  // the batch entry whose rows are in flight
@@ -388,7 +408,13 @@ void attn_mfma_kernel(KernelArgs a) {
   };
   // key interval of the query at position x (only the first len keys exist)
   auto interval = [&](int x, int& lo, int& hi) {
-    key_interval(a, b, x, lo, hi);
+    if (doc_lds) {
+      doc_run((const int*)lds + b * (a.n_docs + 1), a.n_docs, x, lo, hi);
+      lo = max(lo, 0);
+      hi = min(hi, a.sk - 1);
+    } else {
+      key_interval(a, b, x, lo, hi);
+    }
     if constexpr (C::DEC) hi = min(hi, len - 1);
   };
 
@@ -444,6 +470,8 @@ void attn_mfma_kernel(KernelArgs a) {
       }
     }
   }
+  // the prologue's last read of the LDS offsets
+  if (doc_lds) __syncthreads();
 
   // ---- Q operands in registers ---------------------------------------------
   // B operand of S^T = K Q^T: lane (c, g) holds Q[row c][16t + 8g .. +7].

@@ -236,10 +236,13 @@ fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* b
   // Two 32-row blocks per wave halve the LDS operand traffic per product.
   // Dense rows take them when that still leaves two work-groups per compute
   // unit (ALiBi too: its two-block form spills a few registers, about one
-  // dword per lane per tile of extra traffic, and is still 8% faster).  Under a positional mask the taller tiles cross more partial key
-  // tiles and balance worse, so masked rows take them only when the grid is
-  // deep (eight work-groups per unit); a sliding window, whose rows see few
-  // keys, never does.
+  // dword per lane per tile of extra traffic, and is still 8% faster).
+  // Under a positional mask the taller tiles cross more partial key tiles
+  // and balance worse: causal and PrefixLM rows take them from four
+  // work-groups per unit (3% faster at B4 H16 S4096), document rows from
+  // eight (at four they are 7% slower: short documents leave the taller
+  // tiles mostly masked), and a sliding window, whose rows see few keys,
+  // never does.
   const int64_t wg2 = (int64_t)grid_qtiles(S_q, attn_rows_per_wg(2)) * B * H_q;
 #ifdef FL_FORCE_QB
   const int qb = FL_FORCE_QB;
@@ -251,8 +254,10 @@ fl_status fl_attn_fwd(const void* q, const void* k, const void* v, const void* b
     qb = wg2 >= 512 ? 2 : 1;
   else if (a.iv_kind == IV_WINDOW_CAUSAL || a.iv_kind == IV_WINDOW_TWO_SIDED)
     qb = 1;
-  else
+  else if (a.iv_kind == IV_DOCUMENT)
     qb = wg2 >= 2048 ? 2 : 1;
+  else
+    qb = wg2 >= 1024 ? 2 : 1;
 #endif
   a.n_qt = grid_qtiles(S_q, attn_rows_per_wg(qb));
   if ((int64_t)a.n_qt * B * H_q > kMaxGrid) return FL_ERR_SHAPE;

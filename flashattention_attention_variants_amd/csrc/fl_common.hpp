@@ -98,6 +98,21 @@ struct BwdArgs {
   float* delta;  // [B, H_q, S_q]: written by the dQ launch, read by the dK, dV launch
 };
 
+// Document mask: the document holding row i (the largest d < n_docs with
+// off[d] <= i, by binary search over the n_docs + 1 offsets of one batch
+// entry) and its run of keys [off[d], off[d+1] - 1], unclamped.  `off`
+// points at global memory or at an LDS copy.
+template <class P>
+__device__ __forceinline__ void doc_run(P off, int n_docs, int i, int& lo, int& hi) {
+  int dlo = 0, dhi = n_docs - 1;
+  while (dlo < dhi) {
+    const int mid = (dlo + dhi + 1) >> 1;
+    if (off[mid] <= i) dlo = mid; else dhi = mid - 1;
+  }
+  lo = off[dlo];
+  hi = off[dlo + 1] - 1;
+}
+
 // Key interval [lo, hi] of query i, clamped to [0, S_k-1] (empty: lo > hi).
 __device__ __forceinline__ void key_interval(const KernelArgs& a, int b, int i, int& lo,
                                              int& hi) {
@@ -118,18 +133,9 @@ __device__ __forceinline__ void key_interval(const KernelArgs& a, int b, int i, 
       lo = 0;
       hi = i > a.prefix - 1 ? i : a.prefix - 1;
       break;
-    case IV_DOCUMENT: {
-      // largest d with off[d] <= i (binary search over n_docs+1 offsets)
-      const int32_t* off = a.doc_offsets + (int64_t)b * (a.n_docs + 1);
-      int dlo = 0, dhi = a.n_docs - 1;
-      while (dlo < dhi) {
-        const int mid = (dlo + dhi + 1) >> 1;
-        if (off[mid] <= i) dlo = mid; else dhi = mid - 1;
-      }
-      lo = off[dlo];
-      hi = off[dlo + 1] - 1;
+    case IV_DOCUMENT:
+      doc_run(a.doc_offsets + (int64_t)b * (a.n_docs + 1), a.n_docs, i, lo, hi);
       break;
-    }
     default:
       lo = 0;
       hi = a.sk - 1;
@@ -161,17 +167,9 @@ __device__ __forceinline__ void query_interval(const KernelArgs& a, int b, int j
       lo = j < a.prefix ? 0 : j;
       hi = a.sq - 1;
       break;
-    case IV_DOCUMENT: {
-      const int32_t* off = a.doc_offsets + (int64_t)b * (a.n_docs + 1);
-      int dlo = 0, dhi = a.n_docs - 1;
-      while (dlo < dhi) {
-        const int mid = (dlo + dhi + 1) >> 1;
-        if (off[mid] <= j) dlo = mid; else dhi = mid - 1;
-      }
-      lo = off[dlo];
-      hi = off[dlo + 1] - 1;
+    case IV_DOCUMENT:
+      doc_run(a.doc_offsets + (int64_t)b * (a.n_docs + 1), a.n_docs, j, lo, hi);
       break;
-    }
     default:
       lo = 0;
       hi = a.sq - 1;

@@ -4,11 +4,12 @@ zero scales.
 The launcher gives each wave two 32-row query blocks (256-row work-groups)
 when the grid of 256-row work-groups is deep enough: at least 512 of them
 for rows that see every key (vanilla, ALiBi, softcap, with or without a
-bias; ALiBi with a bias keeps one block), at least 2048 under a causal,
-PrefixLM or document mask; a sliding window always keeps one.  The shapes
-below pass those thresholds, so every two-block instance the launcher can
-choose runs here, with ragged tails (S % 64 != 0 and rows past S_q inside
-the last 256-row tile), on sampled rows against the float64 oracle:
+bias; ALiBi with a bias keeps one block), at least 1024 under a causal or
+PrefixLM mask, at least 2048 under a document mask; a sliding window always
+keeps one.  The shapes below pass those thresholds, so every two-block
+instance the launcher can choose runs here, with ragged tails (S % 64 != 0
+and rows past S_q inside the last 256-row tile), on sampled rows against
+the float64 oracle:
 
 * dense, no bias, B4 H32 S1000 (512 work-groups): plain scores, ALiBi, the
   bounded softcap (cap 50) and the softcap with a running reference (cap 80);
@@ -17,7 +18,10 @@ the last 256-row tile), on sampled rows against the float64 oracle:
 * masked, B1 H128 S4000 (2048): causal, PrefixLM, document, and ALiBi,
   softcap (both caps) composed with them;
 * masked with a bias, B64 H4 S2000 (2048): causal, document and
-  softcap + causal.
+  softcap + causal;
+* masked at the causal threshold, B2 H32 S4000 (1024): causal, PrefixLM,
+  ALiBi + causal, softcap + PrefixLM at two blocks, and the document mask,
+  which keeps one block there.
 
 Row sampling takes random rows plus the first and last rows of a few heads
 and the rows on both sides of each 64, 128, 256, 512 and 768-row boundary.
@@ -45,10 +49,10 @@ def _setup():
     api.load_library()
 
 
-def two_block_grid(B, H, S, masked):
+def two_block_grid(B, H, S, masked, document=False):
     """The launcher's depth rule for two query blocks per wave."""
     wg2 = B * H * ((S + 255) // 256)
-    return wg2 >= (2048 if masked else 512)
+    return wg2 >= (512 if not masked else 2048 if document else 1024)
 
 
 def compare_rows(q, k, v, kw, rows, what, bias=None, lse_scale=False):
@@ -115,7 +119,7 @@ MASKED = [
                               "softcap+document", "softcap80+causal"])
 def test_two_blocks_masked_deep(variant, mask, extra):
     B, H, S = 1, 128, 4000
-    assert two_block_grid(B, H, S, masked=True)
+    assert two_block_grid(B, H, S, masked=True, document="document" in (variant, mask))
     q, k, v = inputs.attn_inputs(B, H, H, S, S, 64, "bf16", seed=920)
     kw = dict(variant=variant, **extra)
     if mask is not None:
@@ -131,7 +135,7 @@ def test_two_blocks_masked_deep(variant, mask, extra):
                          ids=["causal", "document", "softcap+causal"])
 def test_two_blocks_masked_bias(variant, mask, extra):
     B, H, S = 64, 4, 2000
-    assert two_block_grid(B, H, S, masked=True)
+    assert two_block_grid(B, H, S, masked=True, document=variant == "document")
     q, k, v = inputs.attn_inputs(B, H, H, S, S, 64, "bf16", seed=930)
     bias = inputs.bias_inputs(H, S, S, "bf16", seed=931)
     kw = dict(variant=variant, **extra)
@@ -141,6 +145,29 @@ def test_two_blocks_masked_bias(variant, mask, extra):
         kw["doc_offsets"] = inputs.doc_offsets(B, S, 8, seed=932)
     rows = sample_rows(B, H, S, 384, seed=933, extra_tiles=TILES)
     compare_rows(q, k, v, kw, rows, "%s+%s QB2 masked bias" % (variant, mask), bias=bias)
+
+
+MID = [("causal", None, {}), ("prefix_lm", None, dict(prefix=512)),
+       ("alibi", "causal", dict(alibi_max_bias=8.0)), ("softcap", "prefix_lm", dict(softcap=50.0, prefix=777)),
+       ("document", None, {})]
+
+
+@pytest.mark.parametrize("variant,mask,extra", MID,
+                         ids=["causal", "prefix", "alibi+causal", "softcap+prefix", "document"])
+def test_two_blocks_masked_threshold(variant, mask, extra):
+    """1024 two-block work-groups: causal and PrefixLM rows take two blocks,
+    document rows one."""
+    B, H, S = 2, 32, 4000
+    doc = "document" in (variant, mask)
+    assert two_block_grid(B, H, S, masked=True) and not two_block_grid(B, H, S, True, document=True)
+    q, k, v = inputs.attn_inputs(B, H, H, S, S, 64, "bf16", seed=940)
+    kw = dict(variant=variant, **extra)
+    if mask is not None:
+        kw["mask"] = mask
+    if doc:
+        kw["doc_offsets"] = inputs.doc_offsets(B, S, 8, seed=941)
+    rows = sample_rows(B, H, S, 384, seed=942, extra_tiles=TILES)
+    compare_rows(q, k, v, kw, rows, "%s+%s at the causal threshold" % (variant, mask))
 
 
 # ---------------------------------------------------------------------------
