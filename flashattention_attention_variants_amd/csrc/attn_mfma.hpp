@@ -383,6 +383,9 @@ void attn_mfma_kernel(KernelArgs a) {
     if (!(doc_lds && a.doc_order && doc_order_tile<C::NW * 64, BN>(a, C::BM, (int*)lds, bh, qt)))
       decode_tile(a, blockIdx.x, bh, qt);
   }
+  // (the work order read from LDS is uniform too)
+  bh = __builtin_amdgcn_readfirstlane(bh);
+  qt = __builtin_amdgcn_readfirstlane(qt);
   int b = bh / a.nh;  // the batch entry whose rows are in flight
   const int h = bh % a.nh, hk = h / a.group;
   const int q0 = qt * C::BM;
@@ -447,32 +450,6 @@ void attn_mfma_kernel(KernelArgs a) {
   interval(wp_max, w_lo_max, w_hi_max);
   const bool wave_idle = wq0 >= a.sq;
 
-  int row_lo[QB], row_hi[QB];
-  // positions of this lane's row and of the first and last row of each
-  // 32-row block (the block's place against the diagonal)
-  int lane_pos[QB], blk_pmin[QB], blk_pmax[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qi = min(wq0 + 32 * qb + c, a.sq - 1);  // rows past S_q copy the last row
-    interval(pos_of(qi), row_lo[qb], row_hi[qb]);
-    if constexpr (C::DEC) {
-      lane_pos[qb] = pos_of(qi);
-      const int r0 = min(wq0 + 32 * qb, a.sq - 1);
-      pos_range(r0, max(min(wq0 + 32 * qb + 31, a.sq - 1), r0), blk_pmin[qb], blk_pmax[qb]);
-    } else {
-      lane_pos[qb] = wq0 + 32 * qb + c;
-      blk_pmin[qb] = wq0 + 32 * qb;
-      blk_pmax[qb] = wq0 + 32 * qb + 31;
-      if constexpr (C::ALIBI_FOLD) {
-        // wave-uniform: the per-unit diagonal tests become scalar compares
-        blk_pmin[qb] = __builtin_amdgcn_readfirstlane(blk_pmin[qb]);
-        blk_pmax[qb] = __builtin_amdgcn_readfirstlane(blk_pmax[qb]);
-      }
-    }
-  }
-  // the prologue's last read of the LDS offsets
-  if (doc_lds) __syncthreads();
-
   // ---- Q operands in registers ---------------------------------------------
   // B operand of S^T = K Q^T: lane (c, g) holds Q[row c][16t + 8g .. +7].
   // Folded scores: Q is multiplied by the signed power-of-two part of
@@ -524,6 +501,138 @@ void attn_mfma_kernel(KernelArgs a) {
     }
   };
   load_q(b);
+
+  // ---- global -> LDS tile movement ---------------------------------------------
+  // K and V tiles go from global memory straight into LDS (buffer loads with
+  // the LDS flag: no registers, no LDS store instructions), two tiles ahead of
+  // the one being consumed.  Each (b, K/V head) block is addressed through a
+  // bounds-checked buffer resource re-based at every tile, so keys past S_k
+  // read as zeros.  One load instruction of a wave fills 1 KiB of LDS in lane
+  // order, so the swizzled layout is realised by choosing, per lane, which
+  // global 16-byte chunk to fetch.
+  auto kblk = [&](int s, int bb) {
+    return (const char*)((const bf16*)a.k[s] + bb * a.k_sb + hk * a.k_sh);
+  };
+  auto vblk = [&](int bb) { return (const char*)((const bf16*)a.v + bb * a.v_sb + hk * a.v_sh); };
+  const int64_t k_row_b = a.k_si * 2, v_row_b = a.v_si * 2;
+  // (decode: only the first len rows exist; cache slots past them may hold
+  // anything, NaN included, and must not reach even a zero-weighted product)
+  const int64_t k_span = len > 0 ? (int64_t)(len - 1) * k_row_b + DQK * 2 : 0;
+  const int64_t v_span = len > 0 ? (int64_t)(len - 1) * v_row_b + DV * 2 : 0;
+
+  int k_off[C::KCH], v_off[C::VCH];
+#pragma unroll
+  for (int i = 0; i < C::KCH; ++i) {
+    const int q = (i * C::NW + w) * 64 + lane;  // 16-byte slot in the K tile
+    const int row = q / C::KCPR, phys = q % C::KCPR;
+    k_off[i] = row * (int)k_row_b + 16 * (phys ^ C::kswz(row));
+  }
+#pragma unroll
+  for (int i = 0; i < C::VCH; ++i) {
+    const int q = (i * C::NW + w) * 64 + lane;
+    const int row = q / C::VCPR, phys = q % C::VCPR;
+    v_off[i] = row * (int)v_row_b + 16 * (phys ^ C::vswz(row));
+  }
+  float kmpre = 0.0f;
+
+  // issue the loads of tile kt of batch entry bb into LDS stage `stage`
+  auto load_tile = [&](int bb, int kt, int stage) {
+    const int64_t j0 = (int64_t)kt * BN;
+    if (C::KMASK && tid < BN) {
+      const int j = (int)j0 + tid;
+      kmpre = (j < a.sk && (!a.kmask || a.kmask[bb * a.km_sb + (int64_t)j * a.km_sj] != 0))
+                  ? 0.0f
+                  : kNegInf;
+    }
+    bf16* ks = lds + stage * C::STAGE;
+    // one resource over the whole (b, K/V head) block; the tile's offset
+    // rides in the per-lane offset, which the launcher keeps below 2^31 for
+    // every row up to 63 past S_k
+    const int kt_off = (int)j0 * (int)k_row_b, vt_off = (int)j0 * (int)v_row_b;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(kblk(s, bb), k_span);
+#pragma unroll
+      for (int i = 0; i < C::KCH; ++i)
+        lds_load16(rs, ks + s * C::K_ELEMS + (i * C::NW + w) * 512, k_off[i] + kt_off);
+    }
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(vblk(bb), v_span);
+#pragma unroll
+    for (int i = 0; i < C::VCH; ++i)
+      lds_load16(rs, ks + NS * C::K_ELEMS + (i * C::NW + w) * 512, v_off[i] + vt_off);
+  };
+  // the key-mask column of a tile travels through a register
+  auto store_kmask = [&](int stage) {
+    if (C::KMASK && tid < BN) kmadd[stage * BN + tid] = kmpre;
+  };
+
+  constexpr int LOADS = NS * C::KCH + C::VCH;  // LDS-bound loads per thread per tile
+  constexpr int AHEAD = C::STAGES - 1;          // tiles issued ahead of the one consumed
+  // Tile order: ascending keys, except under ALiBi, where the visit starts
+  // at the work-group's diagonal tile and wraps round.  The scores of a row
+  // peak near its diagonal, so the running reference is set there first
+  // instead of climbing (and being moved) tile after tile.
+  const int n_kt = kt_hi - kt_lo;
+  int kt_start = 0;
+  if constexpr (C::MOD == MOD_ALIBI) kt_start = min(max(p_first / BN - kt_lo, 0), max(n_kt - 1, 0));
+  auto tile_of = [&](int it) {
+    const int x = it + kt_start;
+    return kt_lo + (x >= n_kt ? x - n_kt : x);
+  };
+  // the visit: n_kt tiles of each of the n_rep batch entries, in sequence
+  const int n_total = n_rep * n_kt;
+  auto issue = [&](int it, int stage) {
+    if constexpr (C::PERSIST)
+      load_tile(b_first + it / n_kt, tile_of(it % n_kt), stage);
+    else
+      load_tile(b, tile_of(it), stage);
+  };
+  // The softcap pass runs against the reference c = cap log2(e): it is
+  // tried for c <= 76, where rows of scores near 0 end far above its bound.
+  const bool fast_try = !C::SCAPB || a.softcap_log2 <= 76.0f;
+
+  // Folded first pass: Q and the first tiles go out as soon as the
+  // work-group's key range is known, so that their latency runs under the
+  // rest of the set-up.  (Under a document mask the offsets hold the LDS
+  // until the set-up ends; its tiles go out after it.)
+  bool pre_issued = false;
+  if constexpr (C::FASTP) {
+    if (fast_try && !doc_lds && n_total > 0) {
+      issue(0, 0);
+#pragma unroll
+      for (int t = 1; t < AHEAD; ++t)
+        if (t < n_total) issue(t, t);
+      pre_issued = true;
+    }
+  }
+
+  int row_lo[QB], row_hi[QB];
+  // positions of this lane's row and of the first and last row of each
+  // 32-row block (the block's place against the diagonal)
+  int lane_pos[QB], blk_pmin[QB], blk_pmax[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = min(wq0 + 32 * qb + c, a.sq - 1);  // rows past S_q copy the last row
+    interval(pos_of(qi), row_lo[qb], row_hi[qb]);
+    if constexpr (C::DEC) {
+      lane_pos[qb] = pos_of(qi);
+      const int r0 = min(wq0 + 32 * qb, a.sq - 1);
+      pos_range(r0, max(min(wq0 + 32 * qb + 31, a.sq - 1), r0), blk_pmin[qb], blk_pmax[qb]);
+    } else {
+      lane_pos[qb] = wq0 + 32 * qb + c;
+      blk_pmin[qb] = wq0 + 32 * qb;
+      blk_pmax[qb] = wq0 + 32 * qb + 31;
+      if constexpr (C::ALIBI_FOLD) {
+        // wave-uniform: the per-unit diagonal tests become scalar compares
+        blk_pmin[qb] = __builtin_amdgcn_readfirstlane(blk_pmin[qb]);
+        blk_pmax[qb] = __builtin_amdgcn_readfirstlane(blk_pmax[qb]);
+      }
+    }
+  }
+  // the prologue's last read of the LDS offsets
+  if (doc_lds) __syncthreads();
+
+
 
   // Gate rows of entry bb (rows q0.., DV values each) into gate buffer
   // `buf`, straight from global memory; rows past S_q read as zeros.  They
@@ -656,69 +765,6 @@ void attn_mfma_kernel(KernelArgs a) {
   // denominator share the reference.
   const float thr = 8.0f;
 
-  // ---- global -> LDS tile movement ---------------------------------------------
-  // K and V tiles go from global memory straight into LDS (buffer loads with
-  // the LDS flag: no registers, no LDS store instructions), two tiles ahead of
-  // the one being consumed.  Each (b, K/V head) block is addressed through a
-  // bounds-checked buffer resource re-based at every tile, so keys past S_k
-  // read as zeros.  One load instruction of a wave fills 1 KiB of LDS in lane
-  // order, so the swizzled layout is realised by choosing, per lane, which
-  // global 16-byte chunk to fetch.
-  auto kblk = [&](int s, int bb) {
-    return (const char*)((const bf16*)a.k[s] + bb * a.k_sb + hk * a.k_sh);
-  };
-  auto vblk = [&](int bb) { return (const char*)((const bf16*)a.v + bb * a.v_sb + hk * a.v_sh); };
-  const int64_t k_row_b = a.k_si * 2, v_row_b = a.v_si * 2;
-  // (decode: only the first len rows exist; cache slots past them may hold
-  // anything, NaN included, and must not reach even a zero-weighted product)
-  const int64_t k_span = len > 0 ? (int64_t)(len - 1) * k_row_b + DQK * 2 : 0;
-  const int64_t v_span = len > 0 ? (int64_t)(len - 1) * v_row_b + DV * 2 : 0;
-
-  int k_off[C::KCH], v_off[C::VCH];
-#pragma unroll
-  for (int i = 0; i < C::KCH; ++i) {
-    const int q = (i * C::NW + w) * 64 + lane;  // 16-byte slot in the K tile
-    const int row = q / C::KCPR, phys = q % C::KCPR;
-    k_off[i] = row * (int)k_row_b + 16 * (phys ^ C::kswz(row));
-  }
-#pragma unroll
-  for (int i = 0; i < C::VCH; ++i) {
-    const int q = (i * C::NW + w) * 64 + lane;
-    const int row = q / C::VCPR, phys = q % C::VCPR;
-    v_off[i] = row * (int)v_row_b + 16 * (phys ^ C::vswz(row));
-  }
-  float kmpre = 0.0f;
-
-  // issue the loads of tile kt of batch entry bb into LDS stage `stage`
-  auto load_tile = [&](int bb, int kt, int stage) {
-    const int64_t j0 = (int64_t)kt * BN;
-    if (C::KMASK && tid < BN) {
-      const int j = (int)j0 + tid;
-      kmpre = (j < a.sk && (!a.kmask || a.kmask[bb * a.km_sb + (int64_t)j * a.km_sj] != 0))
-                  ? 0.0f
-                  : kNegInf;
-    }
-    bf16* ks = lds + stage * C::STAGE;
-    // one resource over the whole (b, K/V head) block; the tile's offset
-    // rides in the per-lane offset, which the launcher keeps below 2^31 for
-    // every row up to 63 past S_k
-    const int kt_off = (int)j0 * (int)k_row_b, vt_off = (int)j0 * (int)v_row_b;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(kblk(s, bb), k_span);
-#pragma unroll
-      for (int i = 0; i < C::KCH; ++i)
-        lds_load16(rs, ks + s * C::K_ELEMS + (i * C::NW + w) * 512, k_off[i] + kt_off);
-    }
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(vblk(bb), v_span);
-#pragma unroll
-    for (int i = 0; i < C::VCH; ++i)
-      lds_load16(rs, ks + NS * C::K_ELEMS + (i * C::NW + w) * 512, v_off[i] + vt_off);
-  };
-  // the key-mask column of a tile travels through a register
-  auto store_kmask = [&](int stage) {
-    if (C::KMASK && tid < BN) kmadd[stage * BN + tid] = kmpre;
-  };
 
   // LDS element offsets of this lane's operand reads.  K: row 32kb + c,
   // logical 16-byte chunk 2t + g.
@@ -1077,8 +1123,6 @@ void attn_mfma_kernel(KernelArgs a) {
   // goes into the stage freed at the end of the previous iteration.  The
   // barrier at the end of an iteration both publishes the next tile (every
   // wave waited for its own loads) and frees the current stage.
-  constexpr int LOADS = NS * C::KCH + C::VCH;  // LDS-bound loads per thread per tile
-  constexpr int AHEAD = C::STAGES - 1;          // tiles issued ahead of the one consumed
   static_assert((AHEAD - 1) * LOADS < 64, "vmcnt range");
   // Publish a landed tile: wait for this wave's loads of it (leaving the
   // `newer` tiles issued after it in flight) and its LDS stores, then the
@@ -1109,17 +1153,6 @@ void attn_mfma_kernel(KernelArgs a) {
       return;
     }
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  };
-  // Tile order: ascending keys, except under ALiBi, where the visit starts
-  // at the work-group's diagonal tile and wraps round.  The scores of a row
-  // peak near its diagonal, so the running reference is set there first
-  // instead of climbing (and being moved) tile after tile.
-  const int n_kt = kt_hi - kt_lo;
-  int kt_start = 0;
-  if constexpr (C::MOD == MOD_ALIBI) kt_start = min(max(p_first / BN - kt_lo, 0), max(n_kt - 1, 0));
-  auto tile_of = [&](int it) {
-    const int x = it + kt_start;
-    return kt_lo + (x >= n_kt ? x - n_kt : x);
   };
   // normalise, combine, gate and store the rows of batch entry b
   // the full row sum of this lane's row (both lane halves)
@@ -1234,26 +1267,17 @@ void attn_mfma_kernel(KernelArgs a) {
         }
     }
   };
-  // the visit: n_kt tiles of each of the n_rep batch entries, in sequence
-  const int n_total = n_rep * n_kt;
-  auto issue = [&](int it, int stage) {
-    if constexpr (C::PERSIST)
-      load_tile(b_first + it / n_kt, tile_of(it % n_kt), stage);
-    else
-      load_tile(b, tile_of(it), stage);
-  };
-  // The softcap pass runs against the reference c = cap log2(e): it is
-  // tried for c <= 76, where rows of scores near 0 end far above its bound.
-  const bool fast_try = !C::SCAPB || a.softcap_log2 <= 76.0f;
   if constexpr (C::FASTP) if (fast_try) {
     using F = std::integral_constant<bool, false>;
     using T = std::integral_constant<bool, true>;
     using FD = std::integral_constant<bool, C::ALIBI_FOLD>;  // the penalty rides on the fold
     if (n_total > 0) {
-      issue(0, 0);
+      if (!pre_issued) {
+        issue(0, 0);
 #pragma unroll
-      for (int t = 1; t < AHEAD; ++t)
-        if (t < n_total) issue(t, t);
+        for (int t = 1; t < AHEAD; ++t)
+          if (t < n_total) issue(t, t);
+      }
       sync_tile(min(AHEAD, n_total) - 1);
     }
     for (int it = 0; it < n_total; ++it) {
