@@ -500,6 +500,25 @@ def test_evoformer_col(dtype, N_seq):
     assert (np64(o)[:, 3] == 0).all()
 
 
+@pytest.mark.parametrize("axis,n", [("row", 72), ("row", 200), ("col", 40), ("col", 129)])
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_evoformer_no_key_mask(axis, n, with_bias):
+    """No key mask: every key below the length counts (the instances without
+    a mask, with ragged key tiles, one and two query blocks per wave)."""
+    if axis == "col" and with_bias:
+        pytest.skip("the column form takes no pair bias")
+    q, k, v, gate, bias, _ = evo_small("bf16", N_seq=n if axis == "col" else 5,
+                                       N_res=n if axis == "row" else 24, seed=85)
+    pb = bias if with_bias else None
+    o = api.fl_evoformer_gated_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), gate.to(DEV),
+                                        pair_bias=None if pb is None else pb.to(DEV),
+                                        key_mask=None, axis=axis)
+    torch.cuda.synchronize()
+    ro = oracle.evoformer(np64(q), np64(k), np64(v), np64(gate),
+                          pair_bias=None if pb is None else np64(pb), key_mask=None, axis=axis)
+    check(np64(o), ro, "bf16", "evoformer %s without a key mask" % axis)
+
+
 # ---------------------------------------------------------------------------
 # a score modification composed with a mask
 
