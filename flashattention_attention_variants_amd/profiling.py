@@ -202,8 +202,9 @@ def decode_stats_markdown(dirname: str, bench_json: str) -> str:
     d = b["decode"]
     out = ["# attn_mfma_kernel (decode form) and merge_kernel -- %s" % d["workload"], "",
            "Kernel trace of the default bench command, which times each decode variant after the "
-           "step (a settle, then three batches of back-to-back calls; one call = the decode kernel "
-           "plus the merge kernel), one MI355X.", "", CMD_VARS, "",
+           "step (per-call HIP events; cold: a 1 GiB buffer read before each call, outside the "
+           "events; warm: back-to-back calls; one call = the decode kernel plus the merge "
+           "kernel), one MI355X.", "", CMD_VARS, "",
            "```",
            "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/kt -o run "
            "-- python3 $REPO/bench.py",
@@ -214,12 +215,15 @@ def decode_stats_markdown(dirname: str, bench_json: str) -> str:
            "Kernel names: `MfmaCfg<64, 64, 1, 1, MOD, false, false, false, true>` is the decode form "
            "with MOD 0 = none (causal, window), 1 = ALiBi, 3 = bounded softcap; `merge_kernel<bf16>` "
            "recombines the key ranges.", "",
-           "Bench line of the same build (per call, decode + merge):", "",
-           "| variant | ms / call | GB/s (algorithmic) | % of 8 TB/s | algorithmic MB |",
-           "|---|---:|---:|---:|---:|"]
+           "Bench line of the same build (per call, decode + merge; medians; GB/s and the "
+           "fraction from the cold median):", "",
+           "| variant | cold ms / call | warm ms / call | GB/s (algorithmic) | % of 8 TB/s | "
+           "algorithmic MB |",
+           "|---|---:|---:|---:|---:|---:|"]
     for k, v in d["per_variant"].items():
-        out.append("| %s | %.4f | %.1f | %.1f | %.1f |" % (
-            k, v["ms"], v["gbs"], 100 * v["frac_hbm"], v["algorithmic_bytes"] / 1e6))
+        warm = v.get("warm", {}).get("ms_median", float("nan"))
+        out.append("| %s | %.4f | %.4f | %.1f | %.1f | %.1f |" % (
+            k, v["ms_median"], warm, v["gbs"], 100 * v["frac_hbm"], v["algorithmic_bytes"] / 1e6))
     out.append("")
     return "\n".join(out)
 
@@ -230,7 +234,7 @@ def bwd_stats_markdown(dirname: str, bench_json: str, workload: str) -> str:
     b = json.load(open(bench_json))
     out = ["# attn_bwd_kernel -- %s, all variants" % workload, "",
            "Kernel trace of the default bench command, which times the backward of each variant "
-           "after the step (a settle, then three batches of back-to-back calls; one call = the dQ "
+           "after the step (per-call HIP events over back-to-back calls; one call = the dQ "
            "launch plus the dK, dV launch), one MI355X.", "", CMD_VARS, "",
            "```",
            "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/kt -o run "
@@ -242,11 +246,13 @@ def bwd_stats_markdown(dirname: str, bench_json: str, workload: str) -> str:
            "Kernel names: `BwdCfg<role, MOD>` with role 0 = dQ (rows are queries, K and V "
            "streamed), 1 = dK, dV (rows are keys, Q and dO of every query head of the group "
            "streamed); MOD 0 = none, 1 = ALiBi, 2 = softcap.  One instance serves every mask.", "",
-           "Bench line of the same build (per call, both launches; useful FLOPs = 2.5 x the "
-           "forward's):", "",
-           "| variant | ms / call | useful TFLOP/s | % of bf16 peak |", "|---|---:|---:|---:|"]
+           "Bench line of the same build (per call, both launches; median and min; useful FLOPs "
+           "= 2.5 x the forward's, TFLOP/s from the median):", "",
+           "| variant | ms / call (median) | ms (min) | useful TFLOP/s | % of bf16 peak |",
+           "|---|---:|---:|---:|---:|"]
     for k, v in b["backward"]["per_variant"].items():
-        out.append("| %s | %.4f | %.1f | %.1f |" % (k, v["ms"], v["tflops"], 100 * v["frac_bf16_peak"]))
+        out.append("| %s | %.4f | %.4f | %.1f | %.1f |" % (k, v["ms_median"], v["ms_min"], v["tflops"],
+                                                          100 * v["frac_bf16_peak"]))
     out.append("")
     return "\n".join(out)
 
