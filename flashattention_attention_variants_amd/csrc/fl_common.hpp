@@ -241,4 +241,44 @@ __device__ __forceinline__ float softcap_log2(const KernelArgs& a, float raw) {
 
 __device__ __forceinline__ float bf16_to_f32(bf16 x) { return (float)x; }
 
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds + 16*l (lds is wave-uniform).  Issued from assembly: the compiler's
+// wait-count pass cannot tell which LDS bytes such a load writes, and would
+// make every later LDS read wait for all tiles still in flight (the next
+// tiles' loads included), which serialises the tile pipeline.  The pipeline
+// waits for these loads itself (s_waitcnt vmcnt before the barrier that
+// publishes a tile).  The load writes no register; M0, which carries the LDS
+// address, is restored before the statement ends.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, void* lds, int byte_off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(byte_off), "s"(rs));
+#else
+  (void)rs;
+  (void)lds;
+  (void)byte_off;
+#endif
+}
+
+// Buffer resource over [base, base + bytes); 0x00020000 is the raw 32-bit
+// data-format word of gfx9 buffer descriptors.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
 }  // namespace fl

@@ -150,26 +150,19 @@ __global__ __launch_bounds__(256) void ipa_kernel(IpaArgs a) {
   for (int r = 0; r < (K::NBW > 0 ? K::NBW : 1); ++r) acc_z[r] = f32x4{};
 
   // z_i tile -> LDS, straight from global memory (bytes past the last key
-  // read as zeros through the bounds-checked resource)
+  // read as zeros through the bounds-checked resource).  Issued from
+  // assembly (lds_load16), so that the compiler does not make the pair
+  // product's LDS reads wait for the next tile's z in flight; the tile
+  // barrier waits for it.
   const bf16* zrow = CZ > 0 ? a.z + (int64_t)res * L * CZ : nullptr;
   auto issue_z = [&](int kt, int buf) {
     if constexpr (CZ > 0) {
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(zrow), 0, L * CZ * 2, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(zrow, (int64_t)L * CZ * 2);
       constexpr int CHUNKS = BN * CZ / 8;  // 16-byte chunks of a tile
 #pragma unroll
       for (int c0 = 0; c0 < CHUNKS; c0 += 256) {
         const int chunk = c0 + w * 64 + lane;  // wave-uniform LDS base, lanes in order
-#if defined(__HIP_DEVICE_COMPILE__)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (__attribute__((address_space(3))) void*)(zs + buf * BN * CZ + (c0 + w * 64) * 8), 16,
-            kt * BN * CZ * 2 + chunk * 16, 0, 0, 0);
-#else
-        (void)rs;
-        (void)chunk;
-        (void)buf;
-        (void)kt;
-#endif
+        lds_load16(rs, zs + buf * BN * CZ + (c0 + w * 64) * 8, kt * BN * CZ * 2 + chunk * 16);
       }
     }
   };
@@ -178,14 +171,19 @@ __global__ __launch_bounds__(256) void ipa_kernel(IpaArgs a) {
   if (n_kt > 0) issue_z(0, 0);
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
+    // Every lane loads its key's data unconditionally (keys past L and idle
+    // waves read a valid key's bytes), so that all loads of a tile go out
+    // together instead of behind the key-mask load; the mask and the bounds
+    // enter as a select on the logit.
     const int j = kt * BN + lane;
+    const int jj = min(j, L - 1);
     bool valid = active && j < L;
-    if (valid && a.kmask) valid = a.kmask[(int64_t)b * L + j] != 0;
-    float s = kNegInf;
+    if (a.kmask) valid = valid && a.kmask[(int64_t)b * L + jj] != 0;
+    float s;
     float vv[C], vg[PV][3];
-    if (valid) {
-      const int64_t kres = (int64_t)b * L + j;
-      const int64_t krow = kres * H + h;
+    {
+      const int64_t kres = (int64_t)b * L + jj;
+      const int64_t krow = kres * H + hh;
       const float* Rj = a.rot + kres * 9;
       const float* tj = a.trans + kres * 3;
       float R[9], tt[3];
@@ -229,7 +227,7 @@ __global__ __launch_bounds__(256) void ipa_kernel(IpaArgs a) {
           }
       }
       s = dot - wpt * d2;
-      if (a.bias) s = fmaf(a.w_bias, (float)a.bias[(((int64_t)b * H + h) * L + i) * L + j], s);
+      if (a.bias) s = fmaf(a.w_bias, (float)a.bias[(((int64_t)b * H + hh) * L + i) * L + jj], s);
       // value points in the global frame
       {
         const f32x4* vp4 = (const f32x4*)(a.v_pts + krow * PV * 3);
@@ -246,12 +244,15 @@ __global__ __launch_bounds__(256) void ipa_kernel(IpaArgs a) {
           for (int r = 0; r < 3; ++r)
             vg[p][r] = fmaf(R[3 * r], vl[3 * p], fmaf(R[3 * r + 1], vl[3 * p + 1], fmaf(R[3 * r + 2], vl[3 * p + 2], tt[r])));
       }
-    } else {
-#pragma unroll
-      for (int c = 0; c < C; ++c) vv[c] = 0.0f;
-#pragma unroll
-      for (int p = 0; p < PV; ++p) vg[p][0] = vg[p][1] = vg[p][2] = 0.0f;
     }
+    // a key outside the mask may hold anything: nothing of it reaches a sum
+    s = valid ? s : kNegInf;
+#pragma unroll
+    for (int c = 0; c < C; ++c) vv[c] = valid ? vv[c] : 0.0f;
+#pragma unroll
+    for (int p = 0; p < PV; ++p)
+#pragma unroll
+      for (int r = 0; r < 3; ++r) vg[p][r] = valid ? vg[p][r] : 0.0f;
     // online softmax: the head's maximum moves, partial sums rescale
     const float m_new = fmaxf(m_run, wave_max(s));
     const float alpha = m_new == kNegInf ? 1.0f : fast_exp2(m_run - m_new);
