@@ -29,6 +29,8 @@
 // transposed LDS reads, with the tile's weights (rounded to bf16) as A.
 #pragma once
 
+#include <type_traits>
+
 #include "fl_common.hpp"
 
 namespace fl {
@@ -61,16 +63,33 @@ struct IpaCfg {
   static_assert(C % 8 == 0 && CZ % 16 == 0 && (PQ * 3) % 4 == 0 && (PV * 3) % 4 == 0, "ipa sizes");
 };
 
-// wave-wide butterfly sum / max: every lane ends with the total
+// Wave-wide sum / max, every lane ending with the total: within rows of 16
+// lanes by DPP (swaps of neighbours and pairs, then the half-row and row
+// mirrors), then the four row results read into scalar registers and
+// combined in one order for every lane.  Vector-ALU and scalar reads only:
+// the LDS permute behind a generic shuffle costs an LDS round trip per step.
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float x, Op op) {
+  auto dpp = [](float v, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 decltype(ctrl)::value, 0xf, 0xf, false));
+  };
+  x = op(x, dpp(x, std::integral_constant<int, 0xb1>{}));   // quad_perm [1,0,3,2]
+  x = op(x, dpp(x, std::integral_constant<int, 0x4e>{}));   // quad_perm [2,3,0,1]
+  x = op(x, dpp(x, std::integral_constant<int, 0x141>{}));  // row_half_mirror
+  x = op(x, dpp(x, std::integral_constant<int, 0x140>{}));  // row_mirror
+  const int xi = __builtin_bit_cast(int, x);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
+  return op(op(r0, r1), op(r2, r3));
+}
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  return wave_reduce(x, [](float u, float v) { return u + v; });
 }
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  return wave_reduce(x, [](float u, float v) { return fmaxf(u, v); });
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
