@@ -317,14 +317,29 @@ void attn_mfma_kernel(KernelArgs a) {
     // XCD, whose L2 then serves each 128-byte line to both of its heads.
     const int n_grp = (a.nb + a.rows_per_wg - 1) / a.rows_per_wg;
     int item = blockIdx.x;  // (row group, query tile, head), head fastest
-    if ((n_grp & 7) == 0) {
+    int hh, grp;
+    // With a pair bias shared by every batch entry, an XCD takes one pair of
+    // heads (the two heads of a 128-byte line) for a share of the row
+    // groups, so that each XCD's L2 holds only its heads' bias.
+    const int n_pair = a.nh >> 1, per_pair = n_pair > 0 && 8 % n_pair == 0 ? 8 / n_pair : 0;
+    if (C::BIAS && a.bias && (a.nh & 1) == 0 && per_pair > 0 && n_grp % per_pair == 0) {
       const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-      const int per = a.nh * a.n_qt;  // items of one row group
-      item = ((slot / per) * 8 + xcd) * per + slot % per;
+      const int e = slot & 1, rest = slot >> 1;
+      qt = rest % a.n_qt;
+      grp = (xcd / n_pair) + per_pair * (rest / a.n_qt);
+      hh = 2 * (xcd % n_pair) + e;
+    } else {
+      if ((n_grp & 7) == 0) {
+        const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        const int per = a.nh * a.n_qt;  // items of one row group
+        item = ((slot / per) * 8 + xcd) * per + slot % per;
+      }
+      hh = item % a.nh;
+      const int rest = item / a.nh;
+      qt = rest % a.n_qt;
+      grp = rest / a.n_qt;
     }
-    const int hh = item % a.nh, rest = item / a.nh;
-    qt = rest % a.n_qt;
-    b_first = (rest / a.n_qt) * a.rows_per_wg;
+    b_first = grp * a.rows_per_wg;
     n_rep = min(a.rows_per_wg, a.nb - b_first);
     bh = b_first * a.nh + hh;
   } else {
