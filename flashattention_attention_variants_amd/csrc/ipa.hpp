@@ -95,8 +95,11 @@ __device__ __forceinline__ float wave_max(float x) {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
+// Three waves per SIMD (at most 168 registers, no spills at C_z = 128): the
+// residues x head groups of the structure-module shape (768 work-groups)
+// then run in one round on 256 compute units.
 template <class K>
-__global__ __launch_bounds__(256) void ipa_kernel(IpaArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void ipa_kernel(IpaArgs a) {
   constexpr int C = K::C, PQ = K::PQ, PV = K::PV, CZ = K::CZ, BN = K::BN, HW = K::HW;
   __shared__ __attribute__((aligned(16))) bf16 zs[CZ > 0 ? 2 * BN * CZ : 8];
   __shared__ __attribute__((aligned(16))) bf16 ps[2][16 * BN];  // weights, rows = heads
