@@ -68,12 +68,13 @@ struct IpaCfg {
 // mirrors), then the four row results read into scalar registers and
 // combined in one order for every lane.  Vector-ALU and scalar reads only:
 // the LDS permute behind a generic shuffle costs an LDS round trip per step.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
 template <class Op>
 __device__ __forceinline__ float wave_reduce(float x, Op op) {
-  auto dpp = [](float v, auto ctrl) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                                 decltype(ctrl)::value, 0xf, 0xf, false));
-  };
+  auto dpp = [](float v, auto ctrl) { return dpp_f32<decltype(ctrl)::value>(v); };
   x = op(x, dpp(x, std::integral_constant<int, 0xb1>{}));   // quad_perm [1,0,3,2]
   x = op(x, dpp(x, std::integral_constant<int, 0x4e>{}));   // quad_perm [2,3,0,1]
   x = op(x, dpp(x, std::integral_constant<int, 0x141>{}));  // row_half_mirror
@@ -322,32 +323,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void i
   }
 
   // ---- epilogue: reduce over the wave, normalise, store ---------------------
-  const float l = wave_sum(l_lane);
-  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  // The per-lane partial sums (C values, PV x 3 point coordinates, l) go
+  // through LDS: each quad of lanes adds its four (two DPP steps), one lane
+  // of each quad writes the quad sums into this wave's block (row = value,
+  // column = quad), and lane r adds row r's 16 quad sums (the lanes of the
+  // points take the three rows of theirs).  The z tiles (or a buffer of its
+  // own without z) hold the blocks once every wave is past the last tile.
+  constexpr int NR = C + 3 * PV + 1;  // rows: values, point coordinates, l
+  constexpr int RS = 20;              // row stride in floats (16 quads, 16-byte rows)
+  constexpr int RED = HW * NR * RS;
+  __shared__ __attribute__((aligned(16))) float red_own[CZ > 0 ? 4 : RED];
+  static_assert(CZ == 0 || 2 * BN * CZ * 2 >= RED * 4, "reduction blocks in the z tiles");
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  float* red = (CZ > 0 ? (float*)zs : red_own) + w * NR * RS;
+  auto put = [&](int row, float x) {
+    x += dpp_f32<0xb1>(x);  // quad_perm [1,0,3,2]
+    x += dpp_f32<0x4e>(x);  // quad_perm [2,3,0,1]
+    if ((lane & 3) == 0) red[row * RS + (lane >> 2)] = x;
+  };
 #pragma unroll
-  for (int c = 0; c < C; ++c) acc_o[c] = wave_sum(acc_o[c]) * inv;
+  for (int c = 0; c < C; ++c) put(c, acc_o[c]);
 #pragma unroll
   for (int q = 0; q < PV; ++q)
 #pragma unroll
-    for (int r = 0; r < 3; ++r) acc_g[q][r] = wave_sum(acc_g[q][r]) * inv;
-  if (active && lane == 0) {
-    bf16x8* op = (bf16x8*)(a.o + qrow * C);
+    for (int r = 0; r < 3; ++r) put(C + 3 * q + r, acc_g[q][r]);
+  put(NR - 1, l_lane);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  auto row_total = [&](int row) {
+    float t = 0.0f;
 #pragma unroll
-    for (int t = 0; t < C / 8; ++t) {
-      bf16x8 x;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (bf16)acc_o[8 * t + e];
-      op[t] = x;
+    for (int k = 0; k < 4; ++k) {
+      const f32x4 v = *(const f32x4*)(red + row * RS + 4 * k);
+      t += (v[0] + v[1]) + (v[2] + v[3]);
     }
+    return t;
+  };
+  const float t0 = row_total(min(lane, NR - 1));
+  const float l = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t0), NR - 1));
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  if (active && lane < C) a.o[qrow * C + lane] = (bf16)(t0 * inv);
+  if (active && lane >= C && lane < C + PV) {
     // back to the query residue's frame: R_i^T (y - t_i); no key: 0
-    float* pp = a.o_pts + qrow * PV * 3;
+    const int q = lane - C;
+    const float g0 = row_total(C + 3 * q) * inv, g1 = row_total(C + 3 * q + 1) * inv,
+                g2 = row_total(C + 3 * q + 2) * inv;
+    const float d0 = g0 - ti[0], d1 = g1 - ti[1], d2 = g2 - ti[2];
+    float* pp = a.o_pts + (qrow * PV + q) * 3;
 #pragma unroll
-    for (int q = 0; q < PV; ++q) {
-      const float d0 = acc_g[q][0] - ti[0], d1 = acc_g[q][1] - ti[1], d2 = acc_g[q][2] - ti[2];
-#pragma unroll
-      for (int r = 0; r < 3; ++r)
-        pp[3 * q + r] = l > 0.0f ? fmaf(Ri[r], d0, fmaf(Ri[3 + r], d1, Ri[6 + r] * d2)) : 0.0f;
-    }
+    for (int r = 0; r < 3; ++r)
+      pp[r] = l > 0.0f ? fmaf(Ri[r], d0, fmaf(Ri[3 + r], d1, Ri[6 + r] * d2)) : 0.0f;
   }
   if constexpr (CZ > 0) {
     if (lane == 0) lsum[w] = l;
