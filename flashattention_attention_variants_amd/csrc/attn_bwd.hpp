@@ -201,8 +201,14 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
   const int64_t s_span = n_s > 0 ? (int64_t)(n_s - 1) * s_row_b + D * 2 : 0;
   float st_lse = 0.0f, st_del = 0.0f;  // DKDV: one entry's statistics, staged through registers
   auto tile_coords = [&](int it, int& head, int& tile) {
-    head = DQ ? hr : hk * a.group + it / max(n_t, 1);
-    tile = t_lo + (DQ ? it : it % max(n_t, 1));
+    if (DQ || a.group == 1) {
+      // one head: no division (a scalar division costs tens of instructions)
+      head = DQ ? hr : hk;
+      tile = t_lo + it;
+    } else {
+      head = hk * a.group + it / max(n_t, 1);
+      tile = t_lo + it % max(n_t, 1);
+    }
   };
   auto load_tile = [&](int it, int stage) {
     int head, tile;
