@@ -305,7 +305,7 @@ def main():
     if not args.no_backward:
         d_o = inputs.randn(inputs._gen(wl.seed + 100), tuple(q.shape), wl.dtype).to(dev)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        ws = torch.empty(B * Hq * S, dtype=torch.float32, device=dev)
+        ws = torch.empty(2 * B * Hq * S, dtype=torch.float32, device=dev)
         bper = {}
         for vname in variants:
             o_, lse_ = api.fl_attn_fwd(q, k, v, return_lse=True, **kws[vname])

@@ -314,8 +314,11 @@ def fl_attn_bwd(q, k, v, o, lse, d_o, *, variant="vanilla", scale=None, softcap=
     dk = torch.empty_like(k) if dk is None else _dev(dk, "dk", dt)
     dv = torch.empty_like(v) if dv is None else _dev(dv, "dv", dt)
     if workspace is None:
-        workspace = torch.empty(max(B * Hq * Sq, 1), dtype=torch.float32, device=q.device)
+        workspace = torch.empty(max(2 * B * Hq * Sq, 1), dtype=torch.float32, device=q.device)
     _dev(workspace, "workspace", torch.float32)
+    if workspace.numel() < 2 * B * Hq * Sq:
+        raise ValueError("fl_attn_bwd: workspace needs %d float32 values, got %d"
+                         % (2 * B * Hq * Sq, workspace.numel()))
     docs = None
     if VARIANTS["document"] in (VARIANTS.get(variant, variant), VARIANTS.get(mask, mask)):
         docs = _dev(doc_offsets, "doc_offsets", torch.int32)

@@ -17,8 +17,9 @@
 // float32 beside it, Z = sum_j P and Dx = sum_j P dP; with P/Z exact and
 // D = Dx / Z, and dQ linear in D, one more product corrects it at the end:
 // dQ = scale / Z (dS~ K + (D~ - D) E), E = sum_j P mod' K.  It writes D
-// for the dK, dV launch, whose P keeps the factor Z (a relative error of
-// the order of the forward's rounding, not amplified).
+// and the LSE in log2 units for the dK, dV launch, whose P keeps the
+// factor Z (a relative error of the order of the forward's rounding, not
+// amplified).
 //
 // with mod' = 1 for plain scores and ALiBi (an additive term) and
 // 1 - tanh^2(S / cap) for softcap; P is recomputed from the scores and the
@@ -42,8 +43,10 @@
 // with ds_read_b64_tr_b16, and the packed bf16 dS (or P) registers are
 // directly their B operands, because the key order inside each 16-entry
 // step is the forward's permutation (16st + 4g + 0..3, 16st + 8 + 4g + 0..3).
-// DQ runs first and also writes D for the DKDV launch, which visits, for
-// each key tile, the tiles of every query head of the group that may see it.
+// DQ runs first and also writes D and LSE log2(e) for the DKDV launch,
+// which visits, for each key tile, the tiles of every query head of the
+// group that may see it, loading those two per streamed query into LDS
+// beside the tile.
 #pragma once
 
 #include "attn_mfma.hpp"
@@ -63,6 +66,9 @@ struct BwdCfg {
   static constexpr int BN = 64;       // streamed entries per tile
   static constexpr int T_ELEMS = BN * D;
   static constexpr int STAGE = 2 * T_ELEMS;
+  // LDS stages: the next tile loads while one computes (a third stage, two
+  // tiles in flight, measured 0.5-2% slower in either launch)
+  static constexpr int NSTAGE = 2;
   static constexpr int CH = BN * D / 8 / (NW * 64);  // 16-byte chunks per thread per tensor
   // 16-byte chunks of a row are XOR-swizzled by row & 7 in LDS
   __device__ static constexpr int swz(int row) { return row & 7; }
@@ -74,8 +80,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
   constexpr int D = C::D, BN = C::BN;
   constexpr bool DQ = C::ROLE == BWD_DQ;
-  __shared__ __attribute__((aligned(16))) bf16 lds[2 * C::STAGE];
-  __shared__ __attribute__((aligned(16))) float stat[2][2][BN];  // [stage][lse2, delta][entry]
+  __shared__ __attribute__((aligned(16))) bf16 lds[C::NSTAGE * C::STAGE];
+  // DKDV: the streamed queries' LSE and D, [stage][lse, delta][entry]
+  __shared__ __attribute__((aligned(16))) float stat[C::NSTAGE][2][BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -199,7 +206,6 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
   }
   const int n_s = DQ ? a.sk : a.sq;  // streamed entities
   const int64_t s_span = n_s > 0 ? (int64_t)(n_s - 1) * s_row_b + D * 2 : 0;
-  float st_lse = 0.0f, st_del = 0.0f;  // DKDV: one entry's statistics, staged through registers
   auto tile_coords = [&](int it, int& head, int& tile) {
     if (DQ || a.group == 1) {
       // one head: no division (a scalar division costs tens of instructions)
@@ -235,21 +241,15 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
     for (int i = 0; i < C::CH; ++i)
       lds_load16(rs2, ts + C::T_ELEMS + (i * C::NW + w) * 512, t_off[i] + e_off);
     if constexpr (!DQ) {
-      if (tid < BN) {
-        const int qi = (int)e0 + tid;
-        const int64_t li = b * a.lse_sb + head * a.lse_sh + qi;
-        const float l = qi < a.sq ? a.lse[0][li] : kNegInf;
-        st_lse = l == kNegInf ? __builtin_inff() : l * kLog2e;
-        st_del = qi < a.sq ? g2.delta[li] : 0.0f;
-      }
-    }
-  };
-  auto store_stats = [&](int stage) {
-    if constexpr (!DQ) {
-      if (tid < BN) {
-        stat[stage][0][tid] = st_lse;
-        stat[stage][1][tid] = st_del;
-      }
+      // the tile's 64 queries' LSE (log2 units, from the dQ launch) and D,
+      // straight into LDS as well (every wave loads both, so that each wave
+      // issues the same number of loads; the copies write equal values);
+      // queries past the end read 0 and are masked
+      const int64_t so = b * a.lse_sb + head * a.lse_sh;
+      const int64_t n_b = (int64_t)a.sq * 4;
+      const int eo = 4 * ((int)e0 + lane);
+      lds_load4(make_rsrc(g2.lse2 + so, n_b), &stat[stage][0][0], eo);
+      lds_load4(make_rsrc(g2.delta + so, n_b), &stat[stage][1][0], eo);
     }
   };
   auto sync_all = [&]() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
@@ -401,16 +401,23 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
     }
   };
 
-  // ---- main loop: two LDS stages, the next tile loads while this one computes
-  if (n_it > 0) {
-    load_tile(0, 0);
-    store_stats(0);
-    sync_all();
-  }
+  // ---- main loop: NSTAGE LDS stages, tiles it + 1 .. it + NSTAGE - 1 load
+  // while tile it computes
+  constexpr int NS = C::NSTAGE;
+  constexpr int LOADS = 2 * C::CH + (DQ ? 0 : 2);  // DMA loads per tile and wave
+  static_assert(NS == 2 || NS == 3, "stages");
+  static_assert(LOADS < 64, "vmcnt range");
+  for (int i = 0; i < NS - 1 && i < n_it; ++i) load_tile(i, i);
+  int stage = 0;
   for (int it = 0; it < n_it; ++it) {
-    const int stage = it & 1;
-    const bool next = it + 1 < n_it;
-    if (next) load_tile(it + 1, stage ^ 1);
+    // tile it has landed once no more than the next tile's loads are in
+    // flight; the barrier publishes it and closes every wave's reads of the
+    // stage that the load below refills (tile it - 1's)
+    if (NS == 3 && it + 1 < n_it)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LOADS) : "memory");
+    else
+      sync_all();
+    if (it + NS - 1 < n_it) load_tile(it + NS - 1, stage == 0 ? NS - 1 : stage - 1);
     int head, tile;
     tile_coords(it, head, tile);
     const int e0 = tile * BN, e1 = e0 + BN - 1;
@@ -422,10 +429,7 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
       else
         compute_tile(it, stage, std::integral_constant<bool, true>{});
     }
-    if (next) {
-      store_stats(stage ^ 1);
-      sync_all();
-    }
+    stage = stage == NS - 1 ? 0 : stage + 1;
   }
 
   // ---- epilogue: lane = row, registers = head dimension --------------------------
@@ -436,7 +440,11 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
     zinv = z > 0.0f ? 1.0f / z : 0.0f;  // no key: every product is zero
     const float dn = (dex + __shfl_xor(dex, 32)) * zinv;
     dfix = delta_row - dn;
-    if (g == 0 && wr0 + c < a.sq) g2.delta[b * a.lse_sb + hr * a.lse_sh + row] = dn;
+    if (g == 0 && wr0 + c < a.sq) {
+      const int64_t li = b * a.lse_sb + hr * a.lse_sh + row;
+      g2.delta[li] = dn;
+      g2.lse2[li] = lse2_row;
+    }
   }
   if (wr0 + c >= n_rows) return;
   const float sc = a.scale_log2 * kLn2;  // scale

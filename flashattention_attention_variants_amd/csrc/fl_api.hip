@@ -687,6 +687,7 @@ fl_status fl_attn_bwd(const void* q, const void* k, const void* v, const void* o
   g.dk = dk;
   g.dv = dv;
   g.delta = workspace;
+  g.lse2 = workspace + (int64_t)B * H_q * S_q;
   return launch_status(launch_bwd_bf16(a, g, mod, st));
 }
 

@@ -95,7 +95,10 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // [B, H_q, S_q]: written by the dQ launch, read by the dK, dV launch
+  // [B, H_q, S_q] each, written by the dQ launch and read by the dK, dV
+  // launch: D, and the LSE in log2 units (+inf for a query with no key)
+  float* delta;
+  float* lse2;
 };
 
 // Document mask: the document holding row i (the largest d < n_docs with
@@ -263,6 +266,28 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, void* lds,
       "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
       "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(byte_off), "s"(rs));
+#else
+  (void)rs;
+  (void)lds;
+  (void)byte_off;
+#endif
+}
+
+// 4 bytes per lane, the same way: lane l's dword lands at lds + 4*l, and a
+// lane whose offset lies past the resource's end writes 0.
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t rs, void* lds, int byte_off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
       "s_nop 0\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define FL_ABI_VERSION 4
+#define FL_ABI_VERSION 5
 
 typedef enum {
   FL_OK = 0,
@@ -259,8 +259,9 @@ fl_status fl_attn_merge(const float* o_parts, const float* lse_parts, void* o, f
  *   dq                [B, H_q, S_q, D] output
  *   dk, dv            [B, H_kv, S_k, D] outputs (query heads of a group add
  *                     into their K/V head)
- *   workspace         device float32 [B, H_q, S_q] (16 KiB per 4096 rows):
- *                     holds D between the two kernels the call enqueues
+ *   workspace         device float32 [2, B, H_q, S_q] (32 KiB per 4096 rows):
+ *                     holds D and the LSE in log2 units between the two
+ *                     kernels the call enqueues (twice the size of ABI 4's)
  * FL_BF16 with D = 64 only; every variant and composed mask of
  * fl_attn_fwd; positional masks need S_q == S_k.  Errors as fl_attn_fwd.
  */

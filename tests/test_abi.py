@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.fl_abi_version() == 4
+    assert lib.fl_abi_version() == 5
     for s in range(8):
         assert lib.fl_status_str(s)
     assert lib.fl_status_str(99) == b"unknown status"

@@ -157,3 +157,12 @@ def test_bwd_full_mha_s4096_sampled_heads():
         for b, h in heads:
             for name, gg, rr in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
                 check_grad(np64(gg[b, h]), rr[b, h], "%s %s (b %d, h %d)" % (name, kw, b, h))
+
+
+def test_bwd_workspace_size_checked():
+    """The workspace holds two float32 values per query row (D and the LSE
+    in log2 units); a smaller one is refused before anything launches."""
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16, device=DEV)
+    lse = torch.zeros(1, 2, 8, device=DEV)
+    with pytest.raises(ValueError):
+        api.fl_attn_bwd(q, q, q, q, lse, q, workspace=torch.empty(16, device=DEV))
