@@ -70,8 +70,20 @@ struct BwdCfg {
   // tiles in flight, measured 0.5-2% slower in either launch)
   static constexpr int NSTAGE = 2;
   static constexpr int CH = BN * D / 8 / (NW * 64);  // 16-byte chunks per thread per tensor
-  // 16-byte chunks of a row are XOR-swizzled by row & 7 in LDS
-  __device__ static constexpr int swz(int row) { return row & 7; }
+  // The 16-byte chunks of a row are XOR-swizzled in LDS by a function of
+  // the row pair j = (row >> 1) & 7, chosen for the two read shapes (64
+  // banks of 4 bytes; a 16-byte read serves 16 lanes per cycle, an 8-byte
+  // read 32): a row read takes one chunk of 16 consecutive rows, so the
+  // eight rows of each parity (one bank half each) need eight distinct
+  // swizzles; a transposed read takes four chunks (one half of the row) of
+  // rows r..r+3, so rows r and r + 2 (r = 0, 1 mod 4) need swizzles in
+  // opposite halves (bit 2).  j ^ 4 (j & 1) meets both; row & 7 met
+  // neither and cost every read of both kinds a two-way conflict.  Rows
+  // 8 apart differ by 4 in j, so their swizzles differ by 4.
+  __device__ static constexpr int swz(int row) {
+    const int j = (row >> 1) & 7;
+    return j ^ ((j & 1) << 2);
+  }
   static_assert(MOD == MOD_NONE || MOD == MOD_ALIBI || MOD == MOD_SOFTCAP, "score modification");
 };
 
@@ -194,6 +206,14 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
   if constexpr (C::MOD == MOD_ALIBI) {
     if constexpr (DQ) alibi_l2 = alibi_slope_log2(a, hr);
   }
+  // DKDV: key-side operand of the statistics' k-step (-1 in k-slots 0..2 of
+  // lane half 0) and the factor that takes the LSE to score units
+  bf16x8 fold_b = {};
+  if constexpr (!DQ) {
+    const bf16 m1 = (bf16)-1.0f, z = (bf16)0.0f;
+    if (g == 0) fold_b = bf16x8{m1, m1, m1, z, z, z, z, z};
+  }
+  const float inv_sc = 1.0f / a.scale_log2;
 
   // ---- tile loads: global -> LDS ----------------------------------------------------
   int t_off[C::CH];
@@ -261,13 +281,15 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
   for (int t = 0; t < D / 16; ++t) rd[t] = c * D + 8 * ((2 * t + g) ^ C::swz(c));
   // Transposed reads (A operands of the accumulations): lane i of a 16-lane
   // block points at row i/4 of a 4-entry group and 4 columns 4*(i%4) of the
-  // block's 16; rows 8m + tr_row share tr_row's swizzle.
+  // block's 16; rows 8m + tr_row take tr_row's swizzle for even m and that
+  // swizzle ^ 4 for odd m (tr[1]).
   const int tr_row = 4 * g + ((c & 15) >> 2);
-  int tr[D / 32];
+  int tr[2][D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
     const int d = 32 * db + 16 * (c >> 4) + 4 * (c & 3);
-    tr[db] = tr_row * D + 8 * ((d >> 3) ^ C::swz(tr_row)) + (d & 7);
+    tr[0][db] = tr_row * D + 8 * ((d >> 3) ^ C::swz(tr_row)) + (d & 7);
+    tr[1][db] = tr_row * D + 8 * ((d >> 3) ^ C::swz(tr_row + 8)) + (d & 7);
   }
 
   f32x16 acc1[D / 32], acc2[D / 32];  // DQ: dQ^T and E^T; DKDV: dK^T and dV^T
@@ -283,9 +305,15 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
   auto read_tr = [&](uint32_t tb, int kb, bf16x8 (&op)[D / 32][2]) {
     u32x2 raw[D / 32 * 4];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db) {
+      // one register per base, so that the row offsets below become the
+      // reads' immediate offsets (left alone, the compiler adds them to the
+      // stage address first and spends an add per read)
+      uint32_t b0 = tb + 2 * tr[0][db], b1 = tb + 2 * tr[1][db];
+      asm("" : "+v"(b0), "+v"(b1));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) raw[4 * db + i] = ds_read_tr(tb + 2 * tr[db] + 2 * (8 * i + 32 * kb) * D);
+      for (int i = 0; i < 4; ++i) raw[4 * db + i] = ds_read_tr((i & 1 ? b1 : b0) + 2 * (8 * i + 32 * kb) * D);
+    }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -304,10 +332,43 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
     const bf16* t2 = t1 + C::T_ELEMS;
     float sl = alibi_l2;
     if constexpr (C::MOD == MOD_ALIBI && !DQ) sl = alibi_slope_log2(a, head);
+    // DKDV: the tile's statistics enter the products as one more k-step
+    // (the forward folds its reference the same way).  The streamed side
+    // (A, a query per row) carries -(hi + mid + lo) of the query's value in
+    // k-slots 0..2 of lane half 0 against ones on the key side (B), so
+    //   X = Q K^T - L,   L = LSE log2(e) / (scale log2(e)) = LSE / scale,
+    //   Y = dO V^T - D,
+    // and s = X scale log2(e) = S log2(e) - LSE log2(e), p = 2^s, dS =
+    // p Y: no statistic is read per score.  The three bf16 parts hold the
+    // float32 value exactly (each takes the next 8 significant bits), and
+    // each product with 1 is exact.  Softcap keeps L out of X (its scores
+    // pass through tanh first) and reads the LSE per score.
+    constexpr bool FOLD_L = !DQ && C::MOD != MOD_SOFTCAP;
+    bf16x8 fold_a[2][2];  // [kb][L, D]
+    if constexpr (!DQ) {
+      auto split3 = [&](float v) {
+        v = g == 0 ? v : 0.0f;
+        const uint32_t u = __builtin_bit_cast(uint32_t, v), h = u & 0xffff0000u;
+        const float r1 = v - __builtin_bit_cast(float, h);
+        const uint32_t m = __builtin_bit_cast(uint32_t, r1) & 0xffff0000u;
+        const float r2 = r1 - __builtin_bit_cast(float, m);
+        const u32x4 w = {(h >> 16) | m, __builtin_bit_cast(uint32_t, r2) >> 16, 0u, 0u};
+        return __builtin_bit_cast(bf16x8, w);
+      };
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        // +inf (a query with no key) becomes a huge finite L: its p is 0
+        const float l = FOLD_L ? fminf(stat[stage][0][32 * kb + c] * inv_sc, 1e30f) : 0.0f;
+        fold_a[kb][0] = split3(l);
+        fold_a[kb][1] = split3(stat[stage][1][32 * kb + c]);
+      }
+    }
     // X = T1 R1^T and Y = T2 R2^T of entry half kb
     auto products = [&](int kb, f32x16& x, f32x16& y) {
       x = f32x16{};
       y = f32x16{};
+      if constexpr (FOLD_L) x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fold_a[kb][0], fold_b, x, 0, 0, 0);
+      if constexpr (!DQ) y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fold_a[kb][1], fold_b, y, 0, 0, 0);
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
         const bf16x8 a1 = *(const bf16x8*)(t1 + rd[t] + 32 * kb * D);
@@ -327,17 +388,13 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
       products(kb, x, y);
       // streamed entity of register 0 in this lane; register r adds acc_row(r)
       const int eb = e0 + 32 * kb + 4 * g;
-      float lse4[16], del4[16];
-      if constexpr (!DQ) {
+      float lse4[16];
+      if constexpr (!DQ && !FOLD_L) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const f32x4 lv = *(const f32x4*)&stat[stage][0][32 * kb + 4 * g + 8 * m];
-          const f32x4 dv = *(const f32x4*)&stat[stage][1][32 * kb + 4 * g + 8 * m];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            lse4[4 * m + e] = lv[e];
-            del4[4 * m + e] = dv[e];
-          }
+          for (int e = 0; e < 4; ++e) lse4[4 * m + e] = lv[e];
         }
       }
       f32x16 ds, pp;
@@ -353,9 +410,10 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
           const float th = s * (1.0f / a.softcap_log2);
           dmod = 1.0f - th * th;
         }
-        const float l2 = DQ ? lse2_row : lse4[r];
-        const float dl = DQ ? delta_row : del4[r];
-        float p = fast_exp2(s - l2);
+        float p;
+        if constexpr (DQ) p = fast_exp2(s - lse2_row);
+        else if constexpr (FOLD_L) p = fast_exp2(s);
+        else p = fast_exp2(s - lse4[r]);
         if constexpr (MASKED) p = (ent >= lane_lo && ent <= lane_hi) ? p : 0.0f;
         if constexpr (DQ) {
           dex = fmaf(p, y[r], dex);
@@ -364,7 +422,7 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
         } else {
           pp[r] = p;
         }
-        ds[r] = p * (y[r] - dl) * dmod;
+        ds[r] = DQ ? p * (y[r] - delta_row) * dmod : p * y[r] * dmod;
       }
       // B operands: 16-entry steps 2kb and 2kb + 1 in the permuted order
       bf16x8 pds[2], ppk[2];
