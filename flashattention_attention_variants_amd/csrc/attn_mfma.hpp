@@ -77,8 +77,13 @@ struct MfmaCfg {
   static constexpr int BN = 64;              // keys per tile
   // K and V tiles sit in LDS row-major without padding; the 16-byte chunks
   // of a row are XOR-swizzled by the row index so that the operand reads
-  // (eight consecutive K rows per 128-byte b128 group; four V rows x two
-  // chunks per transposed-read group) hit distinct banks.
+  // hit distinct banks (64 banks of 4 bytes).  A K read serves 16 lanes
+  // (16 consecutive rows, one logical chunk) per cycle: the eight rows of
+  // each parity share a bank half, so with 128-byte rows the swizzle
+  // follows the row pair, (row >> 1) & 7 (row & 7 gave rows 8 apart the
+  // same banks, a two-way conflict on every K read); with 64-byte rows,
+  // rows 4 apart share banks and it follows (row >> 2) & 3.  A transposed
+  // V read serves 32 lanes (four rows x four chunks) per cycle.
   static constexpr int KCPR = DQK / 8;       // 16-byte chunks per K row
   static constexpr int VCPR = DV / 8;        // 16-byte chunks per V row
   static constexpr int K_ELEMS = BN * DQK;
@@ -97,7 +102,7 @@ struct MfmaCfg {
 #define FL_FWD_STAGES 3
 #endif
   static constexpr int STAGES = DEC ? FL_DEC_STAGES : (GATE ? FL_EVO_STAGES : FL_FWD_STAGES);
-  __device__ static constexpr int kswz(int row) { return KCPR == 4 ? (row >> 1) & 3 : row & 7; }
+  __device__ static constexpr int kswz(int row) { return KCPR == 4 ? (row >> 2) & 3 : (row >> 1) & 7; }
   __device__ static constexpr int vswz(int row) { return VCPR == 4 ? 2 * ((row >> 1) & 1) : 2 * (row & 3); }
   static constexpr int KCH = BN * DQK / 8 / (NW * 64);  // 16-byte K chunks per thread
   static constexpr int VCH = BN * DV / 8 / (NW * 64);   // 16-byte V chunks per thread
