@@ -14,9 +14,11 @@
 // 25); under a sharp softmax dP - D is a small difference of large values,
 // so either error dominates the gradients (1.1% mean relative error of dQ
 // at those logits).  The dQ launch runs its sweep with D~ = dO . O and, in
-// float32 beside it, Z = sum_j P and Dx = sum_j P dP; with P/Z exact and
-// D = Dx / Z, and dQ linear in D, one more product corrects it at the end:
-// dQ = scale / Z (dS~ K + (D~ - D) E), E = sum_j P mod' K.  It writes D
+// float32 beside it, Z = sum_j P and X = sum_j P (dP - D~) (D~ enters the
+// dP product as one more k-step, so X carries no cancellation); with P/Z
+// exact, D = sum_j P dP / Z = D~ + X / Z, and dQ linear in D, one more
+// product corrects it at the end: dQ = scale / Z (dS~ K + (D~ - D) E),
+// E = sum_j P mod' K.  It writes D
 // and the LSE in log2 units for the dK, dV launch, whose P keeps the
 // factor Z (a relative error of the order of the forward's rounding, not
 // amplified).
@@ -54,6 +56,19 @@
 namespace fl {
 
 enum BwdRole { BWD_DQ = 0, BWD_DKDV = 1 };
+
+// The float32 value v as three bf16 parts in k-slots 0..2 of a lane-half-0
+// matrix operand (zero for lane half 1, `half0` false): each part takes the
+// next 8 significant bits, so hi + mid + lo == v exactly.
+__device__ __forceinline__ bf16x8 split3_operand(float v, bool half0) {
+  v = half0 ? v : 0.0f;
+  const uint32_t u = __builtin_bit_cast(uint32_t, v), h = u & 0xffff0000u;
+  const float r1 = v - __builtin_bit_cast(float, h);
+  const uint32_t m = __builtin_bit_cast(uint32_t, r1) & 0xffff0000u;
+  const float r2 = r1 - __builtin_bit_cast(float, m);
+  const u32x4 w = {(h >> 16) | m, __builtin_bit_cast(uint32_t, r2) >> 16, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, w);
+}
 
 
 template <int ROLE_, int MOD_>
@@ -213,6 +228,11 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
     const bf16 m1 = (bf16)-1.0f, z = (bf16)0.0f;
     if (g == 0) fold_b = bf16x8{m1, m1, m1, z, z, z, z, z};
   }
+  // DQ: Y = dP^T - D~ starts from -D~ (the lane's query is the column of
+  // every accumulator register)
+  f32x16 y_init;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) y_init[r] = -delta_row;
   const float inv_sc = 1.0f / a.scale_log2;
 
   // ---- tile loads: global -> LDS ----------------------------------------------------
@@ -346,21 +366,12 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
     constexpr bool FOLD_L = !DQ && C::MOD != MOD_SOFTCAP;
     bf16x8 fold_a[2][2];  // [kb][L, D]
     if constexpr (!DQ) {
-      auto split3 = [&](float v) {
-        v = g == 0 ? v : 0.0f;
-        const uint32_t u = __builtin_bit_cast(uint32_t, v), h = u & 0xffff0000u;
-        const float r1 = v - __builtin_bit_cast(float, h);
-        const uint32_t m = __builtin_bit_cast(uint32_t, r1) & 0xffff0000u;
-        const float r2 = r1 - __builtin_bit_cast(float, m);
-        const u32x4 w = {(h >> 16) | m, __builtin_bit_cast(uint32_t, r2) >> 16, 0u, 0u};
-        return __builtin_bit_cast(bf16x8, w);
-      };
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         // +inf (a query with no key) becomes a huge finite L: its p is 0
         const float l = FOLD_L ? fminf(stat[stage][0][32 * kb + c] * inv_sc, 1e30f) : 0.0f;
-        fold_a[kb][0] = split3(l);
-        fold_a[kb][1] = split3(stat[stage][1][32 * kb + c]);
+        fold_a[kb][0] = split3_operand(l, g == 0);
+        fold_a[kb][1] = split3_operand(stat[stage][1][32 * kb + c], g == 0);
       }
     }
     // X = T1 R1^T and Y = T2 R2^T of entry half kb
@@ -369,6 +380,7 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
       y = f32x16{};
       if constexpr (FOLD_L) x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fold_a[kb][0], fold_b, x, 0, 0, 0);
       if constexpr (!DQ) y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fold_a[kb][1], fold_b, y, 0, 0, 0);
+      else y = y_init;
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
         const bf16x8 a1 = *(const bf16x8*)(t1 + rd[t] + 32 * kb * D);
@@ -422,7 +434,7 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
         } else {
           pp[r] = p;
         }
-        ds[r] = DQ ? p * (y[r] - delta_row) * dmod : p * y[r] * dmod;
+        ds[r] = p * y[r] * dmod;
       }
       // B operands: 16-entry steps 2kb and 2kb + 1 in the permuted order
       bf16x8 pds[2], ppk[2];
@@ -496,8 +508,9 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
   if constexpr (DQ) {
     const float z = zex + __shfl_xor(zex, 32);
     zinv = z > 0.0f ? 1.0f / z : 0.0f;  // no key: every product is zero
-    const float dn = (dex + __shfl_xor(dex, 32)) * zinv;
-    dfix = delta_row - dn;
+    // dex sums p (dP - D~): D = D~ + dex / Z
+    dfix = -(dex + __shfl_xor(dex, 32)) * zinv;
+    const float dn = delta_row - dfix;
     if (g == 0 && wr0 + c < a.sq) {
       const int64_t li = b * a.lse_sb + hr * a.lse_sh + row;
       g2.delta[li] = dn;
