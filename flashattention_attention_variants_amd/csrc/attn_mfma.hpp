@@ -161,6 +161,26 @@ __device__ __forceinline__ u32x2 ds_read_tr(uint32_t addr) {
       u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)addr));
 }
 
+// Cross-lane reads whose lane-address register is formed where it is used
+// (the lane index comes from assembly, which the compiler does not hoist):
+// left to itself the compiler computes such addresses once, at the top of
+// the kernel, and keeps them live across the whole tile loop.
+__device__ __forceinline__ int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+// x of lane (this lane & 15)
+__device__ __forceinline__ float lane_read16(float x) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_ds_bpermute((lane_here() & 15) << 2, __builtin_bit_cast(int, x)));
+}
+// x of lane (this lane ^ 32)
+__device__ __forceinline__ float lane_xor32(float x) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_ds_bpermute((lane_here() ^ 32) << 2, __builtin_bit_cast(int, x)));
+}
+
 #ifndef FL_SCHED_INTERLEAVE
 #define FL_SCHED_INTERLEAVE 1
 #endif
@@ -422,7 +442,21 @@ void attn_mfma_kernel(KernelArgs a) {
   }
 
   // ---- this wave's rows and their key intervals ----------------------------
+  // cross-lane reads: walking launches use them inside their loop and keep
+  // the plain forms
+  auto xor32 = [&](float x) {
+    if constexpr (C::PERSIST) return __shfl_xor(x, 32);
+    else return lane_xor32(x);
+  };
+  auto read16 = [&](float x) {
+    if constexpr (C::PERSIST) return __shfl(x, c & 15);
+    else return lane_read16(x);
+  };
   const int wq0 = q0 + wr * 32 * QB;
+  // the same in a scalar register, for the epilogue (a vector copy would
+  // stay live across the loop); walking launches keep the vector one, which
+  // their loop uses anyway
+  const int wq0_s = __builtin_amdgcn_readfirstlane(wq0);
   const int wq1 = min(wq0 + 32 * QB, a.sq) - 1;  // last valid row of the wave
   int wp_min, wp_max, w_lo_min, w_hi_min, w_lo_max, w_hi_max;
   pos_range(min(wq0, a.sq - 1), max(wq1, min(wq0, a.sq - 1)), wp_min, wp_max);
@@ -684,6 +718,14 @@ void attn_mfma_kernel(KernelArgs a) {
   const float alibi_f = alibi_l2 / fold_m;  // the folded slope, in the units of S^T
   bf16 sl0, sl1, sl2;
   split3(alibi_f, sl0, sl1, sl2);
+  // k-slots 4..7 of the query-side operand, the same in every lane: held in
+  // scalar registers (decode rows of one wave may belong to several heads)
+  uint32_t sl01 = __builtin_bit_cast(uint32_t, bf16x2{sl0, sl1});
+  uint32_t sl2z = __builtin_bit_cast(uint32_t, bf16x2{sl2, zero});
+  if constexpr (C::ALIBI_FOLD && !C::DEC) {
+    sl01 = __builtin_amdgcn_readfirstlane(sl01);
+    sl2z = __builtin_amdgcn_readfirstlane(sl2z);
+  }
   // query-side operand for reference m (bf16-exact) and, under ALiBi, the
   // tile at j0
   auto set_qext = [&](int s, int qb, float m, int j0) {
@@ -691,7 +733,9 @@ void attn_mfma_kernel(KernelArgs a) {
     if constexpr (C::ALIBI_FOLD) {
       bf16 x0, x1, x2;
       split3(-alibi_f * (float)(lane_pos[qb] - j0), x0, x1, x2);
-      qext[s][qb] = bf16x8{mt, x0, x1, x2, sl0, sl1, sl2, zero};
+      const u32x4 w4 = {__builtin_bit_cast(uint32_t, bf16x2{mt, x0}),
+                        __builtin_bit_cast(uint32_t, bf16x2{x1, x2}), sl01, sl2z};
+      qext[s][qb] = __builtin_bit_cast(bf16x8, w4);
     } else if constexpr (C::KMASK) {
       qext[s][qb] = bf16x8{mt, one, zero, zero, zero, zero, zero, zero};
     } else {
@@ -983,13 +1027,13 @@ void attn_mfma_kernel(KernelArgs a) {
           float xm = kNegInf;
 #pragma unroll
           for (int r = 0; r < 16; ++r) xm = fmaxf(xm, rs[r]);
-          xm = fmaxf(xm, __shfl_xor(xm, 32));
+          xm = fmaxf(xm, xor32(xm));
           // move when the row maximum passes 32 units of S^T (terms of 2^16
           // to 2^32), or when the row (both lane halves, this unit included)
           // has no mass and its maximum is below -32 units; both halves of a
           // row decide alike
           const float lr = l_run[s][qb] + lsum;
-          const float l_row = lr + __shfl_xor(lr, 32);
+          const float l_row = lr + xor32(lr);
           const bool move = xm != kNegInf && (xm > 32.0f || (l_row == 0.0f && xm < -32.0f));
           // the new reference is the row maximum rounded to bf16, so that
           // one k-slot carries it exactly
@@ -1072,7 +1116,7 @@ void attn_mfma_kernel(KernelArgs a) {
         const float m_old = m_run[s][qb];
         interleave_hint();
         if (__builtin_amdgcn_ballot_w64(xm > m_old + thr)) {
-          const float xf = fmaxf(xm, __shfl_xor(xm, 32));
+          const float xf = fmaxf(xm, xor32(xm));
           const bool move = xf > m_old + thr;
           const float m_new = move ? xf : m_old;
           const float alpha = !move ? 1.0f : (m_old == kNegInf ? 0.0f : fast_exp2(m_old - m_new));
@@ -1139,11 +1183,11 @@ void attn_mfma_kernel(KernelArgs a) {
   bool fast_ok = false;  // the first pass stands (its sums are in lacc)
   auto row_sum = [&](int s, int qb) {
     if (C::SCAPB || (C::FASTP && fast_ok)) {
-      const float l0 = __shfl(lacc[s][qb][0], c & 15);
-      const float l1 = __shfl(lacc[s][qb][1], c & 15);
+      const float l0 = read16(lacc[s][qb][0]);
+      const float l1 = read16(lacc[s][qb][1]);
       return c < 16 ? l0 : l1;
     } else {
-      return l_run[s][qb] + __shfl_xor(l_run[s][qb], 32);
+      return l_run[s][qb] + xor32(l_run[s][qb]);
     }
   };
   auto finish_row = [&](bool gate_wait) {
@@ -1152,6 +1196,13 @@ void attn_mfma_kernel(KernelArgs a) {
     } else {
       (void)gate_wait;
     }
+    // the lane's row and half and the wave's first row, formed again here:
+    // kept from the prologue, the values derived from them stay live (or
+    // spilled) across the loop (walking launches finish rows inside their
+    // loop and use the prologue's)
+    const int lane_f = C::PERSIST ? lane : lane_here();
+    const int cf = C::PERSIST ? c : lane_f & 31, gf = C::PERSIST ? g : lane_f >> 5;
+    const int wq0f = C::PERSIST ? wq0 : wq0_s;
     float inv[NSU][QB];
   #pragma unroll
     for (int s = 0; s < NSU; ++s)
@@ -1159,9 +1210,9 @@ void attn_mfma_kernel(KernelArgs a) {
       for (int qb = 0; qb < QB; ++qb) {
         const float l = row_sum(s, qb);
         inv[s][qb] = l > 0.0f ? 1.0f / l : 0.0f;
-        const int qi = wq0 + 32 * qb + c;
+        const int qi = wq0f + 32 * qb + cf;
         float* lse_out = a.lse[stream_of(s)];
-        if (lse_out && g == 0 && qi < a.sq) {
+        if (lse_out && gf == 0 && qi < a.sq) {
           const float m = m_run[s][qb] * fold_m;  // base-2 units
           const float lse = l > 0.0f ? (m + __builtin_log2f(l)) * kLn2 : kNegInf;
           lse_out[b * a.lse_sb + h * a.lse_sh + qi] = lse;
@@ -1180,14 +1231,14 @@ void attn_mfma_kernel(KernelArgs a) {
       if (ws == 1) {
   #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          float* xr = xo + (wr * 32 * QB + 32 * qb + c) * XS;
+          float* xr = xo + (wr * 32 * QB + 32 * qb + cf) * XS;
   #pragma unroll
           for (int db = 0; db < DV / 32; ++db)
   #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
               const f32x4 v = {oacc[0][qb][db][4 * r4] * inv[0][qb], oacc[0][qb][db][4 * r4 + 1] * inv[0][qb],
                                oacc[0][qb][db][4 * r4 + 2] * inv[0][qb], oacc[0][qb][db][4 * r4 + 3] * inv[0][qb]};
-              *(f32x4*)(xr + 32 * db + 8 * r4 + 4 * g) = v;
+              *(f32x4*)(xr + 32 * db + 8 * r4 + 4 * gf) = v;
             }
         }
       }
@@ -1197,14 +1248,14 @@ void attn_mfma_kernel(KernelArgs a) {
 
   #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const int qi = wq0 + 32 * qb + c;
+      const int qi = wq0f + 32 * qb + cf;
       if (qi >= a.sq) continue;
       bf16* op = (bf16*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_si;
       const bf16* gp = !C::GATE ? nullptr
                        : C::GATE_LDS
-                           ? gbuf + ((b - b_first) & 1) * C::G_ELEMS + (wq0 - q0 + 32 * qb + c) * DV
+                           ? gbuf + ((b - b_first) & 1) * C::G_ELEMS + (wq0f - q0 + 32 * qb + cf) * DV
                            : (const bf16*)a.gate + b * a.o_sb + h * a.o_sh + (int64_t)qi * a.o_si;
-      const float* xr = xo + (wr * 32 * QB + 32 * qb + c) * XS;
+      const float* xr = xo + (wr * 32 * QB + 32 * qb + cf) * XS;
   // A lane holds dims 8 r4 + 4g + 0..3 of its row; pairs (r4 = 2r, 2r + 1)
   // trade halves with the lane 32 apart (the same row) so that each lane
   // moves 16 contiguous bytes (dims 16r + 8g .. +7) per global access.
@@ -1214,7 +1265,7 @@ void attn_mfma_kernel(KernelArgs a) {
         for (int r = 0; r < 2; ++r) {
           bf16x4 gvv[2];
           if constexpr (C::GATE && !C::GATE_LDS) {
-            const u32x4 raw = *(const u32x4*)(gp + 32 * db + 16 * r + 8 * g);
+            const u32x4 raw = *(const u32x4*)(gp + 32 * db + 16 * r + 8 * gf);
             const auto s0 = __builtin_amdgcn_permlane32_swap(raw[0], raw[2], false, false);
             const auto s1 = __builtin_amdgcn_permlane32_swap(raw[1], raw[3], false, false);
             gvv[0] = __builtin_bit_cast(bf16x4, u32x2{s0[0], s1[0]});
@@ -1224,7 +1275,7 @@ void attn_mfma_kernel(KernelArgs a) {
   #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const int r4 = 2 * r + hh;
-            const int d = 32 * db + 8 * r4 + 4 * g;
+            const int d = 32 * db + 8 * r4 + 4 * gf;
             float ov[4];
   #pragma unroll
             for (int e = 0; e < 4; ++e) ov[e] = oacc[0][qb][db][4 * r4 + e] * inv[0][qb];
@@ -1243,7 +1294,7 @@ void attn_mfma_kernel(KernelArgs a) {
           }
           const auto t0 = __builtin_amdgcn_permlane32_swap(packed[0][0], packed[1][0], false, false);
           const auto t1 = __builtin_amdgcn_permlane32_swap(packed[0][1], packed[1][1], false, false);
-          *(u32x4*)(op + 32 * db + 16 * r + 8 * g) = u32x4{t0[0], t1[0], t0[1], t1[1]};
+          *(u32x4*)(op + 32 * db + 16 * r + 8 * gf) = u32x4{t0[0], t1[0], t0[1], t1[1]};
         }
     }
   };
@@ -1284,8 +1335,8 @@ void attn_mfma_kernel(KernelArgs a) {
     bool bad = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float l0 = __shfl(lacc[0][qb][0], c & 15);
-      const float l1 = __shfl(lacc[0][qb][1], c & 15);
+      const float l0 = read16(lacc[0][qb][0]);
+      const float l1 = read16(lacc[0][qb][1]);
       const float l = c < 16 ? l0 : l1;
       // rows past S_q (zero queries, under ALiBi possibly far below range)
       // produce no output and are left out
@@ -1294,9 +1345,11 @@ void attn_mfma_kernel(KernelArgs a) {
       bad |= real & ((has & !(l >= lo)) | !(l <= 0x1p100f));
     }
     __shared__ int pass_bad;
-    if (tid == 0) pass_bad = 0;
+    // (every lane of the writing waves stores the same value, so no lane
+    // index stays live across the tile loop for a single-lane store)
+    if (w == 0) pass_bad = 0;
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) pass_bad = 1;
+    if (__builtin_amdgcn_ballot_w64(bad)) pass_bad = 1;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     fast_ok = pass_bad == 0;
     if (!fast_ok) reset_state();
