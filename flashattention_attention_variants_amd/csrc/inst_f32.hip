@@ -1,4 +1,4 @@
-// Template instances of the float32 attention kernel.
+// Template instances of the float32 attention kernel (matrix cores).
 #include "attn_f32.hpp"
 #include "fl_launch.hpp"
 
@@ -8,7 +8,7 @@ template <class C>
 static hipError_t go(const KernelArgs& a, hipStream_t st) {
   const int nwg = a.nb * a.nh * a.n_qt;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(attn_f32_kernel<C>, dim3(nwg), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(attn_f32_kernel<C>, dim3(nwg), dim3(C::NW * 64), 0, st, a);
   return hipGetLastError();
 }
 
