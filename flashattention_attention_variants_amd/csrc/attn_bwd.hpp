@@ -57,16 +57,25 @@ namespace fl {
 
 enum BwdRole { BWD_DQ = 0, BWD_DKDV = 1 };
 
-// The float32 value v as three bf16 parts in k-slots 0..2 of a lane-half-0
-// matrix operand (zero for lane half 1, `half0` false): each part takes the
-// next 8 significant bits, so hi + mid + lo == v exactly.
-__device__ __forceinline__ bf16x8 split3_operand(float v, bool half0) {
-  v = half0 ? v : 0.0f;
+// The float32 value v as three bf16 parts: each takes the next 8
+// significant bits, so hi + mid + lo == v exactly.  Returned as the bit
+// patterns {hi, mid, lo} in the low halves of three words.
+__device__ __forceinline__ void split3_bits(float v, uint32_t (&p)[3]) {
   const uint32_t u = __builtin_bit_cast(uint32_t, v), h = u & 0xffff0000u;
   const float r1 = v - __builtin_bit_cast(float, h);
   const uint32_t m = __builtin_bit_cast(uint32_t, r1) & 0xffff0000u;
   const float r2 = r1 - __builtin_bit_cast(float, m);
-  const u32x4 w = {(h >> 16) | m, __builtin_bit_cast(uint32_t, r2) >> 16, 0u, 0u};
+  p[0] = h >> 16;
+  p[1] = m >> 16;
+  p[2] = __builtin_bit_cast(uint32_t, r2) >> 16;
+}
+// v's three parts in k-slots 0..2 of a lane-half-0 matrix operand (zero for
+// lane half 1, `half0` false); k-slots 3..5 hold `s345` (bf16 bits, 0: none)
+__device__ __forceinline__ bf16x8 split3_operand(float v, bool half0, uint32_t s345 = 0) {
+  uint32_t p[3];
+  split3_bits(half0 ? v : 0.0f, p);
+  const uint32_t k = half0 ? s345 : 0u;
+  const u32x4 w = {p[0] | (p[1] << 16), p[2] | (k << 16), k | (k << 16), 0u};
   return __builtin_bit_cast(bf16x8, w);
 }
 
@@ -234,6 +243,20 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) y_init[r] = -delta_row;
   const float inv_sc = 1.0f / a.scale_log2;
+  // DQ under ALiBi: the query side of the distance k-step (sigma in k-slots
+  // 0..2 of lane half 0) and the LSE with the query term for either sigma
+  bf16x8 sig_pos = {}, sig_neg = {};
+  float lse2_pos = lse2_row, lse2_neg = lse2_row;
+  if constexpr (DQ && C::MOD == MOD_ALIBI) {
+    const bf16 one = (bf16)1.0f, mone = (bf16)-1.0f, z = (bf16)0.0f;
+    if (g == 0) {
+      sig_pos = bf16x8{one, one, one, z, z, z, z, z};
+      sig_neg = bf16x8{mone, mone, mone, z, z, z, z, z};
+    }
+    const float qt = alibi_l2 * (float)(row - wr0);
+    lse2_pos = lse2_row + qt;
+    lse2_neg = lse2_row - qt;
+  }
 
   // ---- tile loads: global -> LDS ----------------------------------------------------
   int t_off[C::CH];
@@ -343,8 +366,11 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
       }
   };
 
-  auto compute_tile = [&](int it, int stage, auto masked_tag) {
+  // straddle_tag: some unit of the tile straddles the diagonal (ALiBi's
+  // correction is compiled only into that form)
+  auto compute_tile = [&](int it, int stage, auto masked_tag, auto straddle_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr bool STR = decltype(straddle_tag)::value;
     int head, tile;
     tile_coords(it, head, tile);
     const int e0 = tile * BN;
@@ -364,13 +390,49 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
     // each product with 1 is exact.  Softcap keeps L out of X (its scores
     // pass through tanh first) and reads the LSE per score.
     constexpr bool FOLD_L = !DQ && C::MOD != MOD_SOFTCAP;
+    // ALiBi: the distance penalty rides on the same k-step (as in the
+    // forward).  With sigma = +1 on a unit whose queries all lie at or after
+    // its keys and -1 on one whose queries all lie at or before them,
+    //   -slope |q - k| = -sigma slope (q - w0) + sigma slope (k - w0),
+    // w0 the wave's first row.  DKDV adds the query term to L (A side) and
+    // takes the key term as three parts of slope (k - w0) / scale in k-slots
+    // 3..5 of the key side (B, sign sigma) against ones; DQ takes the key
+    // term as three parts on the key side (A) against sigma in the query
+    // side (B) and subtracts the query term with the LSE.  A unit that
+    // straddles the diagonal takes sigma = +1 and a vector correction for
+    // its pairs with k > q.  Every value carried is below the distance
+    // scale itself, so the float32 parts lose nothing against the plain
+    // penalty.
+    constexpr bool AF = C::MOD == MOD_ALIBI;
+    const float a_f = sl * inv_sc;  // the slope in units of X
+    bool neg[2] = {false, false}, straddle[2] = {false, false};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int u_lo = e0 + 32 * kb;  // the unit's streamed entities
+      const int q_lo = DQ ? wr0 : u_lo, q_hi = q_lo + 31;
+      const int k_lo = DQ ? u_lo : wr0, k_hi = k_lo + 31;
+      neg[kb] = q_hi <= k_lo;
+      straddle[kb] = !neg[kb] && q_lo < k_hi;
+    }
+    bf16x8 kb_pos = fold_b, kb_neg = fold_b;  // DKDV key side under ALiBi
+    if constexpr (AF && !DQ) {
+      uint32_t kp[3];
+      split3_bits(a_f * (float)(row - wr0), kp);
+      const uint32_t m1 = 0xbf80u;  // bf16 -1
+      u32x4 wv = {m1 | (m1 << 16), m1 | (kp[0] << 16), kp[1] | (kp[2] << 16), 0u};
+      if (g != 0) wv = u32x4{0u, 0u, 0u, 0u};
+      kb_pos = __builtin_bit_cast(bf16x8, wv);
+      if (g == 0) wv ^= u32x4{0u, 0x80000000u, 0x80008000u, 0u};
+      kb_neg = __builtin_bit_cast(bf16x8, wv);
+    }
     bf16x8 fold_a[2][2];  // [kb][L, D]
     if constexpr (!DQ) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         // +inf (a query with no key) becomes a huge finite L: its p is 0
-        const float l = FOLD_L ? fminf(stat[stage][0][32 * kb + c] * inv_sc, 1e30f) : 0.0f;
-        fold_a[kb][0] = split3_operand(l, g == 0);
+        float l = FOLD_L ? fminf(stat[stage][0][32 * kb + c] * inv_sc, 1e30f) : 0.0f;
+        if constexpr (AF) l += (neg[kb] ? -a_f : a_f) * (float)(e0 + 32 * kb + c - wr0);
+        fold_a[kb][0] = split3_operand(l, g == 0, AF ? 0x3f80u : 0u);  // ones in k-slots 3..5
         fold_a[kb][1] = split3_operand(stat[stage][1][32 * kb + c], g == 0);
       }
     }
@@ -378,7 +440,13 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
     auto products = [&](int kb, f32x16& x, f32x16& y) {
       x = f32x16{};
       y = f32x16{};
-      if constexpr (FOLD_L) x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fold_a[kb][0], fold_b, x, 0, 0, 0);
+      if constexpr (FOLD_L)
+        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fold_a[kb][0], AF ? (neg[kb] ? kb_neg : kb_pos) : fold_b, x,
+                                                    0, 0, 0);
+      if constexpr (AF && DQ) {
+        const bf16x8 ka = split3_operand(a_f * (float)(e0 + 32 * kb + c - wr0), g == 0);
+        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, neg[kb] ? sig_neg : sig_pos, x, 0, 0, 0);
+      }
       if constexpr (!DQ) y = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fold_a[kb][1], fold_b, y, 0, 0, 0);
       else y = y_init;
 #pragma unroll
@@ -400,6 +468,17 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
       products(kb, x, y);
       // streamed entity of register 0 in this lane; register r adds acc_row(r)
       const int eb = e0 + 32 * kb + 4 * g;
+      if constexpr (AF && STR) {
+        if (straddle[kb]) {
+          // sigma = +1 gave the pairs with k > q +slope (k - q): subtract twice that
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ent = eb + acc_row(r);
+            const int dk = DQ ? ent - row : row - ent;  // k - q
+            x[r] = dk > 0 ? x[r] - 2.0f * a_f * (float)dk : x[r];
+          }
+        }
+      }
       float lse4[16];
       if constexpr (!DQ && !FOLD_L) {
 #pragma unroll
@@ -413,17 +492,15 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ent = eb + acc_row(r);
-        const int qi = DQ ? row : ent, kj = DQ ? ent : row;
         float s = x[r] * a.scale_log2;
         float dmod = 1.0f;
-        if constexpr (C::MOD == MOD_ALIBI) s -= sl * __builtin_fabsf((float)(qi - kj));
         if constexpr (C::MOD == MOD_SOFTCAP) {
           s = softcap_log2(a, x[r]);
           const float th = s * (1.0f / a.softcap_log2);
           dmod = 1.0f - th * th;
         }
         float p;
-        if constexpr (DQ) p = fast_exp2(s - lse2_row);
+        if constexpr (DQ) p = fast_exp2(s - (AF ? (neg[kb] ? lse2_neg : lse2_pos) : lse2_row));
         else if constexpr (FOLD_L) p = fast_exp2(s);
         else p = fast_exp2(s - lse4[r]);
         if constexpr (MASKED) p = (ent >= lane_lo && ent <= lane_hi) ? p : 0.0f;
@@ -494,10 +571,22 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
     const bool empty = wave_idle || e0 > w_hi_max || e1 < w_lo_min;
     const bool full = e0 >= w_lo_max && e1 <= w_hi_min;
     if (!empty) {
-      if (full)
-        compute_tile(it, stage, std::integral_constant<bool, false>{});
-      else
-        compute_tile(it, stage, std::integral_constant<bool, true>{});
+      using T = std::true_type;
+      using F = std::false_type;
+      // ALiBi: does some unit of the tile straddle the wave's diagonal?
+      bool str = false;
+      if constexpr (C::MOD == MOD_ALIBI) {
+        const int q_lo = DQ ? wr0 : e0, q_hi = DQ ? wr0 + 31 : e1;
+        const int k_lo = DQ ? e0 : wr0, k_hi = DQ ? e1 : wr0 + 31;
+        str = q_hi > k_lo && q_lo < k_hi;
+      }
+      if (str) {
+        if (full) compute_tile(it, stage, F{}, T{});
+        else compute_tile(it, stage, T{}, T{});
+      } else {
+        if (full) compute_tile(it, stage, F{}, F{});
+        else compute_tile(it, stage, T{}, F{});
+      }
     }
     stage = stage == NS - 1 ? 0 : stage + 1;
   }
