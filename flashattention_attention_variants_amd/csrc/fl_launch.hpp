@@ -19,6 +19,12 @@ hipError_t launch_diff_bf16(const KernelArgs& a, int dqk, int dv, hipStream_t st
 // bf16 Evoformer gated attention, C = 32: qb = 1 or 2, bias = pair bias.
 hipError_t launch_evo_bf16(const KernelArgs& a, int c, int qb, bool bias, hipStream_t st);
 
+// bf16 Evoformer gated attention with a pair bias, C = 32, rows of at most
+// 256 positions (evo.hpp): a.sq = a.sk = L; sets a.rows_per_wg, the
+// entries each work-group walks.
+hipError_t launch_evo_short_bf16(KernelArgs& a, hipStream_t st);
+constexpr int kEvoShortMax = 256;  // longest row of the short-row kernel
+
 // bf16 decode against a KV cache, D = 64 (KernelArgs' decode fields set):
 // grid = B * H_kv * n_qt * n_split work-groups.
 hipError_t launch_decode_bf16(const KernelArgs& a, int mod, hipStream_t st);

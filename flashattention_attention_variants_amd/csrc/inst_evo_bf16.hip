@@ -1,6 +1,7 @@
 // Template instances of the bf16 matrix-core kernel for Evoformer gated
 // attention: C = 32, optional pair bias, per-key mask, sigmoid gate.
 #include "attn_mfma.hpp"
+#include "evo.hpp"
 #include "fl_launch.hpp"
 
 namespace fl {
@@ -23,6 +24,36 @@ hipError_t launch_evo_bf16(const KernelArgs& a, int c, int qb, bool bias, hipStr
   }
   if (bias) return go<MfmaCfg<32, 32, 1, 2, MOD_NONE, true, true, true>>(a, st);
   return go<MfmaCfg<32, 32, 1, 2, MOD_NONE, false, true, true>>(a, st);
+}
+
+// Short rows with a pair bias: one work-group per (entry, head) at a time,
+// walking rows_per_wg entries of one head.  Work-groups per compute unit: 8 waves
+// (two per SIMD) over NKU waves each, which the LDS stages also allow.
+// The grid aims at filling every compute unit once; consecutive work-group
+// ids take consecutive heads, so with 8 heads each XCD keeps to one head
+// and its L2 holds that head's pair bias.
+#ifndef FL_EVO_SHORT_FILL
+#define FL_EVO_SHORT_FILL 1
+#endif
+template <int NKU, bool BIAS>
+static hipError_t go_short(KernelArgs& a, hipStream_t st) {
+  using K = EvoCfg<NKU, BIAS>;
+  const int per_cu = 8 / NKU;
+  const int target = 256 * per_cu * FL_EVO_SHORT_FILL;
+  const int per_head = max(1, target / a.nh);
+  a.rows_per_wg = (a.nb + per_head - 1) / per_head;
+  const int64_t groups = (a.nb + a.rows_per_wg - 1) / a.rows_per_wg;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(evo_kernel<K>, dim3((unsigned)(groups * a.nh)), dim3(K::NW * 64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_evo_short_bf16(KernelArgs& a, hipStream_t st) {
+  const int L = a.sq;
+  if (L <= 64) return go_short<2, true>(a, st);
+  if (L <= 128) return go_short<4, true>(a, st);
+  if (L <= 256) return go_short<8, true>(a, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fl
