@@ -92,6 +92,12 @@ def short_name(name: str) -> str:
     return name.replace("void ", "").replace("(fl::KernelArgs)", "")
 
 
+def is_fwd_launch(name: str) -> bool:
+    """A forward attention dispatch: the general kernel or the short-row
+    Evoformer kernel."""
+    return "attn_" in name or "evo_kernel" in name
+
+
 def is_bwd_kernel(name: str) -> bool:
     return "attn_bwd_kernel" in name
 
@@ -137,7 +143,7 @@ def traffic(dir_fetch: str, dir_write: str, variants: list[str]) -> dict:
         if not copies:
             raise RuntimeError("%s: no copy dispatch to calibrate against" % dirname)
         ci, cv = max(copies, key=lambda x: x[1])
-        attn = [(name, v) for (_, name, v) in disp[ci + 1:] if "attn_" in name]
+        attn = [(name, v) for (_, name, v) in disp[ci + 1:] if is_fwd_launch(name)]
         if len(attn) < len(variants):
             raise RuntimeError("%s: %d attention dispatches after the copy, expected %d"
                                % (dirname, len(attn), len(variants)))
@@ -300,7 +306,8 @@ def evo_traffic_markdown(dir_fetch: str, dir_write: str) -> str:
     wl = inputs.WORKLOADS[EVO_WORKLOAD]
     sh = wl.shape
     rec = traffic(dir_fetch, dir_write, list(wl.variants))
-    out = ["# HBM traffic per launch -- attn_mfma_kernel, %s" % EVO_WORKLOAD, "",
+    out = ["# HBM traffic per launch -- Evoformer row (evo_kernel) and column (attn_mfma_kernel), %s"
+           % EVO_WORKLOAD, "",
            "Two counter runs of the Evoformer probe (`bench.py --probe-evoformer`: one row call "
            "with the pair bias and one column call, a %d-byte device copy, then both calls "
            "again), then the summary:" % rec["probe_copy_bytes"], "", CMD_VARS, "", "```",
@@ -351,7 +358,7 @@ def counters_markdown(dirs: list[str], variants: list[str], workload: str, units
     1024 SIMDs); per-unit figures divide by the number of 32x32 work units."""
     per = {v: {} for v in variants}
     for d in dirs:
-        attn = [x for x in _per_dispatch_all(d) if "attn_" in x["name"]][-len(variants):]
+        attn = [x for x in _per_dispatch_all(d) if is_fwd_launch(x["name"])][-len(variants):]
         for v, x in zip(variants, attn):
             per[v].update(x)
     out = ["# Counters -- attn_mfma_kernel, %s" % workload, "",

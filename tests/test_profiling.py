@@ -71,7 +71,8 @@ def test_decode_kernel_names():
 
 def test_evoformer_traffic_table(tmp_path):
     from flashattention_attention_variants_amd import flops
-    row = "void fl::attn_mfma_kernel<fl::MfmaCfg<32, 32, 1, 2, 0, true, true, true, false> >(fl::KernelArgs)"
+    # the row form with its pair bias runs on the short-row kernel
+    row = "void fl::evo_kernel<fl::EvoCfg<8, true> >(fl::KernelArgs)"
     col = "void fl::attn_mfma_kernel<fl::MfmaCfg<32, 32, 1, 1, 0, false, true, true, false> >(fl::KernelArgs)"
     copy_kib = profiling.PROBE_COPY_BYTES / 1024
     alg_row = flops.evoformer_bytes(128, 256, 8, 32, "row")
