@@ -74,8 +74,18 @@ void evo_kernel(KernelArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, g = lane >> 5;
   const int L = a.sq;  // positions per entry: queries and keys
-  const int h = blockIdx.x % a.nh;
-  const int b_first = (int)(blockIdx.x / a.nh) * a.rows_per_wg;
+  // work-group -> (head, run of entries).  Work-group ids go to the 8 XCDs
+  // in turn; units u = (run, head pair) take two consecutive slots of one
+  // XCD, one per head of the pair, so that the two heads' 64-byte halves of
+  // each 128-byte row of q, k, v and gate are fetched into one L2 (one head
+  // per XCD fetched every line twice), and with 8 heads each XCD keeps one
+  // head pair and its pair bias.  Ids past the last unit, and the missing
+  // second head of an odd count, end at once.
+  const int n_hp = (a.nh + 1) >> 1;
+  const int slot = (int)(blockIdx.x >> 3), unit = (slot >> 1) * 8 + (int)(blockIdx.x & 7);
+  const int h = 2 * (unit % n_hp) + (slot & 1);
+  const int b_first = (unit / n_hp) * a.rows_per_wg;
+  if (h >= a.nh || b_first >= a.nb) return;
   const int b_end = min(b_first + a.rows_per_wg, a.nb);
   const int qrow = 32 * w + c;  // this lane's query row
   const bool wave_busy = 32 * w < L;

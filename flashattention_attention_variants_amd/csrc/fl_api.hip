@@ -391,7 +391,7 @@ fl_status fl_evoformer_gated_attn_fwd(const void* q, const void* k, const void* 
   // a bias the general kernel is the faster one (column form 128 x 256:
   // 33 against 34 us cold, 25 against 29 us warm).
   if (pair_bias && L <= kEvoShortMax) {
-    if ((int64_t)a.nb * H > kMaxGrid) return FL_ERR_SHAPE;
+    if ((int64_t)a.nb * (H + 1) + 16 > kMaxGrid) return FL_ERR_SHAPE;
     return launch_status(launch_evo_short_bf16(a, st));
   }
   const int qb = L > 128 ? 2 : 1;

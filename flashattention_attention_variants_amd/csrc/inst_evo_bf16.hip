@@ -29,9 +29,8 @@ hipError_t launch_evo_bf16(const KernelArgs& a, int c, int qb, bool bias, hipStr
 // Short rows with a pair bias: one work-group per (entry, head) at a time,
 // walking rows_per_wg entries of one head.  Work-groups per compute unit: 8 waves
 // (two per SIMD) over NKU waves each, which the LDS stages also allow.
-// The grid aims at filling every compute unit once; consecutive work-group
-// ids take consecutive heads, so with 8 heads each XCD keeps to one head
-// and its L2 holds that head's pair bias.
+// The grid aims at filling every compute unit once (head pairs to XCDs:
+// see the kernel's work-group decode).
 #ifndef FL_EVO_SHORT_FILL
 #define FL_EVO_SHORT_FILL 1
 #endif
@@ -43,8 +42,11 @@ static hipError_t go_short(KernelArgs& a, hipStream_t st) {
   const int per_head = max(1, target / a.nh);
   a.rows_per_wg = (a.nb + per_head - 1) / per_head;
   const int64_t groups = (a.nb + a.rows_per_wg - 1) / a.rows_per_wg;
+  // two work-groups (the heads of a pair) per unit, units dealt 8 at a time
+  const int64_t units = groups * ((a.nh + 1) / 2);
+  const int64_t nwg = 16 * ((units + 7) / 8);
   (void)hipGetLastError();
-  hipLaunchKernelGGL(evo_kernel<K>, dim3((unsigned)(groups * a.nh)), dim3(K::NW * 64), 0, st, a);
+  hipLaunchKernelGGL(evo_kernel<K>, dim3((unsigned)nwg), dim3(K::NW * 64), 0, st, a);
   return hipGetLastError();
 }
 
