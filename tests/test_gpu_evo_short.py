@@ -145,3 +145,15 @@ def test_long_rows_general_kernel(axis, n, with_bias):
         run("row", 3, n, 2, 900 + n, with_bias=with_bias)
     else:
         run("col", n, 3, 2, 900 + n)
+
+
+def test_row_odd_heads_multi_entry():
+    """100 MSA rows x 256 residues x 3 heads: two MSA rows per work-group,
+    head pairs dealt to one XCD with the second head of the last pair
+    missing (those work-groups end at once), compared on sampled rows."""
+    rng = np.random.default_rng(13)
+    rows = np.unique(rng.choice(100 * 256 * 3, 5000, replace=False))
+    # every query row of head 2 (the unpaired head) of MSA rows 0..3
+    extra = [((s * 256 + r) * 3 + 2) for s in range(4) for r in range(256)]
+    rows = np.unique(np.concatenate([rows, np.array(extra, np.int64)]))
+    run("row", 100, 256, 3, 1001, rows=rows)
