@@ -1,0 +1,162 @@
+"""Seeded random sweep of the forward and backward against the float64 oracle.
+
+Each case draws its shape and variant from a generator seeded by the case
+number: batch 1-2, K/V heads 1-4 and GQA group 1-4, lengths 1-600 (query
+and key lengths apart only without a mask, the cases the boundary accepts),
+a score modification (none, ALiBi with a random maximum bias, softcap with a
+random cap) composed with a mask (none, causal, a causal or two-sided
+window of random width, a random prefix, 1-6 documents), sometimes a bias,
+a negative or zero scale, or queries scaled by 5 or 25 (a bias rounds the
+key length up to a multiple of 8, as the boundary requires for bf16).
+Every element of O and the LSE is compared (bf16 tolerance), and of dQ, dK
+and dV for the backward cases (the backward parity tolerance).  The case
+parameters are printed before each GPU call, so a failing case names
+itself.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from flashattention_attention_variants_amd import api, inputs
+from tests._gpu_common import check, errors, np64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+MASKS = (None, "causal", "sliding_window", "prefix_lm", "document")
+MODS = ("vanilla", "alibi", "softcap")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    oracle.build()
+    api.load_library()
+
+
+def draw(case, max_len):
+    """One random configuration (a dict of shapes and keyword arguments)."""
+    rng = np.random.default_rng(9000 + case)
+    B = int(rng.integers(1, 3))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4]))
+    mod = str(rng.choice(MODS))
+    mask = MASKS[int(rng.integers(0, len(MASKS)))]
+    Sq = int(rng.integers(1, max_len + 1))
+    Sk = Sq if mask is not None or rng.random() < 0.5 else int(rng.integers(1, max_len + 1))
+    kw = {}
+    if mask is None:
+        kw["variant"] = mod
+    elif mod == "vanilla":
+        kw["variant"] = mask
+    else:
+        kw["variant"], kw["mask"] = mod, mask
+    if mod == "alibi":
+        kw["alibi_max_bias"] = float(rng.uniform(1.0, 16.0))
+    if mod == "softcap":
+        kw["softcap"] = float(rng.uniform(5.0, 100.0))
+    if mask == "sliding_window":
+        kw["window"] = int(rng.integers(1, Sq + 40))
+        kw["window_causal"] = bool(rng.random() < 0.6)
+    if mask == "prefix_lm":
+        kw["prefix"] = int(rng.integers(0, Sq + 20))
+    if mask == "document":
+        kw["doc_offsets"] = inputs.doc_offsets(B, Sq, min(int(rng.integers(1, 7)), Sq),
+                                               seed=9500 + case)
+    r = rng.random()
+    if r < 0.1:
+        kw["scale"] = -1.0 / math.sqrt(64)
+    elif r < 0.15:
+        kw["scale"] = 0.0
+    q_mul = float(rng.choice([1.0, 1.0, 1.0, 5.0, 25.0]))
+    with_bias = bool(rng.random() < 0.2)
+    if with_bias and Sk % 8:
+        # a bf16 bias needs S_k % 8 == 0 (16-byte bias rows)
+        Sk = Sk + 8 - Sk % 8
+        if mask is not None:
+            Sq = Sk
+            if mask == "document":
+                kw["doc_offsets"] = inputs.doc_offsets(B, Sq, min(int(rng.integers(1, 7)), Sq),
+                                                       seed=9600 + case)
+    return dict(B=B, Hkv=Hkv, Hq=Hkv * G, Sq=Sq, Sk=Sk, kw=kw, q_mul=q_mul, with_bias=with_bias)
+
+
+def describe(case, c):
+    kw = {k: v for k, v in c["kw"].items() if k != "doc_offsets"}
+    return "case %d: B=%d Hq=%d Hkv=%d Sq=%d Sk=%d q*%g bias=%s %s" % (
+        case, c["B"], c["Hq"], c["Hkv"], c["Sq"], c["Sk"], c["q_mul"], c["with_bias"], kw)
+
+
+def make_inputs(case, c, D=64):
+    q, _, _ = inputs.attn_inputs(c["B"], c["Hq"], c["Hkv"], c["Sq"], c["Sq"], D, "bf16",
+                                 seed=9100 + case)
+    _, k, v = inputs.attn_inputs(c["B"], c["Hq"], c["Hkv"], c["Sk"], c["Sk"], D, "bf16",
+                                 seed=9200 + case)
+    if c["q_mul"] != 1.0:
+        q = (q.float() * c["q_mul"]).to(torch.bfloat16)
+    bias = inputs.bias_inputs(c["Hq"], c["Sq"], c["Sk"], "bf16", seed=9300 + case) \
+        if c["with_bias"] else None
+    return q, k, v, bias
+
+
+@pytest.mark.parametrize("case", range(48))
+def test_random_forward(case):
+    c = draw(case, 600)
+    what = describe(case, c)
+    print(what, flush=True)
+    q, k, v, bias = make_inputs(case, c)
+    kw = dict(c["kw"])
+    docs = kw.pop("doc_offsets", None)
+    o, lse = api.fl_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV),
+                             bias=None if bias is None else bias.to(DEV),
+                             doc_offsets=None if docs is None else docs.to(DEV),
+                             return_lse=True, **kw)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attn(np64(q), np64(k), np64(v), bias=None if bias is None else np64(bias),
+                         doc_offsets=None if docs is None else docs.numpy(), **kw)
+    check(np64(o), ro, "bf16", what)
+    mx, _, _ = errors(np64(lse), rl)
+    assert mx <= 2e-2, "%s: lse %g" % (what, mx)
+
+
+def check_grad(got, want, what):
+    # the tolerance of the backward parity tests: errors against the size of
+    # each gradient tensor (largest element 2e-2, mean 5e-3, sizes >= 0.05)
+    got, want = np.asarray(got, np.float64), np.asarray(want, np.float64)
+    assert np.isfinite(got).all(), what + ": non-finite"
+    err = np.abs(got - want)
+    smax = max(np.abs(want).max(), 0.05)
+    smean = max(np.abs(want).mean(), 0.05)
+    assert err.max() <= 2e-2 * smax and err.mean() <= 5e-3 * smean, \
+        "%s: max err %.3g (|ref| max %.3g), mean err %.3g (|ref| mean %.3g)" % (
+            what, err.max(), smax, err.mean(), smean)
+
+
+@pytest.mark.parametrize("case", range(100, 124))
+def test_random_backward(case):
+    c = draw(case, 300)
+    if c["with_bias"]:
+        c["with_bias"] = False  # the backward takes no bias
+    if c["q_mul"] == 25.0:
+        c["q_mul"] = 5.0
+    what = describe(case, c)
+    print(what, flush=True)
+    q, k, v, _ = make_inputs(case, c)
+    do = inputs.randn(torch.Generator().manual_seed(9400 + case), tuple(q.shape), "bf16")
+    kw = dict(c["kw"])
+    docs = kw.pop("doc_offsets", None)
+    dkw = dict(kw)
+    if docs is not None:
+        dkw["doc_offsets"] = docs.to(DEV)
+    g = [t.to(DEV) for t in (q, k, v, do)]
+    o, lse = api.fl_attn_fwd(g[0], g[1], g[2], return_lse=True, **dkw)
+    dq, dk, dv = api.fl_attn_bwd(g[0], g[1], g[2], o, lse, g[3], **dkw)
+    torch.cuda.synchronize()
+    ref = oracle.attn_bwd(np64(q), np64(k), np64(v), np64(do),
+                          doc_offsets=None if docs is None else docs.numpy(), **kw)
+    for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        check_grad(np64(got), want, "%s %s" % (what, name))
