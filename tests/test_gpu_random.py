@@ -9,7 +9,8 @@ window of random width, a random prefix, 1-6 documents), sometimes a bias,
 a negative or zero scale, or queries scaled by 5 or 25 (a bias rounds the
 key length up to a multiple of 8, as the boundary requires for bf16).
 Every element of O and the LSE is compared (bf16 tolerance), and of dQ, dK
-and dV for the backward cases (the backward parity tolerance).  The case
+and dV for the backward cases (the backward parity tolerance).  Decode,
+differential attention and both Evoformer forms get sweeps of their own.  The case
 parameters are printed before each GPU call, so a failing case names
 itself.
 """
@@ -160,3 +161,114 @@ def test_random_backward(case):
                           doc_offsets=None if docs is None else docs.numpy(), **kw)
     for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
         check_grad(np64(got), want, "%s %s" % (what, name))
+
+
+DEC_MASKS = (None, "causal", "sliding_window", "prefix_lm")
+
+
+@pytest.mark.parametrize("case", range(200, 224))
+def test_random_decode(case):
+    """Decode against KV caches of random capacity and lengths (0 .. capacity),
+    GQA groups 1-8, 1-8 new tokens, either cache layout, 0-5 key splits."""
+    rng = np.random.default_rng(9000 + case)
+    B = int(rng.integers(1, 6))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    Sq = int(rng.integers(1, 9))
+    S_cap = int(rng.integers(1, 801))
+    layout = str(rng.choice(["bhsd", "bshd"]))
+    splits = int(rng.choice([0, 1, 2, 3, 5]))
+    mod = str(rng.choice(MODS))
+    mask = DEC_MASKS[int(rng.integers(0, len(DEC_MASKS)))]
+    kw = dict(variant=mod if mask is None or mod != "vanilla" else mask)
+    if mask is not None and mod != "vanilla":
+        kw["mask"] = mask
+    if mod == "alibi":
+        kw["alibi_max_bias"] = float(rng.uniform(1.0, 16.0))
+    if mod == "softcap":
+        kw["softcap"] = float(rng.uniform(5.0, 100.0))
+    if mask == "sliding_window":
+        kw["window"] = int(rng.integers(1, S_cap + 40))
+        kw["window_causal"] = mod == "alibi" or bool(rng.random() < 0.6)
+    if mask == "prefix_lm":
+        kw["prefix"] = int(rng.integers(0, S_cap + 20))
+    if rng.random() < 0.1:
+        kw["scale"] = -1.0 / math.sqrt(64)
+    q_mul = float(rng.choice([1.0, 1.0, 5.0, 25.0]))
+    seqlens = torch.tensor(rng.integers(0, S_cap + 1, size=B), dtype=torch.int32)
+    what = "case %d: B=%d Hq=%d Hkv=%d Sq=%d S_cap=%d %s splits=%d q*%g %s lens=%s" % (
+        case, B, Hkv * G, Hkv, Sq, S_cap, layout, splits, q_mul, kw, seqlens.tolist())
+    print(what, flush=True)
+    q, kc, vc = inputs.decode_inputs(B, Hkv * G, Hkv, Sq, S_cap, 64, seed=9700 + case,
+                                     layout=layout)
+    if q_mul != 1.0:
+        q = (q.float() * q_mul).to(torch.bfloat16)
+    o, lse = api.fl_attn_decode_fwd(q.to(DEV), kc.to(DEV), vc.to(DEV), seqlens.to(DEV),
+                                    layout=layout, num_splits=splits, return_lse=True, **kw)
+    torch.cuda.synchronize()
+    if layout == "bshd":
+        kc, vc = kc.transpose(1, 2), vc.transpose(1, 2)
+    ro, rl = oracle.decode(np64(q), np64(kc), np64(vc), seqlens.numpy(), **kw)
+    check(np64(o), ro, "bf16", what)
+    mx, _, _ = errors(np64(lse), rl)
+    assert mx <= 2e-2, "%s: lse %g" % (what, mx)
+
+
+@pytest.mark.parametrize("case", range(300, 312))
+def test_random_diffattn(case):
+    """Differential attention: random lengths (equal under the causal mask),
+    heads, lambda in [0, 1.2], value dims 64 or 128, logits x1 or x5."""
+    rng = np.random.default_rng(9000 + case)
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 5))
+    causal = bool(rng.random() < 0.5)
+    Sq = int(rng.integers(1, 500))
+    Sk = Sq if causal else int(rng.integers(1, 500))
+    Dv = int(rng.choice([64, 128]))
+    lam = float(rng.uniform(0.0, 1.2))
+    q_mul = float(rng.choice([1.0, 5.0]))
+    what = "case %d: B=%d H=%d Sq=%d Sk=%d Dv=%d causal=%s lam=%.3f q*%g" % (
+        case, B, H, Sq, Sk, Dv, causal, lam, q_mul)
+    print(what, flush=True)
+    g = torch.Generator().manual_seed(9800 + case)
+    q1, q2 = (inputs.randn(g, (B, H, Sq, 64), "bf16") for _ in range(2))
+    k1, k2 = (inputs.randn(g, (B, H, Sk, 64), "bf16") for _ in range(2))
+    v = inputs.randn(g, (B, H, Sk, Dv), "bf16")
+    if q_mul != 1.0:
+        q1, q2 = ((t.float() * q_mul).to(torch.bfloat16) for t in (q1, q2))
+    o = api.fl_diffattn_fwd(*(t.to(DEV) for t in (q1, q2, k1, k2, v)), lam=lam, causal=causal)
+    torch.cuda.synchronize()
+    ro, _, _ = oracle.diffattn(*(np64(t) for t in (q1, q2, k1, k2, v)), lam=lam, causal=causal)
+    check(np64(o), ro, "bf16", what)
+
+
+@pytest.mark.parametrize("case", range(400, 416))
+def test_random_evoformer(case):
+    """Evoformer gated attention: row form (with or without the pair bias) or
+    column form, random MSA sizes and heads, random key masks with some rows
+    or columns fully masked, or no mask."""
+    rng = np.random.default_rng(9000 + case)
+    axis = str(rng.choice(["row", "col"]))
+    H = int(rng.integers(1, 9))
+    with_bias = axis == "row" and bool(rng.random() < 0.7)
+    N_seq = int(rng.integers(1, 90))
+    N_res = int(rng.integers(1, 300))
+    if with_bias:
+        N_res = N_res + (-N_res) % 8  # a bf16 pair bias needs N_res % 8 == 0
+    with_mask = bool(rng.random() < 0.8)
+    what = "case %d: %s N_seq=%d N_res=%d H=%d bias=%s mask=%s" % (
+        case, axis, N_seq, N_res, H, with_bias, with_mask)
+    print(what, flush=True)
+    q, k, v, gate, bias, km = inputs.evoformer_inputs(N_seq, N_res, H, 32, "bf16", 9900 + case,
+                                                      masked_frac=float(rng.uniform(0.0, 0.3)))
+    if with_mask and N_seq > 2 and N_res > 2:
+        km[int(rng.integers(0, N_seq)), :] = 0
+        km[:, int(rng.integers(0, N_res))] = 0
+    pb = bias if with_bias else None
+    o = api.fl_evoformer_gated_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), gate.to(DEV),
+                                        pair_bias=None if pb is None else pb.to(DEV),
+                                        key_mask=km.to(DEV) if with_mask else None, axis=axis)
+    torch.cuda.synchronize()
+    ro = oracle.evoformer(np64(q), np64(k), np64(v), np64(gate),
+                          pair_bias=None if pb is None else np64(pb),
+                          key_mask=km.numpy() if with_mask else None, axis=axis)
+    check(np64(o), ro, "bf16", what)
