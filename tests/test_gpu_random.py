@@ -10,7 +10,8 @@ a negative or zero scale, or queries scaled by 5 or 25 (a bias rounds the
 key length up to a multiple of 8, as the boundary requires for bf16).
 Every element of O and the LSE is compared (bf16 tolerance), and of dQ, dK
 and dV for the backward cases (the backward parity tolerance).  Decode,
-differential attention and both Evoformer forms get sweeps of their own.  The case
+differential attention, both Evoformer forms and the IPA core get sweeps
+of their own.  The case
 parameters are printed before each GPU call, so a failing case names
 itself.
 """
@@ -272,3 +273,43 @@ def test_random_evoformer(case):
                           pair_bias=None if pb is None else np64(pb),
                           key_mask=km.numpy() if with_mask else None, axis=axis)
     check(np64(o), ro, "bf16", what)
+
+
+PTS_MAX_ABS, PTS_MEAN_ABS = 1e-3, 1e-4  # the IPA parity tests' o_pts bar
+
+
+@pytest.mark.parametrize("case", range(500, 512))
+def test_random_ipa(case):
+    """IPA core: random residue counts 1-200, heads 1-12, pair channels 0, 64
+    or 128, with or without bias and key mask, key-mask density 0-50%."""
+    rng = np.random.default_rng(9000 + case)
+    B, L, H = int(rng.integers(1, 3)), int(rng.integers(1, 201)), int(rng.integers(1, 13))
+    cz = int(rng.choice([0, 64, 128]))
+    with_bias, with_mask = bool(rng.random() < 0.7), bool(rng.random() < 0.7)
+    frac = float(rng.uniform(0.0, 0.5))
+    what = "case %d: B=%d L=%d H=%d cz=%d bias=%s mask=%s (%.2f)" % (
+        case, B, L, H, cz, with_bias, with_mask, frac)
+    print(what, flush=True)
+    t = inputs.ipa_inputs(B, L, H, 16, 4, 8, cz or 128, "bf16", seed=10000 + case,
+                          masked_frac=frac)
+    if cz == 64:
+        t["z"] = t["z"][..., :64].contiguous()
+    g = {n: x.to(DEV) for n, x in t.items()}
+    o, op, oz = api.fl_ipa_attn_fwd(g["q"], g["k"], g["v"], g["q_pts"], g["k_pts"], g["v_pts"],
+                                    g["rot"], g["trans"], g["gamma"],
+                                    pair_bias=g["pair_bias"] if with_bias else None,
+                                    z=g["z"] if cz else None,
+                                    key_mask=g["key_mask"] if with_mask else None)
+    torch.cuda.synchronize()
+    c = {n: np64(x) for n, x in t.items()}
+    ro, rp, rz = oracle.ipa(c["q"], c["k"], c["v"], c["q_pts"], c["k_pts"], c["v_pts"],
+                            c["rot"], c["trans"], c["gamma"],
+                            pair_bias=c["pair_bias"] if with_bias else None,
+                            z=c["z"] if cz else None,
+                            key_mask=t["key_mask"].numpy() if with_mask else None)
+    check(np64(o), ro, "bf16", what + " o")
+    mx, mean, _ = errors(np64(op), rp)
+    assert mx <= PTS_MAX_ABS and mean <= PTS_MEAN_ABS, "%s o_pts: max %.3g mean %.3g" % (
+        what, mx, mean)
+    if cz:
+        check(np64(oz), rz, "bf16", what + " o_pair")
