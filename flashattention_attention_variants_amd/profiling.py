@@ -121,6 +121,26 @@ def stats_table(dirname: str, keep=None) -> str:
     return "\n".join(out)
 
 
+def dispatch_table(dirname: str, keep=None) -> str:
+    """Per-dispatch durations from the kernel trace, grouped by kernel and
+    launch shape (work-groups = grid / work-group size): a kernel instance
+    that serves several workloads of one run gets a row per shape."""
+    groups: dict[tuple, list] = {}
+    for r in _csv(dirname, "kernel_trace.csv"):
+        name = r["Kernel_Name"]
+        if keep is not None and not keep(name):
+            continue
+        nwg = int(r["Grid_Size_X"]) // max(int(r["Workgroup_Size_X"]), 1)
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups.setdefault((short_name(name), nwg), []).append(us)
+    out = ["| kernel | work-groups | calls | avg (us) | min (us) | max (us) |",
+           "|---|---:|---:|---:|---:|---:|"]
+    for (name, nwg), v in sorted(groups.items(), key=lambda x: (x[0][0], -x[0][1])):
+        out.append("| `%s` | %d | %d | %.1f | %.1f | %.1f |" % (
+            name, nwg, len(v), sum(v) / len(v), min(v), max(v)))
+    return "\n".join(out)
+
+
 def _per_dispatch(dirname: str, counter: str) -> list[tuple[int, str, float]]:
     vals: dict[int, list] = {}
     for r in _csv(dirname, "counter_collection.csv"):
@@ -197,7 +217,14 @@ def stats_markdown(dirname: str, bench_json: str, workload: str) -> str:
         out.append("| %s | %.4f | %.1f | %.1f |" % (k, v["ms"], v["tflops"], 100 * v["frac_bf16_peak"]))
     r = b["roofline"]
     out += ["", "Step value %.1f TFLOP/s.  Dominant kernel: %s, %.4f ms per launch." % (
-        b["value"], r["kernel"], r["ms_per_launch"]), ""]
+        b["value"], r["kernel"], r["ms_per_launch"]), "",
+            "Per launch shape (the same kernel trace, dispatches grouped by kernel instance and "
+            "work-group count): the headline launches are the rows with the headline shape's "
+            "work-group count (B H_q ceil(S / rows per work-group): 1024 for the two-block "
+            "instances, 2048 for the one-block ones at B 4, H 16, S 4096); the others are the "
+            "smaller configurations the same run times.", "",
+            dispatch_table(dirname, lambda n: "attn_mfma_kernel" in n and not is_decode_kernel(n)),
+            ""]
     return "\n".join(out)
 
 

@@ -109,3 +109,27 @@ def test_traffic_record_guard(tmp_path):
         path.write_text(json.dumps(bad))
         assert profiling.traffic_for(str(path), "vanilla") is None, key
     assert profiling.traffic_for(str(tmp_path / "missing.json"), "vanilla") is None
+
+
+def test_dispatch_table(tmp_path):
+    """Dispatches of one kernel instance at two launch shapes get a row each,
+    with the average of their own durations."""
+    d = tmp_path / "kt"
+    os.makedirs(d)
+    name = "void fl::attn_mfma_kernel<fl::MfmaCfg<64, 64, 1, 2, 3> >(fl::KernelArgs)"
+    head = ["Kind", "Agent_Id", "Queue_Id", "Stream_Id", "Thread_Id", "Dispatch_Id", "Kernel_Id",
+            "Kernel_Name", "Correlation_Id", "Start_Timestamp", "End_Timestamp", "LDS_Block_Size",
+            "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Workgroup_Size_X",
+            "Workgroup_Size_Y", "Workgroup_Size_Z", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"]
+    with open(d / "run_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(head)
+        # 1024 work-groups: 360 and 362 us; 512 work-groups: 100 us
+        for i, (t0, t1, grid) in enumerate([(0, 360000, 262144), (10 ** 6, 10 ** 6 + 362000, 262144),
+                                             (2 * 10 ** 6, 2 * 10 ** 6 + 100000, 131072)]):
+            w.writerow(["KERNEL_DISPATCH", "Agent 1", 1, 0, 1, i + 1, 3, name, i + 1, t0, t1, 0, 0,
+                        128, 0, 96, 256, 1, 1, grid, 1, 1])
+    t = profiling.dispatch_table(str(d))
+    rows = [l for l in t.splitlines() if l.startswith("| `")]
+    assert rows[0].endswith("| 1024 | 2 | 361.0 | 360.0 | 362.0 |"), rows
+    assert rows[1].endswith("| 512 | 1 | 100.0 | 100.0 | 100.0 |"), rows
