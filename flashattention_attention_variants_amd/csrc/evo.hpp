@@ -8,17 +8,19 @@
 // same for every MSA row) or over the 128 sequences of one residue column
 // (column form, no bias).  Rows this short fit a work-group whole: NKU waves
 // hold the 32*NKU query rows of one (entry, head), and the work-group walks a
-// run of entries (MSA rows or residue columns) of one head.  The launcher
-// takes this kernel for the row form with its bias, which then stays in
-// registers for the whole walk; without a bias the general kernel's gated
-// form measured faster.  (Loading K and V two entries ahead through three
+// run of entries (MSA rows or residue columns) of one head.  With the row
+// form's bias, the bias stays in registers for the whole walk (two waves
+// per SIMD); without a bias (the column form) the gate rows are read from
+// memory in the epilogue instead of LDS, and the kernel runs three waves
+// per SIMD (129 registers; at 128 positions three work-groups of four
+// waves share a compute unit).  (Loading K and V two entries ahead through three
 // LDS stages, the gate one entry ahead, did not help: a timestamp trace
 // puts an entry at about 3.4 us of units and 3 us of load issue and
 // barrier wait however the loads are placed.)
 //
-// Per entry, K, V, Q and the gate rows land in LDS by DMA while the entry
-// before computes (two LDS stages, by entry parity); the keys' mask terms
-// follow through registers.  A wave then computes, per 32-key unit,
+// Per entry, K, V, Q and (with a bias) the gate rows land in LDS by DMA
+// while the entry before computes (two LDS stages, by entry parity); the
+// keys' mask terms follow through registers.  A wave then computes, per 32-key unit,
 //
 //   S^T  = K (f Q)^T + c I Bias^T + ext     MFMA 32x32x16 bf16
 //   p    = 2^(m S^T)                         one multiply, one exponential
@@ -48,13 +50,18 @@ namespace fl {
 template <int NKU_, bool BIAS_>
 struct EvoCfg {
   static constexpr int NKU = NKU_;  // 32-key units per row, and waves per work-group
-  static constexpr bool BIAS = BIAS_;  // (only the bias instances are built)
+  static constexpr bool BIAS = BIAS_;
   static constexpr int NW = NKU_;
   static constexpr int LP = 32 * NKU_;  // positions per entry, padded
   static constexpr int MAT = LP * 64;   // bytes of one [LP, 32] bf16 matrix
   // one LDS stage: K, V, Q, gate, then the keys' mask terms (bf16)
-  static constexpr int K_OFF = 0, V_OFF = MAT, Q_OFF = 2 * MAT, G_OFF = 3 * MAT, T_OFF = 4 * MAT;
-  static constexpr int STAGE = 4 * MAT + 2 * LP;
+  // without a bias: the gate is read from memory in the epilogue, and three
+  // waves per SIMD
+  static constexpr bool GLDS = BIAS_;
+  static constexpr int WPE = BIAS_ ? 2 : 3;
+  static constexpr int K_OFF = 0, V_OFF = MAT, Q_OFF = 2 * MAT, G_OFF = 3 * MAT,
+                       T_OFF = (GLDS ? 4 : 3) * MAT;
+  static constexpr int STAGE = (GLDS ? 4 : 3) * MAT + 2 * LP;
   static_assert(NKU == 2 || NKU == 4 || NKU == 8, "row lengths");
   static_assert(2 * STAGE <= 160 * 1024, "LDS");
 };
@@ -65,7 +72,7 @@ struct EvoCfg {
 __device__ __forceinline__ constexpr int evo_swz(int r) { return (r >> 2) & 3; }
 
 template <class C>
-__global__ __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(C::WPE)))
 void evo_kernel(KernelArgs a) {
   constexpr int NKU = C::NKU, LP = C::LP;
   __shared__ __attribute__((aligned(16))) char lds[2 * C::STAGE];
@@ -163,7 +170,7 @@ void evo_kernel(KernelArgs a) {
     dma(a.k[0], a.k_sb, a.k_sh, a.k_si, C::K_OFF, true);
     dma(a.v, a.v_sb, a.v_sh, a.v_si, C::V_OFF, false);
     dma(a.q[0], a.q_sb, a.q_sh, a.q_si, C::Q_OFF, true);
-    dma(a.gate, a.o_sb, a.o_sh, a.o_si, C::G_OFF, true);
+    if constexpr (C::GLDS) dma(a.gate, a.o_sb, a.o_sh, a.o_si, C::G_OFF, true);
     // read raw and tested at the hand-over: a test here would wait for this
     // load, and so for the DMA loads above
     if (a.kmask) mbyte = a.kmask[(int64_t)bb * a.km_sb + (int64_t)min(tid, L - 1) * a.km_sj];
@@ -322,13 +329,16 @@ void evo_kernel(KernelArgs a) {
     // 16 contiguous bytes of dims 16r + 8g .. +7
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     const char* grow_p = sb + C::G_OFF + qrow * 64;
+    const bf16* gmem = (const bf16*)a.gate + (int64_t)bb * a.o_sb + (int64_t)h * a.o_sh +
+                       (int64_t)min(qrow, L - 1) * a.o_si;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       u32x2 packed[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int r4 = 2 * r + hh;
-        const bf16x4 gv = *(const bf16x4*)(grow_p + 16 * (r4 ^ evo_swz(qrow)) + 8 * g);
+        const bf16x4 gv = C::GLDS ? *(const bf16x4*)(grow_p + 16 * (r4 ^ evo_swz(qrow)) + 8 * g)
+                                  : *(const bf16x4*)(gmem + 8 * r4 + 4 * g);
         float ov[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) ov[e] = oacc[4 * r4 + e] * inv * sigmoid((float)gv[e]);

@@ -385,12 +385,12 @@ fl_status fl_evoformer_gated_attn_fwd(const void* q, const void* k, const void* 
     return launch_status(launch_f32(a, C, C, 1, MOD_NONE, st));
   }
   if (!span_ok(L, a.k_si, C)) return FL_ERR_SHAPE;
-  // Rows of at most 256 positions with a pair bias: the short-row kernel,
-  // which keeps each wave's bias rows in registers across the entries it
-  // walks (measured at 128 x 256, H = 8: 42 against 54 us cold).  Without
-  // a bias the general kernel is the faster one (column form 128 x 256:
-  // 33 against 34 us cold, 25 against 29 us warm).
-  if (pair_bias && L <= kEvoShortMax) {
+  // Rows of at most 256 positions: the short-row kernel, which keeps each
+  // wave's bias rows in registers across the entries it walks (row form at
+  // 128 x 256, H = 8: 41 against 54 us cold) and without a bias runs three
+  // waves per SIMD (column form: 31.7 against 32.6 us cold, 22.4 against
+  // 24.8 us warm).
+  if (L <= kEvoShortMax) {
     if ((int64_t)a.nb * (H + 1) + 16 > kMaxGrid) return FL_ERR_SHAPE;
     return launch_status(launch_evo_short_bf16(a, st));
   }

@@ -26,9 +26,10 @@ hipError_t launch_evo_bf16(const KernelArgs& a, int c, int qb, bool bias, hipStr
   return go<MfmaCfg<32, 32, 1, 2, MOD_NONE, false, true, true>>(a, st);
 }
 
-// Short rows with a pair bias: one work-group per (entry, head) at a time,
-// walking rows_per_wg entries of one head.  Work-groups per compute unit: 8 waves
-// (two per SIMD) over NKU waves each, which the LDS stages also allow.
+// Short rows: one work-group per (entry, head) at a time, walking
+// rows_per_wg entries of one head.  Work-groups per compute unit: 8 waves
+// (two per SIMD; with a bias) or 12 (three per SIMD; without) over NKU
+// waves each, which the LDS stages also allow.
 // The grid aims at filling every compute unit once (head pairs to XCDs:
 // see the kernel's work-group decode).
 #ifndef FL_EVO_SHORT_FILL
@@ -37,7 +38,7 @@ hipError_t launch_evo_bf16(const KernelArgs& a, int c, int qb, bool bias, hipStr
 template <int NKU, bool BIAS>
 static hipError_t go_short(KernelArgs& a, hipStream_t st) {
   using K = EvoCfg<NKU, BIAS>;
-  const int per_cu = 8 / NKU;
+  const int per_cu = (BIAS ? 8 : 12) / NKU;
   const int target = 256 * per_cu * FL_EVO_SHORT_FILL;
   const int per_head = max(1, target / a.nh);
   a.rows_per_wg = (a.nb + per_head - 1) / per_head;
@@ -52,9 +53,10 @@ static hipError_t go_short(KernelArgs& a, hipStream_t st) {
 
 hipError_t launch_evo_short_bf16(KernelArgs& a, hipStream_t st) {
   const int L = a.sq;
-  if (L <= 64) return go_short<2, true>(a, st);
-  if (L <= 128) return go_short<4, true>(a, st);
-  if (L <= 256) return go_short<8, true>(a, st);
+  const bool bias = a.bias != nullptr;
+  if (L <= 64) return bias ? go_short<2, true>(a, st) : go_short<2, false>(a, st);
+  if (L <= 128) return bias ? go_short<4, true>(a, st) : go_short<4, false>(a, st);
+  if (L <= 256) return bias ? go_short<8, true>(a, st) : go_short<8, false>(a, st);
   return hipErrorInvalidValue;
 }
 

@@ -1,9 +1,10 @@
 """GPU parity of Evoformer gated attention over rows of at most 256 positions.
 
-Row-form calls with a pair bias run on the kernel whose work-groups hold a
-whole (entry, head) and walk several MSA rows of one head, with the bias
-held in registers and added through the matrix cores; calls without a bias
-(and rows past 256 positions) run on the general kernel's gated form.  Each
+Rows of at most 256 positions run on the kernel whose work-groups hold a
+whole (entry, head) and walk several entries of one head: with the row
+form's pair bias held in registers and added through the matrix cores, or
+without a bias at three waves per SIMD; rows past 256 positions run on the
+general kernel's gated form.  Each
 case is compared element by element with the float64 oracle (papers.lqhl.me
 wiki, "设计取舍": a bias broadcast over an extra dimension; AlphaFold2's
 row- and column-wise gated self-attention).
@@ -99,8 +100,8 @@ def test_row_multi_entry_walk():
 
 
 def test_col_multi_entry_walk():
-    """128 sequences x 71 residue columns x 8 heads with a fully masked
-    column (the general kernel's gated form)."""
+    """128 sequences x 71 residue columns x 8 heads: columns walked two or
+    three per work-group, the last group shorter; a fully masked column."""
     def edit(km):
         km[:, 4] = 0
     got, ro, _ = run("col", 128, 71, 8, 502, edit_mask=edit)
