@@ -333,7 +333,7 @@ def evo_traffic_markdown(dir_fetch: str, dir_write: str) -> str:
     wl = inputs.WORKLOADS[EVO_WORKLOAD]
     sh = wl.shape
     rec = traffic(dir_fetch, dir_write, list(wl.variants))
-    out = ["# HBM traffic per launch -- Evoformer row (evo_kernel) and column (attn_mfma_kernel), %s"
+    out = ["# HBM traffic per launch -- Evoformer row and column (evo_kernel), %s"
            % EVO_WORKLOAD, "",
            "Two counter runs of the Evoformer probe (`bench.py --probe-evoformer`: one row call "
            "with the pair bias and one column call, a %d-byte device copy, then both calls "
