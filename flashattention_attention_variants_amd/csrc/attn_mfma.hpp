@@ -892,10 +892,23 @@ void attn_mfma_kernel(KernelArgs a) {
     read_v(0);
 
     auto mask = [&](f32x16& acc, int kb, int qb) {
+      if constexpr (QB == 1) {
+        // One unsigned compare per score: key j is allowed when j - lo, as
+        // an unsigned number, is below the row's width (0 for a row with
+        // no key; lo >= 0 and hi <= S_k - 1, so nothing overflows).  With
+        // two query blocks the compiler then recomputes LDS addresses in
+        // the full tiles, and those keep two compares.
+        const int base = j0 + 32 * kb + 4 * g - row_lo[qb];
+        const unsigned width = (unsigned)max(row_hi[qb] - row_lo[qb] + 1, 0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = j0 + 32 * kb + 4 * g + acc_row(r);
-        acc[r] = (j >= row_lo[qb] && j <= row_hi[qb]) ? acc[r] : kNegInf;
+        for (int r = 0; r < 16; ++r)
+          acc[r] = (unsigned)(base + acc_row(r)) < width ? acc[r] : kNegInf;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + 32 * kb + 4 * g + acc_row(r);
+          acc[r] = (j >= row_lo[qb] && j <= row_hi[qb]) ? acc[r] : kNegInf;
+        }
       }
     };
     // p = 2^(x - shift) of a unit's 16 scores (folded scores: x and shift
