@@ -620,14 +620,15 @@ void attn_mfma_kernel(KernelArgs a) {
     }
   }
 
-  int row_lo[QB], row_hi[QB];
+  int row_lo[QB], row_w[QB];  // first key and number of keys (0: none) of each lane's row
   // positions of this lane's row and of the first and last row of each
   // 32-row block (the block's place against the diagonal)
   int lane_pos[QB], blk_pmin[QB], blk_pmax[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qi = min(wq0 + 32 * qb + c, a.sq - 1);  // rows past S_q copy the last row
-    interval(pos_of(qi), row_lo[qb], row_hi[qb]);
+    interval(pos_of(qi), row_lo[qb], row_w[qb]);   // first and last key
+    row_w[qb] = max(row_w[qb] - row_lo[qb] + 1, 0);  // from here on: the number of keys
     if constexpr (C::DEC) {
       lane_pos[qb] = pos_of(qi);
       const int r0 = min(wq0 + 32 * qb, a.sq - 1);
@@ -891,25 +892,16 @@ void attn_mfma_kernel(KernelArgs a) {
     };
     read_v(0);
 
+    // One unsigned compare per score: key j is allowed when j - lo, as an
+    // unsigned number, is below the row's width (lo >= 0 and the last key
+    // <= S_k - 1, so nothing overflows); the offset of register 0 is formed
+    // once per unit.
     auto mask = [&](f32x16& acc, int kb, int qb) {
-      if constexpr (QB == 1) {
-        // One unsigned compare per score: key j is allowed when j - lo, as
-        // an unsigned number, is below the row's width (0 for a row with
-        // no key; lo >= 0 and hi <= S_k - 1, so nothing overflows).  With
-        // two query blocks the compiler then recomputes LDS addresses in
-        // the full tiles, and those keep two compares.
-        const int base = j0 + 32 * kb + 4 * g - row_lo[qb];
-        const unsigned width = (unsigned)max(row_hi[qb] - row_lo[qb] + 1, 0);
+      const int base = j0 + 32 * kb + 4 * g - row_lo[qb];
+      const unsigned width = (unsigned)row_w[qb];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          acc[r] = (unsigned)(base + acc_row(r)) < width ? acc[r] : kNegInf;
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = j0 + 32 * kb + 4 * g + acc_row(r);
-          acc[r] = (j >= row_lo[qb] && j <= row_hi[qb]) ? acc[r] : kNegInf;
-        }
-      }
+      for (int r = 0; r < 16; ++r)
+        acc[r] = (unsigned)(base + acc_row(r)) < width ? acc[r] : kNegInf;
     };
     // p = 2^(x - shift) of a unit's 16 scores (folded scores: x and shift
     // in the units of S^T, 2^(fold_m (x - shift))), rounded to bf16 in the
@@ -1023,8 +1015,8 @@ void attn_mfma_kernel(KernelArgs a) {
         // test in vector compares, without divergent control flow.)
         bool has_key = true;
         if constexpr (MASKED)
-          has_key = (row_hi[qb] >= j0 + 32 * kb) & (row_lo[qb] <= j0 + 32 * kb + 31) &
-                    (row_lo[qb] <= row_hi[qb]);
+          has_key = (row_lo[qb] + row_w[qb] - 1 >= j0 + 32 * kb) & (row_lo[qb] <= j0 + 32 * kb + 31) &
+                    (row_w[qb] > 0);
         const bool redo = (has_key & (l_run[s][qb] + lsum == 0.0f)) | !(lsum <= 0x1p64f);
         interleave_hint();
         if (__builtin_amdgcn_ballot_w64(redo) || (!FOLDED && need_fold)) {
@@ -1354,7 +1346,7 @@ void attn_mfma_kernel(KernelArgs a) {
       // rows past S_q (zero queries, under ALiBi possibly far below range)
       // produce no output and are left out
       const bool real = wq0 + 32 * qb + c < a.sq;
-      const bool has = row_lo[qb] <= row_hi[qb];
+      const bool has = row_w[qb] > 0;
       bad |= real & ((has & !(l >= lo)) | !(l <= 0x1p100f));
     }
     __shared__ int pass_bad;
