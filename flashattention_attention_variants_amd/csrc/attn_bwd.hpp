@@ -187,7 +187,11 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
 
   // ---- per-row statistics and intervals ------------------------------------------
   float lse2_row = 0.0f, delta_row = 0.0f;  // DQ: this lane's query
-  int lane_lo, lane_hi;                     // DQ: keys of the query; DKDV: queries of the key
+  // DQ: the keys of the query; DKDV: the queries of the key.  lane_w is the
+  // number of them (0: none), except under ALiBi, where it stays the last
+  // one: its instance sits at 256 registers and the compare of the count
+  // takes it past them
+  int lane_lo, lane_w;
   if constexpr (DQ) {
     // D = dO . O over the row; the lane holds half of the head dimension
     const bf16* po = (const bf16*)g2.o + b * a.q_sb + hr * a.q_sh + (int64_t)row * a.q_si;
@@ -203,9 +207,10 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
     const float l = a.lse[0][li];
     lse2_row = l == kNegInf ? __builtin_inff() : l * kLog2e;  // no key: every p is 0
   }
-  if (doc_lds) doc_ivl(row, lane_lo, lane_hi);
-  else if constexpr (DQ) key_interval(a, b, row, lane_lo, lane_hi);
-  else query_interval(a, b, row, lane_lo, lane_hi);
+  if (doc_lds) doc_ivl(row, lane_lo, lane_w);
+  else if constexpr (DQ) key_interval(a, b, row, lane_lo, lane_w);
+  else query_interval(a, b, row, lane_lo, lane_w);
+  if constexpr (C::MOD != MOD_ALIBI) lane_w = max(lane_w - lane_lo + 1, 0);
 
   // streamed range of the work-group and of this wave (union over rows)
   int lo_first, hi_first, lo_last, hi_last, w_lo_min, w_hi_min, w_lo_max, w_hi_max;
@@ -468,6 +473,7 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
       products(kb, x, y);
       // streamed entity of register 0 in this lane; register r adds acc_row(r)
       const int eb = e0 + 32 * kb + 4 * g;
+      const int ebl = eb - lane_lo;  // entry of register 0 relative to the row's first
       if constexpr (AF && STR) {
         if (straddle[kb]) {
           // sigma = +1 gave the pairs with k > q +slope (k - q): subtract twice that
@@ -503,7 +509,12 @@ void attn_bwd_kernel(KernelArgs a, BwdArgs g2) {
         if constexpr (DQ) p = fast_exp2(s - (AF ? (neg[kb] ? lse2_neg : lse2_pos) : lse2_row));
         else if constexpr (FOLD_L) p = fast_exp2(s);
         else p = fast_exp2(s - lse4[r]);
-        if constexpr (MASKED) p = (ent >= lane_lo && ent <= lane_hi) ? p : 0.0f;
+        // one unsigned compare: lane_lo >= 0 and the last entry is in
+        // range, so ent - lane_lo cannot overflow
+        if constexpr (MASKED) {
+          if constexpr (C::MOD == MOD_ALIBI) p = (ent >= lane_lo && ent <= lane_w) ? p : 0.0f;
+          else p = (unsigned)(ebl + acc_row(r)) < (unsigned)lane_w ? p : 0.0f;
+        }
         if constexpr (DQ) {
           dex = fmaf(p, y[r], dex);
           zex += p;
